@@ -1,0 +1,152 @@
+"""CPU oracle for the sparse MoE FFN layer -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library and its Python binding
+never import it.  The arithmetic lives in ``moe_oracle.cc`` (plain
+single-threaded C++); this module is argument marshalling over ctypes.
+
+Functions take and return numpy arrays.  bf16 tensors are ``np.uint16`` bit
+patterns.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = os.environ.get("MOE_ORACLE_LIB", _build.LIB)
+        if path == _build.LIB and not os.path.exists(path):
+            _build.build()
+        L = ctypes.CDLL(path)
+        L.oracle_route.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]
+        L.oracle_permute.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P]
+        L.oracle_expert.argtypes = [_I, _I, _P, _P, _P, _P]
+        L.oracle_layer.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                   _I, _P, _P, _P, _P, _P]
+        L.oracle_rmsnorm.argtypes = [_I, _I, _P, _P, ctypes.c_float, _P]
+        for f in (L.oracle_route, L.oracle_permute, L.oracle_expert, L.oracle_layer, L.oracle_rmsnorm):
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise ValueError(f"{name} returned {rc}")
+
+
+def route(x, w_router, sel_bias, k, logit_bias=None, want_scores=False):
+    """Routing for every row of x.  Returns (ids [T,k] int32 ascending,
+    weights [T,k] f32, gap [T] f32, scores [T,E] f32 or None)."""
+    x = _c(x, np.uint16)
+    w_router = _c(w_router, np.uint16)
+    sel_bias = _c(sel_bias, np.float32)
+    logit_bias = _c(logit_bias, np.float32)
+    T, d = x.shape
+    E = w_router.shape[0]
+    ids = np.zeros((T, k), np.int32)
+    wts = np.zeros((T, k), np.float32)
+    gap = np.zeros(T, np.float32)
+    scores = np.zeros((T, E), np.float32) if want_scores else None
+    rc = lib().oracle_route(T, d, E, k, _ptr(x), _ptr(w_router), _ptr(sel_bias), _ptr(logit_bias), _ptr(ids),
+                            _ptr(wts), _ptr(gap), _ptr(scores))
+    _check(rc, "oracle_route")
+    return ids, wts, gap, scores
+
+
+def permute(topk_ids, num_experts):
+    """Stable (expert, token) permutation.  Returns (counts [E], offsets [E+1],
+    perm_pairs [T*k], pair_pos [T*k]), all int32."""
+    ids = _c(topk_ids, np.int32)
+    T, k = ids.shape
+    E = num_experts
+    counts = np.zeros(E, np.int32)
+    offsets = np.zeros(E + 1, np.int32)
+    perm = np.zeros(T * k, np.int32)
+    pos = np.zeros(T * k, np.int32)
+    rc = lib().oracle_permute(T, E, k, _ptr(ids), _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(pos))
+    _check(rc, "oracle_permute")
+    return counts, offsets, perm, pos
+
+
+def expert(x_row, w_gu, w_d):
+    """One SwiGLU expert on one bf16 row: W_d (SiLU(W_g x) * W_u x), f32 [d]."""
+    x_row = _c(x_row, np.uint16)
+    w_gu = _c(w_gu, np.uint16)
+    w_d = _c(w_d, np.uint16)
+    d = x_row.shape[0]
+    h = w_gu.shape[0] // 2
+    out = np.zeros(d, np.float32)
+    _check(lib().oracle_expert(d, h, _ptr(x_row), _ptr(w_gu), _ptr(w_d), _ptr(out)), "oracle_expert")
+    return out
+
+
+def layer(x, w_router, sel_bias, k, w_gu, w_d, ws_gu=None, ws_d=None, routed_scale=1.0, logit_bias=None,
+          tokens=None):
+    """Whole layer on the listed token rows (all rows if tokens is None).
+
+    w_gu / w_d: sequences of length E whose entries are [2h,d] / [d,h] uint16
+    arrays, or None for experts no listed token selects.
+    Returns (ids [n,k], weights [n,k], gap [n], y [n,d] f32)."""
+    x = _c(x, np.uint16)
+    w_router = _c(w_router, np.uint16)
+    sel_bias = _c(sel_bias, np.float32)
+    logit_bias = _c(logit_bias, np.float32)
+    T, d = x.shape
+    E = w_router.shape[0]
+    assert len(w_gu) == E and len(w_d) == E
+    h = next(w.shape[0] // 2 for w in w_gu if w is not None)
+    keep = []
+    gu_ptrs = (ctypes.c_void_p * E)()
+    d_ptrs = (ctypes.c_void_p * E)()
+    for e in range(E):
+        if w_gu[e] is not None:
+            a = _c(w_gu[e], np.uint16)
+            b = _c(w_d[e], np.uint16)
+            keep += [a, b]
+            gu_ptrs[e] = a.ctypes.data
+            d_ptrs[e] = b.ctypes.data
+    hs = 0
+    if ws_gu is not None:
+        ws_gu = _c(ws_gu, np.uint16)
+        ws_d = _c(ws_d, np.uint16)
+        hs = ws_gu.shape[0] // 2
+    tok = None if tokens is None else np.ascontiguousarray(tokens, np.int32)
+    n = T if tok is None else tok.shape[0]
+    ids = np.zeros((n, k), np.int32)
+    wts = np.zeros((n, k), np.float32)
+    gap = np.zeros(n, np.float32)
+    y = np.zeros((n, d), np.float32)
+    rc = lib().oracle_layer(T, d, E, k, h, hs, _ptr(x), _ptr(w_router), _ptr(sel_bias), _ptr(logit_bias), gu_ptrs,
+                            d_ptrs, _ptr(ws_gu), _ptr(ws_d), float(routed_scale), n, _ptr(tok), _ptr(ids),
+                            _ptr(wts), _ptr(gap), _ptr(y))
+    _check(rc, "oracle_layer")
+    return ids, wts, gap, y
+
+
+def rmsnorm(v, gamma=None, eps=1e-6):
+    """Zero-centred RMSNorm of bf16 rows; bf16 out (uint16)."""
+    v = _c(v, np.uint16)
+    gamma = _c(gamma, np.float32)
+    T, d = v.shape
+    out = np.zeros((T, d), np.uint16)
+    _check(lib().oracle_rmsnorm(T, d, _ptr(v), _ptr(gamma), float(eps), _ptr(out)), "oracle_rmsnorm")
+    return out

@@ -1,0 +1,420 @@
+"""Pins of the CPU oracle against things other than itself.
+
+The oracle (oracle/moe_oracle.cc) is the parity reference for the GPU library,
+so each of its functions is tied here to brute force, closed forms, library
+routines on special cases, or invariants that a plausible slip (a transposed
+operand, a swapped gate/up branch, a wrong sign, a lost tie rule, an
+off-by-one in the permutation) would break.  Pages (by title):
+"Step 3.5 Flash: Open Frontier-Level Intelligence with 11B Active Parameters"
+(§2.2, §2.2.2, §4.1.2) and "Step 3.5 Flash 技术论文深度解读" (architecture
+table; SwiGLU gate/up branches in the activation-explosion causes).
+"""
+import itertools
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+import torch.nn.functional as F
+
+import oracle
+from tests._util import from_bf16, rand_bf16, rel_l2, to_bf16
+
+
+def _beta(scores, bias):
+    # Biased score in float32, as the routing definition adds them.
+    return (scores.astype(np.float32) + bias.astype(np.float32)).astype(np.float32)
+
+
+def _brute_force_topk(beta_row, k):
+    """Best k-subset by total biased score; among equal totals the
+    lexicographically smallest sorted index tuple (= lower index wins)."""
+    best, best_sum = None, None
+    for sub in itertools.combinations(range(len(beta_row)), k):
+        s = float(np.sum(beta_row[list(sub)].astype(np.float64)))
+        if best is None or s > best_sum:
+            best, best_sum = sub, s
+    return np.array(best, np.int32)
+
+
+# ---------------------------------------------------------------- routing --
+
+@pytest.mark.parametrize("E,k", [(5, 1), (8, 2), (8, 3), (16, 2), (12, 3)])
+def test_route_matches_brute_force_subsets(E, k):
+    rng = np.random.default_rng(100 + E * 10 + k)
+    T, d = 24, 64
+    x = rand_bf16(rng, (T, d))
+    wr = rand_bf16(rng, (E, d), 0.05)
+    b = rng.uniform(-0.05, 0.05, E).astype(np.float32)
+    ids, w, gap, s = oracle.route(x, wr, b, k, want_scores=True)
+    beta = _beta(s, b)
+    for t in range(T):
+        np.testing.assert_array_equal(ids[t], _brute_force_topk(beta[t], k))
+        srt = np.sort(beta[t].astype(np.float64))[::-1]
+        assert gap[t] == np.float32(srt[k - 1] - srt[k])
+
+
+def test_route_tie_goes_to_lower_index():
+    # Experts 1 and 4 (and 2 and 6) get identical router rows and biases, so
+    # their biased scores tie exactly; the lower index must win.
+    rng = np.random.default_rng(7)
+    T, d, E, k = 16, 64, 8, 3
+    x = rand_bf16(rng, (T, d))
+    wr = rand_bf16(rng, (E, d), 0.05)
+    wr[4] = wr[1]
+    wr[6] = wr[2]
+    b = np.zeros(E, np.float32)
+    ids, _, gap, s = oracle.route(x, wr, b, k, want_scores=True)
+    beta = _beta(s, b)
+    assert np.all(beta[:, 1] == beta[:, 4])
+    for t in range(T):
+        np.testing.assert_array_equal(ids[t], _brute_force_topk(beta[t], k))
+    # All experts tied: the first k indices are chosen.
+    ids0, w0, gap0, _ = oracle.route(np.zeros((3, d), np.uint16), wr, b, k)
+    np.testing.assert_array_equal(ids0, np.tile(np.arange(k), (3, 1)))
+    np.testing.assert_array_equal(gap0, 0.0)
+    np.testing.assert_allclose(w0, 1.0 / k, rtol=1e-7)
+
+
+@pytest.mark.parametrize("E,k", [(64, 8), (288, 8), (288, 16)])
+def test_route_many_ties_at_full_expert_count(E, k):
+    # x = 0 makes every score 0.5, so the biased scores tie in whole groups
+    # (bias drawn from a handful of values); the chosen set must be the k
+    # best bias values with the lowest indices inside the tied group.
+    rng = np.random.default_rng(E + k)
+    d = 64
+    wr = rand_bf16(rng, (E, d), 0.05)
+    b = (rng.integers(0, 4, E) * 0.125).astype(np.float32)
+    x = np.zeros((4, d), np.uint16)
+    ids, w, gap, _ = oracle.route(x, wr, b, k)
+    order = np.lexsort((np.arange(E), -b.astype(np.float64)))
+    for t in range(4):
+        np.testing.assert_array_equal(ids[t], np.sort(order[:k]))
+
+
+def test_route_scores_are_library_sigmoid_of_logits():
+    rng = np.random.default_rng(11)
+    T, d, E, k = 32, 256, 16, 2
+    x = rand_bf16(rng, (T, d))
+    wr = rand_bf16(rng, (E, d), 0.02)
+    b = np.zeros(E, np.float32)
+    c = rng.uniform(-1, 1, E).astype(np.float32)
+    _, _, _, s = oracle.route(x, wr, b, k, logit_bias=c, want_scores=True)
+    z = from_bf16(x).astype(np.float64) @ from_bf16(wr).astype(np.float64).T + c.astype(np.float64)
+    np.testing.assert_allclose(s, scipy.special.expit(z), rtol=0, atol=3e-7)
+
+
+def test_route_one_hot_router_closed_form():
+    # Router row e is a_e times the unit vector at column pi(e) (pi not an
+    # involution), so z[t,e] = a_e * x[t, pi(e)] exactly: a transposed router
+    # or a wrong sign would select different experts.
+    rng = np.random.default_rng(12)
+    T, d, E, k = 40, 64, 10, 3
+    pi = rng.permutation(d)[:E]
+    a = np.linspace(0.5, 2.0, E).astype(np.float32)
+    wr_f = np.zeros((E, d), np.float32)
+    wr_f[np.arange(E), pi] = a
+    wr = to_bf16(wr_f)
+    x = rand_bf16(rng, (T, d))
+    b = rng.uniform(-0.1, 0.1, E).astype(np.float32)
+    ids, w, _, s = oracle.route(x, wr, b, k, want_scores=True)
+    z = from_bf16(x)[:, pi].astype(np.float64) * from_bf16(wr)[np.arange(E), pi].astype(np.float64)
+    np.testing.assert_allclose(s, scipy.special.expit(z), rtol=0, atol=1e-7)
+    beta = _beta(s, b)
+    for t in range(T):
+        order = np.lexsort((np.arange(E), -beta[t].astype(np.float64)))
+        np.testing.assert_array_equal(ids[t], np.sort(order[:k]))
+        np.testing.assert_allclose(w[t], s[t, ids[t]] / s[t, ids[t]].astype(np.float64).sum(), rtol=1e-6)
+
+
+def test_forced_selection_by_bias():
+    # Scores lie in (0, 1), so +1 on a k-set forces that set for every token.
+    rng = np.random.default_rng(13)
+    T, d, E, k = 50, 128, 16, 3
+    S = np.array([2, 9, 14])
+    x = rand_bf16(rng, (T, d))
+    wr = rand_bf16(rng, (E, d), 0.05)
+    b = np.zeros(E, np.float32)
+    b[S] = 1.0
+    ids, w, _, s = oracle.route(x, wr, b, k, want_scores=True)
+    np.testing.assert_array_equal(ids, np.tile(S, (T, 1)))
+    # Weights use the unbiased scores of the chosen set.
+    expect = s[:, S] / s[:, S].astype(np.float64).sum(1, keepdims=True)
+    np.testing.assert_allclose(w, expect, rtol=1e-6)
+
+
+def test_all_tokens_to_one_expert_and_k1_weight_is_one():
+    rng = np.random.default_rng(14)
+    T, d, E = 33, 64, 8
+    x = rand_bf16(rng, (T, d))
+    wr = rand_bf16(rng, (E, d), 0.05)
+    b = np.zeros(E, np.float32)
+    b[5] = 10.0
+    ids, w, gap, _ = oracle.route(x, wr, b, 1)
+    assert np.all(ids == 5)
+    assert np.all(w == 1.0)
+    assert np.all(gap > 8.0)
+    b2 = rng.uniform(-0.05, 0.05, E).astype(np.float32)
+    _, w2, _, _ = oracle.route(x, wr, b2, 1)
+    assert np.all(w2 == 1.0)
+
+
+def test_bias_is_used_for_selection_only():
+    rng = np.random.default_rng(15)
+    T, d, E, k = 30, 128, 12, 3
+    x = rand_bf16(rng, (T, d))
+    wr = rand_bf16(rng, (E, d), 0.05)
+    b = rng.uniform(-0.05, 0.05, E).astype(np.float32)
+    ids, w, gap, _ = oracle.route(x, wr, b, k)
+    # Shift all biases by the same amount: the set cannot change (up to
+    # rounding of beta, which the gap bounds), and the weights must not move.
+    for shift in (0.25, -0.125, 0.0625):
+        ids2, w2, _, _ = oracle.route(x, wr, b + np.float32(shift), k)
+        safe = gap > 1e-6
+        np.testing.assert_array_equal(ids2[safe], ids[safe])
+        np.testing.assert_array_equal(w2[safe], w[safe])
+    # Lower the bias of every expert outside each token's set: same set, same
+    # weights, bit for bit.
+    for t in range(T):
+        b3 = b.copy()
+        out = np.setdiff1d(np.arange(E), ids[t])
+        b3[out] -= 0.5
+        ids3, w3, _, _ = oracle.route(x[t:t + 1], wr, b3, k)
+        np.testing.assert_array_equal(ids3[0], ids[t])
+        np.testing.assert_array_equal(w3[0], w[t])
+
+
+def test_k_equals_E_weights_are_normalised_library_sigmoids():
+    rng = np.random.default_rng(16)
+    T, d, E = 20, 64, 6
+    x = rand_bf16(rng, (T, d))
+    wr = rand_bf16(rng, (E, d), 0.1)
+    b = rng.uniform(-0.1, 0.1, E).astype(np.float32)
+    ids, w, gap, _ = oracle.route(x, wr, b, E)
+    np.testing.assert_array_equal(ids, np.tile(np.arange(E), (T, 1)))
+    assert np.all(np.isinf(gap))
+    z = from_bf16(x).astype(np.float64) @ from_bf16(wr).astype(np.float64).T
+    s = scipy.special.expit(z)
+    np.testing.assert_allclose(w, s / s.sum(1, keepdims=True), rtol=2e-6)
+
+
+@pytest.mark.parametrize("T,d,E,k,bias", [(64, 256, 16, 2, 0.05), (48, 512, 288, 8, 0.1)])
+def test_route_invariants(T, d, E, k, bias):
+    rng = np.random.default_rng(T + E)
+    x = rand_bf16(rng, (T, d))
+    wr = rand_bf16(rng, (E, d), 0.02)
+    b = rng.uniform(-bias, bias, E).astype(np.float32)
+    ids, w, gap, _ = oracle.route(x, wr, b, k)
+    assert ids.shape == (T, k)
+    assert np.all((ids >= 0) & (ids < E))
+    assert np.all(np.diff(ids, axis=1) > 0)          # distinct and ascending
+    assert np.all(w >= 0)
+    np.testing.assert_allclose(w.astype(np.float64).sum(1), 1.0, atol=1e-6)
+    assert np.all(gap >= 0)
+
+
+# ------------------------------------------------------------ permutation --
+
+def _random_ids(rng, T, E, k):
+    return np.stack([np.sort(rng.choice(E, k, replace=False)) for _ in range(T)]).astype(np.int32).reshape(T, k)
+
+
+@pytest.mark.parametrize("T,E,k", [(0, 8, 2), (1, 8, 8), (37, 16, 2), (200, 64, 8), (513, 288, 8)])
+def test_permute_is_stable_counting_sort(T, E, k):
+    rng = np.random.default_rng(T * 7 + E)
+    ids = _random_ids(rng, T, E, k) if T else np.zeros((0, k), np.int32)
+    counts, offsets, perm, pos = oracle.permute(ids, E)
+    flat = ids.ravel()
+    np.testing.assert_array_equal(counts, np.bincount(flat, minlength=E))
+    np.testing.assert_array_equal(offsets, np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))]))
+    np.testing.assert_array_equal(perm, np.argsort(flat, kind="stable"))
+    # Invariants: bijection, inverse, grouping.
+    assert counts.sum() == T * k and offsets[-1] == T * k
+    assert np.all(np.diff(offsets) >= 0)
+    np.testing.assert_array_equal(np.sort(perm), np.arange(T * k))
+    np.testing.assert_array_equal(pos[perm], np.arange(T * k))
+    for e in range(E):
+        rows = perm[offsets[e]:offsets[e + 1]]
+        assert np.all(flat[rows] == e)
+        assert np.all(np.diff(rows // k) > 0)            # ascending token order
+
+
+def test_permute_skewed_loads():
+    T, E, k = 100, 16, 2
+    ids = np.zeros((T, k), np.int32)
+    ids[:, 0] = 3
+    ids[:, 1] = 7
+    counts, offsets, perm, pos = oracle.permute(ids, E)
+    assert counts[3] == T and counts[7] == T and counts.sum() == 2 * T
+    np.testing.assert_array_equal(perm[:T], np.arange(T) * 2)
+    np.testing.assert_array_equal(perm[T:], np.arange(T) * 2 + 1)
+
+
+# ----------------------------------------------------------------- experts --
+
+def _torch_swiglu(x, w_gu, w_d):
+    """Textbook SwiGLU with library routines, float64: W_d (silu(W_g x) * W_u x)."""
+    xt = torch.from_numpy(from_bf16(x).astype(np.float64))
+    gu = torch.from_numpy(from_bf16(w_gu).astype(np.float64))
+    wd = torch.from_numpy(from_bf16(w_d).astype(np.float64))
+    h = gu.shape[0] // 2
+    a = F.silu(xt @ gu[:h].T) * (xt @ gu[h:].T)
+    return (a @ wd.T).numpy()
+
+
+def test_expert_permutation_matrix_closed_form():
+    # W_g row j = c_j e_{pi(j)}, W_u row j = e_{rho(j)}, W_d row i = e_{tau(i)}:
+    # out_i = silu(c_tau(i) x_{pi(tau(i))}) * x_{rho(tau(i))}.  Swapping the
+    # gate and up halves, transposing any matrix or flipping SiLU's sign
+    # changes the result.
+    rng = np.random.default_rng(21)
+    d, h = 64, 32
+    pi = rng.permutation(d)[:h]
+    rho = rng.permutation(d)[:h]
+    tau = rng.integers(0, h, d)
+    c = np.linspace(-3, 3, h).astype(np.float32)
+    gu = np.zeros((2 * h, d), np.float32)
+    gu[np.arange(h), pi] = c
+    gu[h + np.arange(h), rho] = 1.0
+    wd = np.zeros((d, h), np.float32)
+    wd[np.arange(d), tau] = 1.0
+    x = rand_bf16(rng, d)
+    out = oracle.expert(x, to_bf16(gu), to_bf16(wd))
+    xf = from_bf16(x).astype(np.float64)
+    cf = from_bf16(to_bf16(c)).astype(np.float64)
+    g = cf[tau] * xf[pi[tau]]
+    expect = F.silu(torch.from_numpy(g)).numpy() * xf[rho[tau]]
+    np.testing.assert_allclose(out, expect, rtol=1e-6, atol=1e-30)
+
+
+def test_expert_matches_library_swiglu():
+    rng = np.random.default_rng(22)
+    d, h = 128, 64
+    gu = rand_bf16(rng, (2 * h, d), 0.05)
+    wd = rand_bf16(rng, (d, h), 0.05)
+    for _ in range(4):
+        x = rand_bf16(rng, d)
+        out = oracle.expert(x, gu, wd)
+        ref = _torch_swiglu(x[None], gu, wd)[0]
+        assert rel_l2(out, ref) < 1e-6
+
+
+def test_expert_zero_input_gives_zero():
+    rng = np.random.default_rng(23)
+    d, h = 64, 32
+    out = oracle.expert(np.zeros(d, np.uint16), rand_bf16(rng, (2 * h, d)), rand_bf16(rng, (d, h)))
+    assert np.all(out == 0)
+
+
+# ------------------------------------------------------------- whole layer --
+
+def _layer_inputs(rng, T, d, E, k, h, hs, bias=0.05):
+    x = rand_bf16(rng, (T, d))
+    wr = rand_bf16(rng, (E, d), 0.05)
+    b = rng.uniform(-bias, bias, E).astype(np.float32)
+    gu = [rand_bf16(rng, (2 * h, d), 0.05) for _ in range(E)]
+    wd = [rand_bf16(rng, (d, h), 0.05) for _ in range(E)]
+    sgu = rand_bf16(rng, (2 * hs, d), 0.05) if hs else None
+    swd = rand_bf16(rng, (d, hs), 0.05) if hs else None
+    return x, wr, b, gu, wd, sgu, swd
+
+
+def test_layer_identical_experts_closed_form():
+    # Every expert has the same weights, so the routed part is
+    # routed_scale * SwiGLU(x) (weights sum to one) whatever the routing.
+    rng = np.random.default_rng(31)
+    T, d, E, k, h, hs = 12, 64, 8, 3, 32, 16
+    x, wr, b, gu, wd, sgu, swd = _layer_inputs(rng, T, d, E, k, h, hs)
+    gu = [gu[0]] * E
+    wd = [wd[0]] * E
+    for lam in (1.0, 0.5):
+        _, _, _, y = oracle.layer(x, wr, b, k, gu, wd, sgu, swd, routed_scale=lam)
+        ref = lam * _torch_swiglu(x, gu[0], wd[0]) + _torch_swiglu(x, sgu, swd)
+        assert rel_l2(y, ref) < 2e-6
+
+
+def test_layer_single_expert_is_dense_swiglu_plus_shared():
+    rng = np.random.default_rng(32)
+    T, d, E, k, h, hs = 9, 128, 1, 1, 64, 32
+    x, wr, b, gu, wd, sgu, swd = _layer_inputs(rng, T, d, E, k, h, hs)
+    ids, w, _, y = oracle.layer(x, wr, b, k, gu, wd, sgu, swd)
+    assert np.all(ids == 0) and np.all(w == 1.0)
+    ref = _torch_swiglu(x, gu[0], wd[0]) + _torch_swiglu(x, sgu, swd)
+    assert rel_l2(y, ref) < 1e-6
+
+
+def test_layer_weighted_sum_over_chosen_experts():
+    # Output = shared + sum_j w_j * expert_j(x) with w from library sigmoids of
+    # the chosen experts; experts pinned by the tests above.
+    rng = np.random.default_rng(33)
+    T, d, E, k, h, hs = 10, 64, 6, 2, 32, 32
+    x, wr, b, gu, wd, sgu, swd = _layer_inputs(rng, T, d, E, k, h, hs)
+    ids, w, _, y = oracle.layer(x, wr, b, k, gu, wd, sgu, swd)
+    z = from_bf16(x).astype(np.float64) @ from_bf16(wr).astype(np.float64).T
+    s = scipy.special.expit(z)
+    ref_sh = _torch_swiglu(x, sgu, swd)
+    for t in range(T):
+        sel = ids[t]
+        wt = s[t, sel] / s[t, sel].sum()
+        np.testing.assert_allclose(w[t], wt, rtol=2e-6)
+        routed = sum(wt[j] * _torch_swiglu(x[t:t + 1], gu[e], wd[e])[0] for j, e in enumerate(sel))
+        assert rel_l2(y[t], ref_sh[t] + routed) < 2e-6
+
+
+def test_layer_zero_input_and_shared_off():
+    rng = np.random.default_rng(34)
+    T, d, E, k, h, hs = 6, 64, 8, 2, 32, 32
+    x, wr, b, gu, wd, sgu, swd = _layer_inputs(rng, T, d, E, k, h, hs)
+    ids0, w0, _, y0 = oracle.layer(np.zeros_like(x), wr, b, k, gu, wd, sgu, swd)
+    assert np.all(y0 == 0)
+    # z = 0 gives equal scores: selection is by bias alone, weights equal.
+    order = np.lexsort((np.arange(E), -b.astype(np.float64)))
+    np.testing.assert_array_equal(ids0, np.tile(np.sort(order[:k]), (T, 1)))
+    np.testing.assert_allclose(w0, 1.0 / k, rtol=1e-7)
+    # Shared expert off = full output minus the shared expert's output.
+    _, _, _, y_full = oracle.layer(x, wr, b, k, gu, wd, sgu, swd)
+    _, _, _, y_routed = oracle.layer(x, wr, b, k, gu, wd)
+    assert rel_l2(y_full - y_routed, _torch_swiglu(x, sgu, swd)) < 2e-6
+    # routed_scale = 0 leaves only the shared expert.
+    _, _, _, y_sh = oracle.layer(x, wr, b, k, gu, wd, sgu, swd, routed_scale=0.0)
+    assert rel_l2(y_sh, _torch_swiglu(x, sgu, swd)) < 1e-6
+
+
+def test_layer_token_subset_matches_full():
+    rng = np.random.default_rng(35)
+    T, d, E, k, h, hs = 16, 64, 8, 2, 32, 32
+    x, wr, b, gu, wd, sgu, swd = _layer_inputs(rng, T, d, E, k, h, hs)
+    ids, w, gap, y = oracle.layer(x, wr, b, k, gu, wd, sgu, swd)
+    sub = np.array([15, 3, 7])
+    ids2, w2, gap2, y2 = oracle.layer(x, wr, b, k, gu, wd, sgu, swd, tokens=sub)
+    np.testing.assert_array_equal(ids2, ids[sub])
+    np.testing.assert_array_equal(y2, y[sub])
+    # Missing weights for a selected expert is an error, not a silent zero.
+    gu_missing = list(gu)
+    gu_missing[int(ids[0, 0])] = None
+    wd_missing = list(wd)
+    wd_missing[int(ids[0, 0])] = None
+    with pytest.raises(ValueError):
+        oracle.layer(x, wr, b, k, gu_missing, wd_missing, sgu, swd, tokens=np.array([0]))
+
+
+# ---------------------------------------------------------------- rmsnorm --
+
+def test_rmsnorm_matches_library_and_is_scale_invariant():
+    rng = np.random.default_rng(41)
+    T, d = 16, 256
+    v = rand_bf16(rng, (T, d), 3.0)
+    out = oracle.rmsnorm(v, eps=0.0)
+    ref = F.rms_norm(torch.from_numpy(from_bf16(v).astype(np.float64)), (d,), eps=0.0)
+    ref_bf16 = to_bf16(ref.numpy().astype(np.float32))
+    diff = np.abs(out.astype(np.int32) - ref_bf16.astype(np.int32))
+    assert diff.max() <= 1 and (diff == 0).mean() > 0.999
+    # Power-of-two scaling of the input is exact, so the output is unchanged.
+    v4 = to_bf16(from_bf16(v) * 4.0)
+    np.testing.assert_array_equal(oracle.rmsnorm(v4, eps=0.0), out)
+    # Zero-centred gain: weight (1 + gamma).
+    gamma = np.full(d, 1.0, np.float32)
+    out2 = oracle.rmsnorm(v, gamma=gamma, eps=0.0)
+    np.testing.assert_array_equal(from_bf16(out2), from_bf16(out) * 2.0)
+    rms = np.sqrt((from_bf16(out).astype(np.float64) ** 2).mean(1))
+    np.testing.assert_allclose(rms, 1.0, atol=4e-3)
