@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Throughput of the sparse MoE FFN layer forward (libmoe) on one MI355X.
+
+A step is one forward pass of the layer over one batch: moe_route ->
+moe_permute -> moe_expert_gate_up -> moe_expert_down -> moe_combine on the main
+stream, with moe_shared_swiglu concurrently on a second stream (joined before
+the combine).  Inputs and weights are resident in HBM before timing starts;
+they come from the seeded generator (synthetic values with the shapes and
+distributions of the model's layer; no trained weights exist here).
+
+Default workload: the decode batch (T=64 tokens, d_model 4096, 288 experts,
+top-8, expert and shared hidden 1280).  The prefill batch (T=8192) is timed
+after it and reported in the "prefill" object.  Prints one JSON line.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill]
+                       [--no-cpu-baseline] [--cpu-sample N]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tok/s; % HBM BW at T=64, % bf16 MFMA peak at T=8192"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    src = os.path.join(ROOT, "sparse_moe_transformer_ffn_amd", "csrc", "expert.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source (else None)."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class Workload:
+    """Device tensors of one recipe, filled by the generator."""
+
+    def __init__(self, cfg, dev):
+        import numpy as np
+        import torch
+        import moegen
+        import sparse_moe_transformer_ffn_amd as moe
+        self.cfg = cfg
+        self.x_h = moegen.x(cfg)
+        self.wr_h = moegen.router(cfg)
+        self.b_h = moegen.sel_bias(cfg)
+        self.c_h = moegen.logit_bias(cfg)
+
+        def bf16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        self.x, self.wr = bf16(self.x_h), bf16(self.wr_h)
+        self.b = torch.from_numpy(self.b_h).to(dev)
+        self.c = None if self.c_h is None else torch.from_numpy(self.c_h).to(dev)
+        E, d, h, hs = cfg.E, cfg.d, cfg.h, cfg.hs
+        self.w_gu = torch.empty((E, 2 * h, d), dtype=torch.bfloat16, device=dev)
+        self.w_d = torch.empty((E, d, h), dtype=torch.bfloat16, device=dev)
+        self.ws_gu = torch.empty((2 * hs, d), dtype=torch.bfloat16, device=dev)
+        self.ws_d = torch.empty((d, hs), dtype=torch.bfloat16, device=dev)
+        s = torch.cuda.current_stream().cuda_stream
+        moegen.fill_experts_device(cfg, 0, self.w_gu.data_ptr(), self.w_d.data_ptr(), s)
+        moegen.fill_shared_device(cfg, 0, self.ws_gu.data_ptr(), self.ws_d.data_ptr(), s)
+        self.buf = moe.LayerBuffers.allocate(cfg.T, d, E, cfg.k, h, hs, device=dev)
+        self.hid = torch.empty((cfg.T * cfg.k, h), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+
+    def step(self, main, side, ev=None):
+        """One forward; ev = (before gate_up, after gate_up, after down) events."""
+        import sparse_moe_transformer_ffn_amd as moe
+        b, sh, c = self.buf, self.buf.shape, self.cfg
+        side.wait_stream(main)
+        moe.moe_shared_swiglu(sh, self.x, self.ws_gu, self.ws_d, b.y_shared, b.workspace_shared, side)
+        moe.moe_route(sh, self.x, self.wr, self.b, self.c, b.topk_ids, b.topk_weights, b.expert_counts, b.topk_gap,
+                      b.workspace, main)
+        moe.moe_permute(sh, b.topk_ids, b.expert_offsets, b.perm_pairs, b.pair_pos, b.workspace, main)
+        if ev:
+            ev[0].record(main)
+        moe.moe_expert_gate_up(sh, self.x, b.expert_offsets, b.perm_pairs, self.w_gu, self.hid, main)
+        if ev:
+            ev[1].record(main)
+        moe.moe_expert_down(sh, b.expert_offsets, self.hid, self.w_d, b.y_perm, main)
+        if ev:
+            ev[2].record(main)
+        main.wait_stream(side)
+        moe.moe_combine(sh, b.y_perm, b.pair_pos, b.topk_weights, b.y_shared, c.routed_scale, b.y, main)
+
+
+def algorithmic(cfg, n_touched):
+    """Bytes and flops the method itself must move / compute (not the dense
+    E-expert work it avoids; intermediates excluded)."""
+    T, d, E, k, h, hs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, cfg.hs
+    w_expert = 3 * d * h * 2
+    step_bytes = n_touched * w_expert + 3 * d * hs * 2 + E * d * 2 + T * d * 2 * 2 + T * k * 4 * 4
+    step_flops = 2 * T * k * 3 * d * h + 2 * T * 3 * d * hs + 2 * T * d * E
+    gate_up_bytes = n_touched * 2 * h * d * 2 + T * d * 2 + T * k * h * 2
+    gate_up_flops = 2 * T * k * 2 * h * d
+    down_bytes = n_touched * d * h * 2 + T * k * h * 2 + T * k * d * 2
+    down_flops = 2 * T * k * h * d
+    return dict(step_bytes=step_bytes, step_flops=step_flops, gate_up_bytes=gate_up_bytes,
+                gate_up_flops=gate_up_flops, down_bytes=down_bytes, down_flops=down_flops)
+
+
+def time_workload(cfg, steps, warmup, dev):
+    import numpy as np
+    import torch
+    wl = Workload(cfg, dev)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream(dev)
+    for _ in range(warmup):
+        wl.step(main, side)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(main)
+    for i in range(steps):
+        wl.step(main, side, evs[i])
+    t1.record(main)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1) / steps
+    gate_up_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    down_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    counts = wl.buf.expert_counts.cpu().numpy()
+    n_touched = int((counts > 0).sum())
+    alg = algorithmic(cfg, n_touched)
+    res = dict(ms_per_step=ms, wall_ms_per_step=wall * 1e3 / steps, gate_up_ms=gate_up_ms, down_ms=down_ms,
+               n_touched=n_touched, max_load=int(counts.max()), idle_experts=int((counts == 0).sum()), alg=alg)
+    return wl, res
+
+
+def cpu_baseline(wl, n_sample):
+    """The CPU oracle, single-threaded, on a bounded sample of the same
+    workload's tokens (whole layer per token).  Weight generation is not
+    timed."""
+    import numpy as np
+    import moegen
+    import oracle
+    cfg = wl.cfg
+    tokens = np.linspace(0, cfg.T - 1, n_sample).astype(np.int32)
+    ids, _, _, _ = oracle.route(wl.x_h[tokens], wl.wr_h, wl.b_h, cfg.k, logit_bias=wl.c_h)
+    needed = sorted(set(ids.ravel().tolist()))
+    ew = moegen.expert_weights_host(cfg, 0, needed)
+    gu = [ew[e][0] if e in ew else None for e in range(cfg.E)]
+    wd = [ew[e][1] if e in ew else None for e in range(cfg.E)]
+    sgu, swd = moegen.shared_weights_host(cfg)
+    t = time.perf_counter()
+    oracle.layer(wl.x_h, wl.wr_h, wl.b_h, cfg.k, gu, wd, sgu, swd, cfg.routed_scale, logit_bias=wl.c_h,
+                 tokens=tokens)
+    dt = time.perf_counter() - t
+    return {"value": n_sample / dt, "unit": "tok/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_sample} of the {cfg.T} tokens of the {cfg.name} workload, whole layer per token "
+                      f"(route over {cfg.E} experts, {cfg.k} routed + 1 shared SwiGLU expert, combine); "
+                      f"{dt:.1f} s on one host thread"}
+
+
+def roofline(kind, achieved, traffic):
+    if kind == "hbm":
+        return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic}
+    return {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / BF16_PEAK_TFLOPS, "traffic": traffic}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=16)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the layer's hot path is built and timed on a single MI355X "
+              "(no expert parallelism across GPUs in this library). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moegen
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    cfg = moegen.CONFIGS[1]
+    wl, r = time_workload(cfg, args.steps, args.warmup, dev)
+    alg = r["alg"]
+    tok_s = cfg.T / (r["ms_per_step"] * 1e-3)
+    gate_up_gbs = alg["gate_up_bytes"] / (r["gate_up_ms"] * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": tok_s, "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.workload, "tokens": cfg.T, "d_model": cfg.d, "experts": cfg.E, "top_k": cfg.k,
+                   "expert_hidden": cfg.h, "shared_hidden": cfg.hs, "seed": cfg.seed},
+        "roofline": roofline("hbm", gate_up_gbs, load_traffic("decode", "gate_up")),
+        "step": {"algorithmic_bytes": alg["step_bytes"], "algorithmic_flops": alg["step_flops"],
+                 "hbm_gbs": alg["step_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9,
+                 "hbm_frac": alg["step_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                 "touched_experts": r["n_touched"], "max_load": r["max_load"], "idle_experts": r["idle_experts"]},
+        "kernels": {"gate_up_ms": r["gate_up_ms"], "down_ms": r["down_ms"],
+                    "gate_up_gbs": gate_up_gbs,
+                    "down_gbs": alg["down_bytes"] / (r["down_ms"] * 1e-3) / 1e9},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
+    del wl
+    torch.cuda.empty_cache()
+
+    if not args.no_prefill:
+        pcfg = moegen.CONFIGS[2]
+        pwl, p = time_workload(pcfg, args.prefill_steps, args.warmup, dev)
+        palg = p["alg"]
+        gate_up_tf = palg["gate_up_flops"] / (p["gate_up_ms"] * 1e-3) / 1e12
+        step_tf = palg["step_flops"] / (p["ms_per_step"] * 1e-3) / 1e12
+        out["prefill"] = {
+            "workload": pcfg.workload, "tok_s": pcfg.T / (p["ms_per_step"] * 1e-3), "ms_per_step": p["ms_per_step"],
+            "steps": args.prefill_steps, "step_tflops": step_tf, "step_mfma_frac": step_tf / BF16_PEAK_TFLOPS,
+            "roofline": roofline("mfma", gate_up_tf, load_traffic("prefill", "gate_up")),
+            "kernels": {"gate_up_ms": p["gate_up_ms"], "down_ms": p["down_ms"],
+                        "down_tflops": palg["down_flops"] / (p["down_ms"] * 1e-3) / 1e12},
+            "touched_experts": p["n_touched"], "max_load": p["max_load"], "idle_experts": p["idle_experts"],
+        }
+        del pwl
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

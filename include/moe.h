@@ -1,0 +1,180 @@
+/* moe.h -- libmoe: forward pass of one fine-grained sparse Mixture-of-Experts
+ * FFN layer on an AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (by title):
+ *   [Blog]    "Step 3.5 Flash: Open Frontier-Level Intelligence with 11B Active
+ *             Parameters" (section-numbered summary of the paper)
+ *   [Digest]  "Step 3.5 Flash 技术论文深度解读：196B MoE 如何做到 11B 激活打 37B"
+ *   [Article] "StepFun团队Step 3.5 Flash：11B参数实现前沿智能水平"
+ *
+ * The layer ([Blog] §2.2 and §2.2.2; [Digest] architecture table): a router
+ * scores every token against E routed experts, a bias used only for selection
+ * steers the top-k choice (loss-free balancing, [Digest] note under the
+ * architecture table; [Article] §9), the chosen SwiGLU experts ([Digest]
+ * activation-explosion cause 3: gate and up branches) run on the token, one
+ * shared expert runs on every token, and the routed outputs are weighted,
+ * explicitly scaled ([Blog] §4.1.2) and added to the shared output.  The
+ * pages' own kernels fuse MoE gather/scatter with a grouped GEMM ([Blog]
+ * §3.2.4); here the same structure is five calls:
+ *
+ *   moe_route          router logits, sigmoid, biased top-k, weights, counts
+ *   moe_permute        stable (expert, token) permutation of the k*T pairs
+ *   moe_expert_swiglu  grouped gate/up GEMM + SwiGLU, then grouped down GEMM
+ *                      (also callable as its two phases, moe_expert_gate_up
+ *                      and moe_expert_down)
+ *   moe_shared_swiglu  the always-on shared expert
+ *   moe_combine        y = y_shared + routed_scale * sum_j w_j * y_perm[pos]
+ *
+ * plus moe_rmsnorm, the zero-centred RMSNorm that sits in front of every FFN
+ * sub-layer ([Blog] §2.2, Figure 2 caption), used between stacked layers.
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates or frees device memory and keeps no state between
+ *     calls.  bf16 tensors are passed as uint16_t bit patterns.
+ *   - Matrices are row-major [out][in] (the reduction dimension contiguous).
+ *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *     Calls only enqueue work: they never synchronise and never copy to the
+ *     host.  Asynchronous kernel faults surface at the caller's next
+ *     synchronisation.
+ *   - Arguments are validated on the host before anything is enqueued; on a
+ *     validation failure nothing is enqueued and the error code is returned.
+ *     A failed kernel launch returns MOE_ERR_HIP.  No C++ exception crosses
+ *     this interface.
+ *   - Device data coming from elsewhere (ids, offsets, positions) is a
+ *     precondition, not checked: it must be what moe_route / moe_permute
+ *     produce for the same shape.
+ *   - `workspace` is caller-provided device scratch of at least
+ *     moe_workspace_bytes() bytes, 256-byte aligned.  Nothing in it survives
+ *     a call.  Calls that may run concurrently (on different streams) need
+ *     distinct workspaces.
+ *   - Vector-loaded tensors must be 16-byte aligned (MOE_ERR_MISALIGNED).
+ */
+#ifndef LIBMOE_MOE_H_
+#define LIBMOE_MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Layer shape.  Limits (MOE_ERR_UNSUPPORTED_SHAPE otherwise):
+ *   0 <= num_tokens <= 1048576
+ *   64 <= d_model <= 65536, d_model % 64 == 0
+ *   1 <= num_experts <= 1024
+ *   1 <= top_k <= min(num_experts, 16)
+ *   64 <= d_expert <= 65536, d_expert % 64 == 0
+ *   d_shared == 0 (no shared expert) or as d_expert                         */
+typedef struct moe_shape {
+  int32_t num_tokens;  /* T   */
+  int32_t d_model;     /* d   */
+  int32_t num_experts; /* E   */
+  int32_t top_k;       /* k   */
+  int32_t d_expert;    /* h   routed expert hidden size  */
+  int32_t d_shared;    /* h_s shared expert hidden size (0: none) */
+} moe_shape;
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,   /* NULL required pointer, NULL shape, bad scalar */
+  MOE_ERR_UNSUPPORTED_SHAPE = 2,  /* shape outside the limits above */
+  MOE_ERR_MISALIGNED = 3,         /* a vector-loaded pointer not 16-byte aligned */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 4,
+  MOE_ERR_HIP = 5                 /* a HIP launch failed */
+} moe_status;
+
+/* Static, human-readable name of a status code. */
+const char* moe_status_str(moe_status status);
+
+/* Checks a shape against the limits above. */
+moe_status moe_check_shape(const moe_shape* shape);
+
+/* Device workspace every call below needs for this shape (the maximum over
+ * the calls), a multiple of 256 bytes.  *bytes is written on success. */
+moe_status moe_workspace_bytes(const moe_shape* shape, size_t* bytes);
+
+/* Router ([Blog] §2.2.2: routing probabilities p_{t,e}, top-K set S_t, mask
+ * s_{t,e}; [Digest]: loss-free balancing by a bias adjustment).
+ *   z[t,e]    = sum_i x[t,i] * w_router[e,i]  (+ logit_bias[e])
+ *   s[t,e]    = 1 / (1 + exp(-z[t,e]))
+ *   beta[t,e] = s[t,e] + sel_bias[e]                 (selection only)
+ *   S_t       = the k largest beta[t,.], ties to the lower expert index
+ * In:  x [T,d] bf16; w_router [E,d] bf16; sel_bias [E] f32;
+ *      logit_bias [E] f32 or NULL (a per-expert additive logit term).
+ * Out: topk_ids [T,k] int32, S_t in ascending expert order;
+ *      topk_weights [T,k] f32, w = s / sum_{S_t} s, aligned with topk_ids;
+ *      expert_counts [E] int32, |{t : e in S_t}| (overwritten, not added to);
+ *      topk_gap [T] f32 or NULL: k-th minus (k+1)-th largest beta
+ *      (+inf when k == E).
+ * Math in f32 (bf16 products, f32 accumulation).                            */
+moe_status moe_route(const moe_shape* shape, const uint16_t* x, const uint16_t* w_router, const float* sel_bias,
+                     const float* logit_bias, int32_t* topk_ids, float* topk_weights, int32_t* expert_counts,
+                     float* topk_gap, void* workspace, size_t ws_bytes, void* stream);
+
+/* Token-to-expert permutation: the gather/scatter order of the grouped
+ * expert GEMMs ([Blog] §3.2.4: fused MoE gather/scatter with grouped GEMM).
+ * Pair p = t*k + j is token t's j-th chosen expert.
+ * In:  topk_ids [T,k] int32 (as moe_route writes them).
+ * Out: expert_offsets [E+1] int32, exclusive prefix sum of the per-expert
+ *      pair counts (expert_offsets[E] = T*k);
+ *      perm_pairs [T*k] int32: row r of the permuted order holds pair
+ *      perm_pairs[r]; rows are ordered by expert, then by token (stable);
+ *      pair_pos [T*k] int32: inverse, pair_pos[perm_pairs[r]] = r.          */
+moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t* expert_offsets,
+                       int32_t* perm_pairs, int32_t* pair_pos, void* workspace, size_t ws_bytes, void* stream);
+
+/* Routed experts ([Digest] architecture table: E SwiGLU experts of hidden h;
+ * activation-explosion cause 3: gate and up projection branches).  For every
+ * permuted row r of expert e, with token t = perm_pairs[r] / k:
+ *   hid[r,:]    = SiLU(W_g^e x[t]) * (W_u^e x[t]),  SiLU(v) = v / (1 + exp(-v))
+ *   y_perm[r,:] = W_d^e hid[r,:]
+ * In:  x [T,d] bf16; expert_offsets [E+1], perm_pairs [T*k] (moe_permute);
+ *      w_gate_up [E, 2h, d] bf16 (rows 0..h-1 gate, h..2h-1 up);
+ *      w_down [E, d, h] bf16.
+ * Out: y_perm [T*k, d] bf16, unweighted expert outputs in permuted order.
+ * hid is rounded to bf16 between the two GEMMs; accumulation is f32.        */
+moe_status moe_expert_swiglu(const moe_shape* shape, const uint16_t* x, const int32_t* expert_offsets,
+                             const int32_t* perm_pairs, const uint16_t* w_gate_up, const uint16_t* w_down,
+                             uint16_t* y_perm, void* workspace, size_t ws_bytes, void* stream);
+
+/* The two phases of moe_expert_swiglu, for callers that keep the hidden
+ * activations themselves.  hid [T*k, h] bf16 (permuted order).             */
+moe_status moe_expert_gate_up(const moe_shape* shape, const uint16_t* x, const int32_t* expert_offsets,
+                              const int32_t* perm_pairs, const uint16_t* w_gate_up, uint16_t* hid, void* stream);
+moe_status moe_expert_down(const moe_shape* shape, const int32_t* expert_offsets, const uint16_t* hid,
+                           const uint16_t* w_down, uint16_t* y_perm, void* stream);
+
+/* Shared expert ([Blog] §2.2: one shared expert, always active):
+ *   y_shared[t,:] = W_d^s (SiLU(W_g^s x[t]) * (W_u^s x[t]))
+ * In:  x [T,d] bf16; ws_gate_up [2h_s, d] bf16; ws_down [d, h_s] bf16.
+ * Out: y_shared [T,d] f32.  Requires d_shared > 0.                          */
+moe_status moe_shared_swiglu(const moe_shape* shape, const uint16_t* x, const uint16_t* ws_gate_up,
+                             const uint16_t* ws_down, float* y_shared, void* workspace, size_t ws_bytes,
+                             void* stream);
+
+/* Weighted scatter-combine ([Blog] §4.1.2: routed-expert aggregation needs
+ * explicit scaling):
+ *   y[t,:] = y_shared[t,:] + routed_scale * sum_{j<k} topk_weights[t,j] * y_perm[pair_pos[t*k+j],:]
+ * summed over j in order (ascending expert id), in f32, stored as bf16.
+ * In:  y_perm [T*k, d] bf16; pair_pos [T*k] int32; topk_weights [T,k] f32;
+ *      y_shared [T,d] f32 or NULL (treated as zero); routed_scale finite.
+ * Out: y [T,d] bf16.                                                        */
+moe_status moe_combine(const moe_shape* shape, const uint16_t* y_perm, const int32_t* pair_pos,
+                       const float* topk_weights, const float* y_shared, float routed_scale, uint16_t* y,
+                       void* stream);
+
+/* Zero-centred RMSNorm of bf16 rows ([Blog] §2.2, Figure 2 caption; the
+ * [Digest] notes the pre-norm placement):
+ *   out[t,i] = in[t,i] / sqrt(mean_i(in[t,:]^2) + eps) * (1 + gamma[i])
+ * gamma [cols] f32 or NULL (unit gain).  in/out [rows, cols] bf16 (may not
+ * alias).  cols % 8 == 0, 8 <= cols <= 65536, rows >= 0, eps >= 0.          */
+moe_status moe_rmsnorm(int32_t rows, int32_t cols, const uint16_t* in, const float* gamma, float eps,
+                       uint16_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMOE_MOE_H_ */

@@ -228,3 +228,33 @@ def fill_shared_device(cfg: Config, layer: int, ws_gu_ptr: int, ws_d_ptr: int, s
 def bf16_to_f32(a: np.ndarray) -> np.ndarray:
     """Decode bf16 bit patterns (uint16) to float32 exactly."""
     return (np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def normal_bf16(seed: int, kind: int, shape, std: float = 1.0) -> np.ndarray:
+    """A free-standing N(0, std^2) bf16 tensor (test inputs for single calls)."""
+    out = np.empty(shape, np.uint16)
+    k = lib().moegen_stream_key(seed, 0, kind, 0)
+    lib().moegen_normal_bf16_host(k, 0, out.size, std, out.ctypes.data, threads())
+    return out
+
+
+def uniform(seed: int, kind: int, n: int) -> np.ndarray:
+    """n uniform [0,1) doubles from a free-standing stream."""
+    u = np.empty(n, np.float64)
+    lib().moegen_uniform_f64_host(lib().moegen_stream_key(seed, 0, kind, 0), 0, n, u.ctypes.data)
+    return u
+
+
+def random_ids(seed: int, T: int, E: int, k: int) -> np.ndarray:
+    """[T, k] int32: k distinct experts per token, ascending (partial
+    Fisher-Yates on a uniform stream) -- synthetic routing for the
+    permutation and expert calls."""
+    u = uniform(seed, 101, T * k).reshape(T, k) if T else np.zeros((0, k))
+    out = np.empty((T, k), np.int32)
+    for t in range(T):
+        pool = list(range(E))
+        for j in range(k):
+            i = j + min(int(u[t, j] * (E - j)), E - j - 1)
+            pool[j], pool[i] = pool[i], pool[j]
+        out[t] = np.sort(pool[:k])
+    return out

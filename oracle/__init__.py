@@ -34,7 +34,9 @@ def lib():
         L.oracle_layer.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
                                    _I, _P, _P, _P, _P, _P]
         L.oracle_rmsnorm.argtypes = [_I, _I, _P, _P, ctypes.c_float, _P]
-        for f in (L.oracle_route, L.oracle_permute, L.oracle_expert, L.oracle_layer, L.oracle_rmsnorm):
+        L.oracle_combine.argtypes = [_I, _I, _I, _P, _P, _P, _P, ctypes.c_float, _P]
+        for f in (L.oracle_route, L.oracle_permute, L.oracle_expert, L.oracle_layer, L.oracle_rmsnorm,
+                  L.oracle_combine):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -140,6 +142,21 @@ def layer(x, w_router, sel_bias, k, w_gu, w_d, ws_gu=None, ws_d=None, routed_sca
                             _ptr(wts), _ptr(gap), _ptr(y))
     _check(rc, "oracle_layer")
     return ids, wts, gap, y
+
+
+def combine(y_perm, pair_pos, weights, y_shared=None, routed_scale=1.0):
+    """y = y_shared + routed_scale * sum_j w[t,j] y_perm[pos[t*k+j]]; f32 [T,d]."""
+    y_perm = _c(y_perm, np.uint16)
+    weights = _c(weights, np.float32)
+    pair_pos = _c(pair_pos, np.int32)
+    y_shared = _c(y_shared, np.float32)
+    T, k = weights.shape
+    d = y_perm.shape[1]
+    y = np.zeros((T, d), np.float32)
+    rc = lib().oracle_combine(T, d, k, _ptr(y_perm), _ptr(pair_pos), _ptr(weights), _ptr(y_shared),
+                              float(routed_scale), _ptr(y))
+    _check(rc, "oracle_combine")
+    return y
 
 
 def rmsnorm(v, gamma=None, eps=1e-6):

@@ -220,6 +220,27 @@ int oracle_layer(int T, int d, int E, int k, int h, int hs, const uint16_t* x, c
   return 0;
 }
 
+// Weighted combine on its own ([Blog] §4.1.2, explicit scaling of the
+// routed aggregation): y[t,i] = y_shared[t,i] + routed_scale *
+// sum_{j<k} weights[t,j] * y_perm[pair_pos[t*k+j], i], with y_perm bf16 rows,
+// y_shared f32 or NULL (zero), everything summed in double, y f32.
+int oracle_combine(int T, int d, int k, const uint16_t* y_perm, const int32_t* pair_pos, const float* weights,
+                   const float* y_shared, float routed_scale, float* y) {
+  if (T < 0 || d <= 0 || k < 1 || !y_perm || !pair_pos || !weights || !y) return -1;
+  for (int t = 0; t < T; ++t) {
+    for (int i = 0; i < d; ++i) {
+      double routed = 0.0;
+      for (int j = 0; j < k; ++j) {
+        const int64_t row = pair_pos[(size_t)t * k + j];
+        routed += (double)weights[(size_t)t * k + j] * (double)bf16_value(y_perm[(size_t)row * d + i]);
+      }
+      const double base = y_shared ? (double)y_shared[(size_t)t * d + i] : 0.0;
+      y[(size_t)t * d + i] = (float)(base + (double)routed_scale * routed);
+    }
+  }
+  return 0;
+}
+
 // Zero-centred RMSNorm (pre-norm placement, [Blog] §2.2, Figure 2 caption): each
 // row v -> v / sqrt(mean(v^2) + eps) * (1 + gamma), gamma NULL meaning 0 (unit
 // gain).  in [T,d] bf16 -> out [T,d] bf16 (round to nearest even).

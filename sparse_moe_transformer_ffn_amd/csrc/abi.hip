@@ -1,0 +1,185 @@
+// abi.hip -- the C ABI of libmoe (declared in include/moe.h): host-side
+// argument validation, workspace sizing, and dispatch to the kernel launchers.
+// Validation runs before any HIP call, so a rejected call enqueues nothing.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kMaxTokens = 1 << 20;
+constexpr int kMaxDim = 65536;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 16;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+moe_status check_shape(const moe_shape* s) {
+  if (!s) return MOE_ERR_INVALID_ARGUMENT;
+  if (s->num_tokens < 0 || s->num_tokens > kMaxTokens) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (s->d_model < 64 || s->d_model > kMaxDim || s->d_model % 64) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (s->num_experts < 1 || s->num_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (s->top_k < 1 || s->top_k > kMaxTopK || s->top_k > s->num_experts) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (s->d_expert < 64 || s->d_expert > kMaxDim || s->d_expert % 64) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (s->d_shared != 0 && (s->d_shared < 64 || s->d_shared > kMaxDim || s->d_shared % 64))
+    return MOE_ERR_UNSUPPORTED_SHAPE;
+  // Every index the kernels form fits the int32 pair/row arithmetic.
+  if ((int64_t)s->num_tokens * s->top_k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED_SHAPE;
+  return MOE_OK;
+}
+
+size_t workspace_bytes(const moe_shape* s) {
+  const int T = s->num_tokens, d = s->d_model, E = s->num_experts, k = s->top_k, h = s->d_expert;
+  size_t b = moe::route_workspace_bytes(T, d, E);
+  b = b > moe::permute_workspace_bytes(T, E) ? b : moe::permute_workspace_bytes(T, E);
+  b = b > moe::expert_workspace_bytes(T, k, h) ? b : moe::expert_workspace_bytes(T, k, h);
+  b = b > moe::shared_workspace_bytes(T, s->d_shared) ? b : moe::shared_workspace_bytes(T, s->d_shared);
+  return round256(b > 256 ? b : 256);
+}
+
+moe_status check_workspace(const moe_shape* s, const void* ws, size_t ws_bytes) {
+  if (!ws) return MOE_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return MOE_ERR_MISALIGNED;
+  if (ws_bytes < workspace_bytes(s)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED_SHAPE: return "MOE_ERR_UNSUPPORTED_SHAPE";
+    case MOE_ERR_MISALIGNED: return "MOE_ERR_MISALIGNED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+moe_status moe_check_shape(const moe_shape* shape) { return check_shape(shape); }
+
+moe_status moe_workspace_bytes(const moe_shape* shape, size_t* bytes) {
+  const moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
+  *bytes = workspace_bytes(shape);
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_shape* shape, const uint16_t* x, const uint16_t* w_router, const float* sel_bias,
+                     const float* logit_bias, int32_t* topk_ids, float* topk_weights, int32_t* expert_counts,
+                     float* topk_gap, void* workspace, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!x || !w_router || !sel_bias || !topk_ids || !topk_weights || !expert_counts) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned4(sel_bias) || !aligned4(topk_ids) ||
+      !aligned4(topk_weights) || !aligned4(expert_counts) || (logit_bias && !aligned4(logit_bias)) ||
+      (topk_gap && !aligned4(topk_gap)))
+    return MOE_ERR_MISALIGNED;
+  if ((st = check_workspace(shape, workspace, ws_bytes)) != MOE_OK) return st;
+  return hip_status(moe::launch_route(shape->num_tokens, shape->d_model, shape->num_experts, shape->top_k, x,
+                                      w_router, sel_bias, logit_bias, topk_ids, topk_weights, expert_counts,
+                                      topk_gap, workspace, (hipStream_t)stream));
+}
+
+moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t* expert_offsets,
+                       int32_t* perm_pairs, int32_t* pair_pos, void* workspace, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!topk_ids || !expert_offsets || !perm_pairs || !pair_pos) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned4(topk_ids) || !aligned4(expert_offsets) || !aligned4(perm_pairs) || !aligned4(pair_pos))
+    return MOE_ERR_MISALIGNED;
+  if ((st = check_workspace(shape, workspace, ws_bytes)) != MOE_OK) return st;
+  return hip_status(moe::launch_permute(shape->num_tokens, shape->num_experts, shape->top_k, topk_ids,
+                                        expert_offsets, perm_pairs, pair_pos, workspace, (hipStream_t)stream));
+}
+
+moe_status moe_expert_gate_up(const moe_shape* shape, const uint16_t* x, const int32_t* expert_offsets,
+                              const int32_t* perm_pairs, const uint16_t* w_gate_up, uint16_t* hid, void* stream) {
+  const moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!x || !expert_offsets || !perm_pairs || !w_gate_up || !hid) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(hid) || !aligned4(expert_offsets) ||
+      !aligned4(perm_pairs))
+    return MOE_ERR_MISALIGNED;
+  return hip_status(moe::launch_gate_up(shape->num_tokens, shape->d_model, shape->num_experts, shape->top_k,
+                                        shape->d_expert, x, expert_offsets, perm_pairs, w_gate_up, hid,
+                                        (hipStream_t)stream));
+}
+
+moe_status moe_expert_down(const moe_shape* shape, const int32_t* expert_offsets, const uint16_t* hid,
+                           const uint16_t* w_down, uint16_t* y_perm, void* stream) {
+  const moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!expert_offsets || !hid || !w_down || !y_perm) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(hid) || !aligned16(w_down) || !aligned16(y_perm) || !aligned4(expert_offsets))
+    return MOE_ERR_MISALIGNED;
+  return hip_status(moe::launch_down(shape->num_tokens, shape->d_model, shape->num_experts, shape->top_k,
+                                     shape->d_expert, expert_offsets, hid, w_down, y_perm, (hipStream_t)stream));
+}
+
+moe_status moe_expert_swiglu(const moe_shape* shape, const uint16_t* x, const int32_t* expert_offsets,
+                             const int32_t* perm_pairs, const uint16_t* w_gate_up, const uint16_t* w_down,
+                             uint16_t* y_perm, void* workspace, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!x || !expert_offsets || !perm_pairs || !w_gate_up || !w_down || !y_perm) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(y_perm) ||
+      !aligned4(expert_offsets) || !aligned4(perm_pairs))
+    return MOE_ERR_MISALIGNED;
+  if ((st = check_workspace(shape, workspace, ws_bytes)) != MOE_OK) return st;
+  uint16_t* hid = static_cast<uint16_t*>(workspace);
+  st = moe_expert_gate_up(shape, x, expert_offsets, perm_pairs, w_gate_up, hid, stream);
+  if (st != MOE_OK) return st;
+  return moe_expert_down(shape, expert_offsets, hid, w_down, y_perm, stream);
+}
+
+moe_status moe_shared_swiglu(const moe_shape* shape, const uint16_t* x, const uint16_t* ws_gate_up,
+                             const uint16_t* ws_down, float* y_shared, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (shape->d_shared == 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (!x || !ws_gate_up || !ws_down || !y_shared) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(ws_gate_up) || !aligned16(ws_down) || !aligned16(y_shared))
+    return MOE_ERR_MISALIGNED;
+  if ((st = check_workspace(shape, workspace, ws_bytes)) != MOE_OK) return st;
+  return hip_status(moe::launch_shared(shape->num_tokens, shape->d_model, shape->d_shared, x, ws_gate_up, ws_down,
+                                       y_shared, static_cast<uint16_t*>(workspace), (hipStream_t)stream));
+}
+
+moe_status moe_combine(const moe_shape* shape, const uint16_t* y_perm, const int32_t* pair_pos,
+                       const float* topk_weights, const float* y_shared, float routed_scale, uint16_t* y,
+                       void* stream) {
+  const moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!y_perm || !pair_pos || !topk_weights || !y) return MOE_ERR_INVALID_ARGUMENT;
+  if (!isfinite(routed_scale)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(y_perm) || !aligned16(y) || !aligned4(pair_pos) || !aligned4(topk_weights) ||
+      (y_shared && !aligned16(y_shared)))
+    return MOE_ERR_MISALIGNED;
+  return hip_status(moe::launch_combine(shape->num_tokens, shape->d_model, shape->top_k, y_perm, pair_pos,
+                                        topk_weights, y_shared, routed_scale, y, (hipStream_t)stream));
+}
+
+moe_status moe_rmsnorm(int32_t rows, int32_t cols, const uint16_t* in, const float* gamma, float eps, uint16_t* out,
+                       void* stream) {
+  if (rows < 0 || rows > kMaxTokens || cols < 8 || cols > kMaxDim || cols % 8) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (!in || !out || in == out) return MOE_ERR_INVALID_ARGUMENT;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(in) || !aligned16(out) || (gamma && !aligned4(gamma))) return MOE_ERR_MISALIGNED;
+  return hip_status(moe::launch_rmsnorm(rows, cols, in, gamma, eps, out, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// common.h -- device helpers shared by libmoe's gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, one L2 each
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t v16) { return __uint_as_float(v16 << 16); }
+
+// float -> bf16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return (b >> 16) | 0x40u;
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return b >> 16;
+}
+
+// 16x16x32 bf16 MFMA, f32 accumulate.  Operand lanes: lane l supplies row
+// (l % 16) of A (and column (l % 16) of B) for the 8 reduction elements
+// 8*(l/16) .. 8*(l/16)+7; any fixed assignment of reduction elements works as
+// long as A and B use the same one.  Result: lane l holds D[4*(l/16)+i][l%16]
+// for i = 0..3.
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 load16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Streamed-once data (expert weights): non-temporal load.
+__device__ __forceinline__ u32x4 load16_stream(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// Workgroups are dispatched round-robin over the XCDs (block b runs on XCD
+// b % 8).  Renumber them so that each XCD receives one contiguous range of
+// logical tile ids: tiles that share operands then share an L2.
+__device__ __forceinline__ int xcd_contiguous(int bid, int nblocks) {
+  const int per = nblocks / kNumXcd, rem = nblocks % kNumXcd;
+  const int xcd = bid % kNumXcd, idx = bid / kNumXcd;
+  return xcd * per + (xcd < rem ? xcd : rem) + idx;
+}
+
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
+
+}  // namespace moe

@@ -1,0 +1,39 @@
+// kernels.h -- libmoe-internal launchers (one per kernel family).  Shapes are
+// validated by the C ABI layer before any of these is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct RouteSplit {
+  int ksplit, kchunk;
+};
+RouteSplit route_split(int T, int d, int E);
+
+hipError_t launch_route(int T, int d, int E, int k, const uint16_t* x, const uint16_t* w_router,
+                        const float* sel_bias, const float* logit_bias, int32_t* topk_ids, float* topk_weights,
+                        int32_t* counts, float* topk_gap, void* workspace, hipStream_t stream);
+size_t route_workspace_bytes(int T, int d, int E);
+
+hipError_t launch_permute(int T, int E, int k, const int32_t* topk_ids, int32_t* expert_offsets,
+                          int32_t* perm_pairs, int32_t* pair_pos, void* workspace, hipStream_t stream);
+size_t permute_workspace_bytes(int T, int E);
+
+hipError_t launch_gate_up(int T, int d, int E, int k, int h, const uint16_t* x, const int32_t* offsets,
+                          const int32_t* perm, const uint16_t* w_gu, uint16_t* hid, hipStream_t stream);
+hipError_t launch_down(int T, int d, int E, int k, int h, const int32_t* offsets, const uint16_t* hid,
+                       const uint16_t* w_down, uint16_t* y_perm, hipStream_t stream);
+hipError_t launch_shared(int T, int d, int hs, const uint16_t* x, const uint16_t* ws_gu, const uint16_t* ws_d,
+                         float* y_shared, uint16_t* hid, hipStream_t stream);
+size_t expert_workspace_bytes(int T, int k, int h);
+size_t shared_workspace_bytes(int T, int hs);
+
+hipError_t launch_combine(int T, int d, int k, const uint16_t* y_perm, const int32_t* pair_pos,
+                          const float* topk_weights, const float* y_shared, float routed_scale, uint16_t* y,
+                          hipStream_t stream);
+hipError_t launch_rmsnorm(int rows, int cols, const uint16_t* in, const float* gamma, float eps, uint16_t* out,
+                          hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,157 @@
+"""libmoe's C ABI on the host: the library loads, exports every function
+include/moe.h declares, sizes workspaces, and rejects bad arguments with the
+documented status codes before anything is enqueued.
+
+Every call made here fails validation, so no kernel is launched and no GPU is
+needed.  Pointers are fake device addresses: they are never dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import moegen
+import sparse_moe_transformer_ffn_amd as moe
+from sparse_moe_transformer_ffn_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, INVALID, UNSUPPORTED, MISALIGNED, WS_SMALL = 0, 1, 2, 3, 4
+A = 0x7f0000000000          # fake, 256-byte aligned device address
+MIS = A + 2                 # misaligned for 16-byte vector loads
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def shape(cfg=1, **kw):
+    c = moegen.CONFIGS[cfg]
+    s = moe.make_shape(c.T, c.d, c.E, c.k, c.h, c.hs)
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    L = moe.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_status_strings():
+    for code, name in _lib.STATUS.items():
+        assert moe.moe_status_str(code) == name
+    assert moe.moe_status_str(99) == "MOE_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("cfg", sorted(moegen.CONFIGS))
+def test_workload_shapes_are_supported(cfg):
+    s = shape(cfg)
+    assert moe.moe_check_shape(s) == OK
+    nb = moe.moe_workspace_bytes(s)
+    c = moegen.CONFIGS[cfg]
+    assert nb % 256 == 0
+    assert nb >= c.T * c.k * c.h * 2       # hidden activations of the routed experts
+
+
+@pytest.mark.parametrize("field,value", [
+    ("num_tokens", -1), ("num_tokens", (1 << 20) + 1), ("d_model", 0), ("d_model", 96), ("d_model", 32),
+    ("num_experts", 0), ("num_experts", 1025), ("top_k", 0), ("top_k", 17), ("d_expert", 0), ("d_expert", 100),
+    ("d_shared", 32), ("d_shared", 96),
+])
+def test_unsupported_shapes(field, value):
+    s = shape(1, **{field: value})
+    assert moe.moe_check_shape(s) == UNSUPPORTED
+    n = ctypes.c_size_t(0)
+    assert moe.lib().moe_workspace_bytes(ctypes.byref(s), ctypes.byref(n)) == UNSUPPORTED
+
+
+def test_top_k_above_expert_count_and_edge_shapes():
+    assert moe.moe_check_shape(shape(0, num_experts=4, top_k=5)) == UNSUPPORTED
+    assert moe.moe_check_shape(shape(0, num_experts=4, top_k=4)) == OK
+    assert moe.moe_check_shape(shape(0, num_tokens=0)) == OK
+    assert moe.moe_check_shape(shape(0, d_shared=0)) == OK
+    assert moe.lib().moe_check_shape(None) == INVALID
+
+
+def _route(s, ws_bytes=1 << 40, **over):
+    args = dict(x=A, w=A, b=A, c=None, ids=A, wts=A, cnt=A, gap=A, ws=A)
+    args.update(over)
+    return moe.lib().moe_route(ctypes.byref(s), args["x"], args["w"], args["b"], args["c"], args["ids"],
+                               args["wts"], args["cnt"], args["gap"], args["ws"], ws_bytes, None)
+
+
+def test_route_validation():
+    s = shape(1)
+    for k in ("x", "w", "b", "ids", "wts", "cnt", "ws"):
+        assert _route(s, **{k: None}) == INVALID, k
+    assert _route(s, x=MIS) == MISALIGNED
+    assert _route(s, w=MIS) == MISALIGNED
+    assert _route(s, ids=A + 1) == MISALIGNED
+    assert _route(s, ws=A + 16) == MISALIGNED
+    assert _route(s, ws_bytes=moe.moe_workspace_bytes(s) - 256) == WS_SMALL
+    assert _route(shape(1, top_k=0)) == UNSUPPORTED
+
+
+def test_permute_validation():
+    s = shape(1)
+    L = moe.lib()
+    nb = moe.moe_workspace_bytes(s)
+    assert L.moe_permute(ctypes.byref(s), None, A, A, A, A, nb, None) == INVALID
+    assert L.moe_permute(ctypes.byref(s), A, A, A, None, A, nb, None) == INVALID
+    assert L.moe_permute(ctypes.byref(s), A + 2, A, A, A, A, nb, None) == MISALIGNED
+    assert L.moe_permute(ctypes.byref(s), A, A, A, A, A, 0, None) == WS_SMALL
+    assert L.moe_permute(ctypes.byref(s), A, A, A, A, None, nb, None) == INVALID
+
+
+def test_expert_and_shared_validation():
+    s = shape(1)
+    L = moe.lib()
+    nb = moe.moe_workspace_bytes(s)
+    assert L.moe_expert_swiglu(ctypes.byref(s), A, A, A, A, None, A, A, nb, None) == INVALID
+    assert L.moe_expert_swiglu(ctypes.byref(s), MIS, A, A, A, A, A, A, nb, None) == MISALIGNED
+    assert L.moe_expert_swiglu(ctypes.byref(s), A, A, A, A, A, A, A, nb - 1, None) == WS_SMALL
+    assert L.moe_expert_gate_up(ctypes.byref(s), A, A, A, A, None, None) == INVALID
+    assert L.moe_expert_gate_up(ctypes.byref(s), A, A, A, MIS, A, None) == MISALIGNED
+    assert L.moe_expert_down(ctypes.byref(s), A, A, A, None, None) == INVALID
+    assert L.moe_expert_down(ctypes.byref(s), A, A, A, MIS, None) == MISALIGNED
+    assert L.moe_shared_swiglu(ctypes.byref(s), A, A, None, A, A, nb, None) == INVALID
+    assert L.moe_shared_swiglu(ctypes.byref(s), A, A, A, A + 4, A, nb, None) == MISALIGNED
+    assert L.moe_shared_swiglu(ctypes.byref(s), A, A, A, A, A, 16, None) == WS_SMALL
+    no_shared = shape(1, d_shared=0)
+    assert L.moe_shared_swiglu(ctypes.byref(no_shared), A, A, A, A, A, nb, None) == INVALID
+
+
+def test_combine_and_rmsnorm_validation():
+    s = shape(1)
+    L = moe.lib()
+    assert L.moe_combine(ctypes.byref(s), None, A, A, A, ctypes.c_float(1.0), A, None) == INVALID
+    assert L.moe_combine(ctypes.byref(s), A, A, A, A, ctypes.c_float(float("nan")), A, None) == INVALID
+    assert L.moe_combine(ctypes.byref(s), A, A, A, A, ctypes.c_float(float("inf")), A, None) == INVALID
+    assert L.moe_combine(ctypes.byref(s), A, A, A, A + 4, ctypes.c_float(1.0), A, None) == MISALIGNED
+    assert L.moe_combine(ctypes.byref(s), A, A + 1, A, A, ctypes.c_float(1.0), A, None) == MISALIGNED
+    assert L.moe_rmsnorm(4, 100, A, None, ctypes.c_float(1e-6), A + 4096, None) == UNSUPPORTED
+    assert L.moe_rmsnorm(-1, 64, A, None, ctypes.c_float(1e-6), A + 4096, None) == UNSUPPORTED
+    assert L.moe_rmsnorm(4, 64, A, None, ctypes.c_float(1e-6), A, None) == INVALID      # aliasing
+    assert L.moe_rmsnorm(4, 64, None, None, ctypes.c_float(1e-6), A, None) == INVALID
+    assert L.moe_rmsnorm(4, 64, A, None, ctypes.c_float(-1.0), A + 4096, None) == INVALID
+    assert L.moe_rmsnorm(4, 64, A + 2, None, ctypes.c_float(1e-6), A + 4096, None) == MISALIGNED
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    s = shape(0)
+    x = torch.zeros((64, 256), dtype=torch.uint16)
+    with pytest.raises(ValueError):
+        moe.moe_rmsnorm(64, 256, x, None, 1e-6, x.clone())

@@ -1,0 +1,221 @@
+"""Per-call parity of libmoe on the GPU against the CPU oracle.
+
+Each call gets generator or oracle-made inputs (never another GPU output) and
+is compared with the oracle on the same inputs: routing, permutation and
+counts bit-exact (near-tie tokens excepted and reported), floating-point
+outputs within the stated tolerances.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moegen
+import oracle
+import sparse_moe_transformer_ffn_amd as moe
+from tests.gpu_harness import (DeviceLayer, bf16_dev, bf16_host, check_output, check_routing, f32_dev, i32_dev, log,
+                               oracle_route_all, stream_ptr)
+
+pytestmark = pytest.mark.gpu
+
+
+def test_device_fill_matches_host_fill(device):
+    # The generator's device fill must reproduce the host fill bit for bit, or
+    # the oracle would see different weights than the GPU.
+    for idx, experts in ((0, range(16)), (1, (0, 143, 287))):
+        cfg = moegen.CONFIGS[idx]
+        log(f"[fill] config {idx}")
+        dl = DeviceLayer(cfg)
+        torch.cuda.synchronize()
+        host = moegen.expert_weights_host(cfg, 0, experts)
+        for e in experts:
+            np.testing.assert_array_equal(bf16_host(dl.w_gu[e]), host[e][0])
+            np.testing.assert_array_equal(bf16_host(dl.w_d[e]), host[e][1])
+        sgu, swd = moegen.shared_weights_host(cfg)
+        np.testing.assert_array_equal(bf16_host(dl.ws_gu), sgu)
+        np.testing.assert_array_equal(bf16_host(dl.ws_d), swd)
+        del dl
+        torch.cuda.empty_cache()
+
+
+def run_route(cfg, x_h, wr_h, b_h, c_h):
+    T = x_h.shape[0]
+    s = moe.make_shape(T, cfg.d, cfg.E, cfg.k, cfg.h, cfg.hs)
+    n = max(T, 1)          # zero-token calls still take valid (unread) buffers
+    ids = torch.full((n, cfg.k), -7, dtype=torch.int32, device="cuda")
+    w = torch.full((n, cfg.k), -1.0, device="cuda")
+    gap = torch.full((n,), -1.0, device="cuda")
+    cnt = torch.full((cfg.E,), 12345, dtype=torch.int32, device="cuda")
+    ws = torch.empty(moe.moe_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    x = bf16_dev(x_h if T else np.zeros((1, cfg.d), np.uint16))
+    moe.moe_route(s, x, bf16_dev(wr_h), f32_dev(b_h), f32_dev(c_h), ids, w, cnt, gap, ws)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy()[:T], w.cpu().numpy()[:T], gap.cpu().numpy()[:T], cnt.cpu().numpy()
+
+
+@pytest.mark.parametrize("idx", [0, 1, 3])
+def test_route_parity(device, idx):
+    cfg = moegen.CONFIGS[idx]
+    log(f"[route] config {idx}: T={cfg.T} E={cfg.E} k={cfg.k}")
+    x_h, wr_h, b_h, c_h = moegen.x(cfg), moegen.router(cfg), moegen.sel_bias(cfg), moegen.logit_bias(cfg)
+    g_ids, g_w, g_gap, g_cnt = run_route(cfg, x_h, wr_h, b_h, c_h)
+    o_ids, o_w, o_gap, _ = oracle.route(x_h, wr_h, b_h, cfg.k, logit_bias=c_h)
+    same, near = check_routing(g_ids, g_w, g_gap, g_cnt, o_ids, o_w, o_gap, cfg.E)
+    log(f"  near-tie tokens: {near}, differing: {int((~same).sum())}")
+
+
+@pytest.mark.parametrize("T,E,k,bias_mode", [
+    (1, 288, 8, "normal"), (0, 288, 8, "normal"), (100, 16, 2, "normal"), (77, 16, 16, "normal"),
+    (50, 5, 3, "normal"), (64, 16, 1, "normal"), (130, 288, 8, "one_expert"), (64, 1024, 16, "normal"),
+    (64, 65, 4, "normal"),
+])
+def test_route_edge_cases(device, T, E, k, bias_mode):
+    cfg = moegen.custom(0, T=T, E=E, k=k, seed=1000 + T + E + k)
+    log(f"[route-edge] T={T} E={E} k={k} {bias_mode}")
+    x_h = moegen.x(cfg) if T else np.zeros((0, cfg.d), np.uint16)
+    wr_h, b_h = moegen.router(cfg), moegen.sel_bias(cfg)
+    if bias_mode == "one_expert":
+        b_h = b_h.copy()
+        b_h[E // 3] = 10.0
+    g_ids, g_w, g_gap, g_cnt = run_route(cfg, x_h, wr_h, b_h, None)
+    if T == 0:
+        assert np.all(g_cnt == 0)
+        return
+    o_ids, o_w, o_gap, _ = oracle.route(x_h, wr_h, b_h, k)
+    check_routing(g_ids, g_w, g_gap, g_cnt, o_ids, o_w, o_gap, E)
+    if k == 1:
+        assert np.all(g_w == 1.0)
+    if bias_mode == "one_expert":
+        assert np.all(np.any(g_ids == E // 3, axis=1)) and g_cnt[E // 3] == T
+
+
+def run_permute(T, E, k, ids_h):
+    s = moe.make_shape(T, 64, E, k, 64, 0)
+    off = torch.full((E + 1,), -3, dtype=torch.int32, device="cuda")
+    perm = torch.full((max(T * k, 1),), -3, dtype=torch.int32, device="cuda")
+    pos = torch.full((max(T * k, 1),), -3, dtype=torch.int32, device="cuda")
+    ws = torch.empty(moe.moe_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    ids = i32_dev(ids_h if T else np.zeros((1, k), np.int32))
+    moe.moe_permute(s, ids, off, perm, pos, ws)
+    torch.cuda.synchronize()
+    return off.cpu().numpy(), perm.cpu().numpy()[:T * k], pos.cpu().numpy()[:T * k]
+
+
+@pytest.mark.parametrize("T,E,k,pattern", [
+    (64, 16, 2, "random"), (1, 16, 2, "random"), (0, 16, 2, "random"), (65, 288, 8, "random"),
+    (1000, 288, 8, "random"), (8192, 288, 8, "random"), (333, 1024, 16, "random"), (257, 288, 8, "one_expert"),
+    (129, 16, 16, "random"), (200, 288, 8, "two_hot"),
+])
+def test_permute_parity(device, T, E, k, pattern):
+    log(f"[permute] T={T} E={E} k={k} {pattern}")
+    ids = moegen.random_ids(T * 31 + E, T, E, k)
+    if pattern == "one_expert":
+        # Expert 0 for every token plus k-1 others.
+        rest = moegen.random_ids(T * 37 + E, T, E - 1, k - 1) + 1
+        ids = np.concatenate([np.zeros((T, 1), np.int32), rest], axis=1)
+    assert np.all(np.diff(ids, axis=1) > 0) if T else True
+    g_off, g_perm, g_pos = run_permute(T, E, k, ids)
+    o_cnt, o_off, o_perm, o_pos = oracle.permute(ids, E)
+    np.testing.assert_array_equal(g_off, o_off)
+    np.testing.assert_array_equal(g_perm, o_perm)
+    np.testing.assert_array_equal(g_pos, o_pos)
+
+
+def oracle_perm_inputs(cfg, dl):
+    o_ids, o_w, o_gap = oracle_route_all(dl)
+    cnt, off, perm, pos = oracle.permute(o_ids, cfg.E)
+    return o_ids, o_w, off, perm, pos
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_expert_swiglu_parity(device, idx):
+    cfg = moegen.CONFIGS[idx]
+    log(f"[experts] config {idx}")
+    dl = DeviceLayer(cfg)
+    o_ids, o_w, off, perm, pos = oracle_perm_inputs(cfg, dl)
+    s = moe.make_shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, cfg.hs)
+    y_perm = torch.zeros((cfg.T * cfg.k, cfg.d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.moe_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    moe.moe_expert_swiglu(s, dl.x, i32_dev(off), i32_dev(perm), dl.w_gu, dl.w_d, y_perm, ws)
+    torch.cuda.synchronize()
+    yp = moegen.bf16_to_f32(bf16_host(y_perm))
+    # Rows to check: every row of config 0; at config 1 three rows of each of
+    # twenty touched experts (first, middle, last of the group).
+    rows = []
+    touched = np.where(np.diff(off) > 0)[0]
+    pick = touched if idx == 0 else touched[np.linspace(0, len(touched) - 1, 20).astype(int)]
+    for e in pick:
+        lo, hi = off[e], off[e + 1]
+        rows += list(range(lo, hi)) if idx == 0 else sorted({lo, (lo + hi - 1) // 2, hi - 1})
+    experts = sorted({int(np.searchsorted(off, r, side="right") - 1) for r in rows})
+    ew = moegen.expert_weights_host(cfg, 0, experts)
+    ref = np.stack([oracle.expert(dl.x_h[perm[r] // cfg.k], *ew[int(np.searchsorted(off, r, side="right") - 1)])
+                    for r in rows])
+    check_output(yp[rows], ref, f"y_perm rows ({len(rows)})")
+    # The phase entry points give the same rows as the combined call.
+    hid = torch.empty((cfg.T * cfg.k, cfg.h), dtype=torch.bfloat16, device="cuda")
+    y2 = torch.zeros_like(y_perm)
+    moe.moe_expert_gate_up(s, dl.x, i32_dev(off), i32_dev(perm), dl.w_gu, hid)
+    moe.moe_expert_down(s, i32_dev(off), hid, dl.w_d, y2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bf16_host(y2), bf16_host(y_perm))
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_shared_swiglu_parity(device, idx):
+    cfg = moegen.CONFIGS[idx]
+    log(f"[shared] config {idx}")
+    dl = DeviceLayer(cfg)
+    s = moe.make_shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, cfg.hs)
+    ys = torch.zeros((cfg.T, cfg.d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    moe.moe_shared_swiglu(s, dl.x, dl.ws_gu, dl.ws_d, ys, ws)
+    torch.cuda.synchronize()
+    sgu, swd = moegen.shared_weights_host(cfg)
+    toks = np.arange(cfg.T) if idx == 0 else np.arange(0, cfg.T, 4)
+    ref = np.stack([oracle.expert(dl.x_h[t], sgu, swd) for t in toks])
+    check_output(ys.cpu().numpy()[toks], ref, "y_shared")
+
+
+@pytest.mark.parametrize("T,d,k,with_shared,scale", [
+    (64, 256, 2, True, 1.0), (64, 4096, 8, True, 1.0), (33, 4096, 8, False, 0.75), (1, 512, 16, True, 2.0),
+    (0, 256, 2, True, 1.0),
+])
+def test_combine_parity(device, T, d, k, with_shared, scale):
+    log(f"[combine] T={T} d={d} k={k} shared={with_shared}")
+    E = 64
+    ids = moegen.random_ids(7 + T, T, E, k)
+    _, _, perm, pos = oracle.permute(ids, E)
+    y_perm_h = moegen.normal_bf16(11 + T, 300, (max(T * k, 1), d))
+    w_h = moegen.uniform(12 + T, 301, max(T * k, 1)).astype(np.float32).reshape(-1, k)[:T]
+    ysh_h = (moegen.bf16_to_f32(moegen.normal_bf16(13 + T, 302, (max(T, 1), d))) * 3.0)[:T]
+    s = moe.make_shape(T, d, E, k, 64, 64 if with_shared else 0)
+    y = torch.full((max(T, 1), d), 7.0, dtype=torch.bfloat16, device="cuda")
+    pos_d = i32_dev(pos if T else np.zeros(1, np.int32))
+    w_d = f32_dev(w_h if T else np.zeros((1, k), np.float32))
+    ysh_d = f32_dev(ysh_h if T else np.zeros((1, d), np.float32)) if with_shared else None
+    moe.moe_combine(s, bf16_dev(y_perm_h), pos_d, w_d, ysh_d, scale, y)
+    torch.cuda.synchronize()
+    if T == 0:
+        assert np.all(bf16_host(y) == bf16_host(torch.full((1, d), 7.0, dtype=torch.bfloat16)))
+        return
+    ref = oracle.combine(y_perm_h[:T * k], pos, w_h, ysh_h if with_shared else None, scale)
+    got = moegen.bf16_to_f32(bf16_host(y))
+    rms = np.sqrt(np.mean(ref.astype(np.float64) ** 2))
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6 * rms)
+
+
+@pytest.mark.parametrize("rows,cols,with_gamma", [(64, 4096, False), (256, 4096, True), (1, 256, False),
+                                                  (7, 8, True), (0, 64, False)])
+def test_rmsnorm_parity(device, rows, cols, with_gamma):
+    log(f"[rmsnorm] {rows}x{cols} gamma={with_gamma}")
+    v = moegen.normal_bf16(rows + cols, 310, (max(rows, 1), cols), 2.5)
+    gamma = (moegen.uniform(rows, 311, cols) - 0.5).astype(np.float32) if with_gamma else None
+    out = torch.zeros((max(rows, 1), cols), dtype=torch.bfloat16, device="cuda")
+    moe.moe_rmsnorm(rows, cols, bf16_dev(v), f32_dev(gamma), 1e-6, out)
+    torch.cuda.synchronize()
+    if rows == 0:
+        return
+    ref = oracle.rmsnorm(v, gamma, 1e-6)
+    got = bf16_host(out)
+    diff = np.abs(got.astype(np.int32) - ref.astype(np.int32))
+    assert diff.max() <= 1, diff.max()

@@ -1,0 +1,178 @@
+"""Whole-layer parity on the GPU: the five libmoe calls in the order and
+launch configuration the benchmark uses (shared expert on its own stream),
+against the CPU oracle's forward pass of the same generator inputs.
+
+Routing is compared for every token (bit-exact except near-ties); the output
+for every token at the small sizes and for sampled tokens at the full sizes,
+on tokens whose routing matches.  The 12-layer stack is checked layer by
+layer on generated inputs (each layer's weights at T=256), and its chained
+run by properties that hold at any size plus full parity of its first layer.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moegen
+import oracle
+import sparse_moe_transformer_ffn_amd as moe
+from tests.gpu_harness import (DeviceLayer, bf16_dev, bf16_host, check_output, check_routing, log,
+                               oracle_layer_tokens, oracle_route_all)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_layer(dl, buf=None, concurrent_shared=True):
+    buf = buf or dl.buffers()
+    side = torch.cuda.Stream() if concurrent_shared else None
+    dl.forward(buf, shared_stream=side)
+    torch.cuda.synchronize()
+    return buf
+
+
+def gpu_results(buf):
+    return (buf.topk_ids.cpu().numpy(), buf.topk_weights.cpu().numpy(), buf.topk_gap.cpu().numpy(),
+            buf.expert_counts.cpu().numpy(), moegen.bf16_to_f32(bf16_host(buf.y)))
+
+
+def check_layer(dl, buf, tokens):
+    cfg = dl.cfg
+    g_ids, g_w, g_gap, g_cnt, g_y = gpu_results(buf)
+    o_ids, o_w, o_gap = oracle_route_all(dl)
+    same, near = check_routing(g_ids, g_w, g_gap, g_cnt, o_ids, o_w, o_gap, cfg.E)
+    # Permutation invariants on the GPU's own routing.
+    off = buf.expert_offsets.cpu().numpy()
+    perm = buf.perm_pairs.cpu().numpy()
+    pos = buf.pair_pos.cpu().numpy()
+    np.testing.assert_array_equal(off, np.concatenate([[0], np.cumsum(g_cnt)]))
+    np.testing.assert_array_equal(pos[perm], np.arange(cfg.T * cfg.k))
+    tokens = np.array([t for t in tokens if same[t]], np.int32)
+    log(f"  near-tie tokens {near}; comparing output of {len(tokens)} tokens")
+    _, y_ref = oracle_layer_tokens(dl, tokens, o_ids[tokens])
+    check_output(g_y[tokens], y_ref, f"config {cfg.index} layer {dl.layer} y")
+    return g_ids, same
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_layer_all_tokens(device, idx):
+    cfg = moegen.CONFIGS[idx]
+    log(f"[layer] config {idx}: {cfg.workload}")
+    dl = DeviceLayer(cfg)
+    buf = run_layer(dl)
+    check_layer(dl, buf, np.arange(cfg.T))
+
+
+def test_layer_is_deterministic(device):
+    cfg = moegen.CONFIGS[1]
+    log("[determinism] config 1, twice, sequential and concurrent shared expert")
+    dl = DeviceLayer(cfg)
+    a = run_layer(dl, concurrent_shared=True)
+    ya = bf16_host(a.y).copy()
+    ia = a.topk_ids.cpu().numpy().copy()
+    b = run_layer(dl, concurrent_shared=False)
+    np.testing.assert_array_equal(bf16_host(b.y), ya)
+    np.testing.assert_array_equal(b.topk_ids.cpu().numpy(), ia)
+    c = run_layer(dl, buf=a, concurrent_shared=True)
+    np.testing.assert_array_equal(bf16_host(c.y), ya)
+
+
+@pytest.mark.parametrize("T,k,hs,scale", [(1, 8, 1280, 1.0), (3, 1, 1280, 1.0), (97, 8, 0, 0.5), (130, 8, 1280, 2.0)])
+def test_layer_edge_shapes(device, T, k, hs, scale):
+    cfg = moegen.custom(1, T=T, k=k, hs=hs, routed_scale=scale, seed=500 + T)
+    log(f"[layer-edge] T={T} k={k} hs={hs} routed_scale={scale}")
+    dl = DeviceLayer(cfg)
+    buf = run_layer(dl)
+    check_layer(dl, buf, np.arange(T))
+
+
+def test_layer_all_tokens_one_expert(device):
+    # A bias of +10 on one expert sends every token there (ties elsewhere
+    # broken normally): one group of T rows, most experts idle.
+    cfg = moegen.custom(0, T=200, seed=77)
+    log("[layer-hot] every token to expert 6")
+    dl = DeviceLayer(cfg)
+    dl.b_h = dl.b_h.copy()
+    dl.b_h[6] = 10.0
+    dl.b = torch.from_numpy(dl.b_h).cuda()
+    buf = run_layer(dl)
+    assert buf.expert_counts.cpu().numpy()[6] == cfg.T
+    check_layer(dl, buf, np.arange(cfg.T))
+
+
+@pytest.mark.parametrize("idx,n_sample", [(2, 16), (3, 16)])
+def test_layer_full_size_sampled(device, idx, n_sample):
+    cfg = moegen.CONFIGS[idx]
+    log(f"[layer] config {idx} ({cfg.workload}), {n_sample} sampled tokens")
+    dl = DeviceLayer(cfg)
+    buf = run_layer(dl)
+    rng = np.random.default_rng(idx)
+    tokens = set(rng.choice(cfg.T, n_sample - 4, replace=False).tolist()) | {0, cfg.T - 1}
+    # Include tokens routed to the busiest expert (the skewed workload's hot spot).
+    g_ids = buf.topk_ids.cpu().numpy()
+    hot = int(np.argmax(buf.expert_counts.cpu().numpy()))
+    tokens |= set(np.where(np.any(g_ids == hot, axis=1))[0][[0, -1]].tolist())
+    check_layer(dl, buf, np.array(sorted(tokens)))
+    del dl, buf
+    torch.cuda.empty_cache()
+
+
+def test_stack_layers_on_generated_inputs(device):
+    # Every layer of the 12-layer stack (distinct weights, T=256) on its own
+    # generated input, all weights resident, launched back to back.
+    cfg = moegen.CONFIGS[4]
+    layers = []
+    for l in range(cfg.layers):
+        log(f"[stack] building layer {l}")
+        layers.append(DeviceLayer(cfg, layer=l))
+    bufs = [dl.buffers() for dl in layers]
+    side = torch.cuda.Stream()
+    for dl, b in zip(layers, bufs):
+        dl.forward(b, shared_stream=side)
+    torch.cuda.synchronize()
+    for l, (dl, b) in enumerate(zip(layers, bufs)):
+        log(f"[stack] checking layer {l}")
+        check_layer(dl, b, np.arange(0, cfg.T, 64 if l else 16))
+    del layers, bufs
+    torch.cuda.empty_cache()
+
+
+def test_stack_chained(device):
+    # The benchmark's chained run: x_{l+1} = unit-gain zero-centred RMSNorm of
+    # y_l.  Layer 0 sees the generator's x, so it gets full parity; later
+    # layers get properties that hold at any size, and the whole chain must be
+    # bit-reproducible.
+    cfg = moegen.CONFIGS[4]
+    layers = [DeviceLayer(cfg, layer=l) for l in range(cfg.layers)]
+    log("[stack-chain] weights resident")
+    bufs = [dl.buffers() for dl in layers]
+    xs = [layers[0].x] + [torch.empty_like(layers[0].x) for _ in range(cfg.layers - 1)]
+
+    def chain():
+        side = torch.cuda.Stream()
+        for l, (dl, b) in enumerate(zip(layers, bufs)):
+            b.forward(xs[l], dl.wr, dl.b, dl.c, dl.w_gu, dl.w_d, dl.ws_gu, dl.ws_d, cfg.routed_scale,
+                      shared_stream=side)
+            if l + 1 < cfg.layers:
+                moe.moe_rmsnorm(cfg.T, cfg.d, b.y, None, 1e-6, xs[l + 1])
+        torch.cuda.synchronize()
+        return [bf16_host(b.y).copy() for b in bufs]
+
+    first = chain()
+    check_layer(layers[0], bufs[0], np.arange(cfg.T))
+    for l in range(cfg.layers):
+        ids = bufs[l].topk_ids.cpu().numpy()
+        cnt = bufs[l].expert_counts.cpu().numpy()
+        assert np.all(np.diff(ids, axis=1) > 0) and np.all((ids >= 0) & (ids < cfg.E))
+        assert cnt.sum() == cfg.T * cfg.k
+        np.testing.assert_array_equal(cnt, np.bincount(ids.ravel(), minlength=cfg.E))
+        w = bufs[l].topk_weights.cpu().numpy()
+        np.testing.assert_allclose(w.astype(np.float64).sum(1), 1.0, atol=2e-5)
+        y = moegen.bf16_to_f32(first[l])
+        assert np.all(np.isfinite(y))
+        if l + 1 < cfg.layers:
+            xn = moegen.bf16_to_f32(bf16_host(xs[l + 1])).astype(np.float64)
+            np.testing.assert_allclose(np.sqrt((xn ** 2).mean(1)), 1.0, atol=5e-3)
+    again = chain()
+    for a, b in zip(first, again):
+        np.testing.assert_array_equal(a, b)
+    del layers, bufs, xs
+    torch.cuda.empty_cache()

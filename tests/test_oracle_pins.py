@@ -398,6 +398,37 @@ def test_layer_token_subset_matches_full():
         oracle.layer(x, wr, b, k, gu_missing, wd_missing, sgu, swd, tokens=np.array([0]))
 
 
+# ---------------------------------------------------------------- combine --
+
+def test_combine_closed_forms():
+    rng = np.random.default_rng(51)
+    T, d, k = 20, 64, 4
+    P = T * k
+    # Row r of y_perm holds the value r in every column (exact in bf16 up to
+    # 256), so a gather through the wrong index shows up as a wrong value.
+    y_perm = to_bf16(np.repeat(np.arange(P, dtype=np.float32)[:, None], d, axis=1))
+    pos = rng.permutation(P).astype(np.int32)
+    # One-hot weights pick exactly one slot.
+    for j in range(k):
+        w = np.zeros((T, k), np.float32)
+        w[:, j] = 1.0
+        y = oracle.combine(y_perm, pos, w)
+        np.testing.assert_array_equal(y, np.repeat(pos.reshape(T, k)[:, j:j + 1].astype(np.float32), d, axis=1))
+    # Equal weights give the mean of the gathered row indices; shared adds;
+    # routed_scale scales only the routed part.
+    w = np.full((T, k), 1.0 / k, np.float32)
+    sh = rng.standard_normal((T, d)).astype(np.float32)
+    y = oracle.combine(y_perm, pos, w, sh, routed_scale=2.0)
+    expect = sh.astype(np.float64) + 2.0 * pos.reshape(T, k).mean(1)[:, None]
+    np.testing.assert_allclose(y, expect, rtol=1e-6)
+    # Random rows and weights: linear in the weights.
+    y_perm2 = rand_bf16(rng, (P, d))
+    w2 = rng.random((T, k)).astype(np.float32)
+    a = oracle.combine(y_perm2, pos, w2)
+    b = oracle.combine(y_perm2, pos, (2 * w2).astype(np.float32))
+    np.testing.assert_allclose(b, 2 * a, rtol=1e-6)
+
+
 # ---------------------------------------------------------------- rmsnorm --
 
 def test_rmsnorm_matches_library_and_is_scale_invariant():
