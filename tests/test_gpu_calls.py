@@ -186,7 +186,7 @@ def test_combine_parity(device, T, d, k, with_shared, scale):
     ids = moegen.random_ids(7 + T, T, E, k)
     _, _, perm, pos = oracle.permute(ids, E)
     y_perm_h = moegen.normal_bf16(11 + T, 300, (max(T * k, 1), d))
-    w_h = moegen.uniform(12 + T, 301, max(T * k, 1)).astype(np.float32).reshape(-1, k)[:T]
+    w_h = moegen.uniform(12 + T, 301, max(T, 1) * k).astype(np.float32).reshape(-1, k)[:T]
     ysh_h = (moegen.bf16_to_f32(moegen.normal_bf16(13 + T, 302, (max(T, 1), d))) * 3.0)[:T]
     s = moe.make_shape(T, d, E, k, 64, 64 if with_shared else 0)
     y = torch.full((max(T, 1), d), 7.0, dtype=torch.bfloat16, device="cuda")
