@@ -1,10 +1,10 @@
 #!/usr/bin/env python3
 """Throughput of the sparse MoE FFN layer forward (libmoe) on one MI355X.
 
-A step is one forward pass of the layer over one batch: moe_route ->
-moe_permute -> moe_expert_gate_up -> moe_expert_down -> moe_combine on the main
-stream, with moe_shared_swiglu concurrently on a second stream (joined before
-the combine).  Inputs and weights are resident in HBM before timing starts;
+A step is one forward pass of the layer over one batch, enqueued on one
+stream: moe_route -> moe_permute -> moe_expert_gate_up -> moe_expert_down ->
+moe_combine, with the shared expert running as one more group inside the two
+grouped expert launches.  Inputs and weights are resident in HBM before timing starts;
 they come from the seeded generator (synthetic values with the shapes and
 distributions of the model's layer; no trained weights exist here).
 
@@ -78,26 +78,26 @@ class Workload:
         moegen.fill_shared_device(cfg, 0, self.ws_gu.data_ptr(), self.ws_d.data_ptr(), s)
         self.buf = moe.LayerBuffers.allocate(cfg.T, d, E, cfg.k, h, hs, device=dev)
         self.hid = torch.empty((cfg.T * cfg.k, h), dtype=torch.bfloat16, device=dev)
+        self.hid_shared = torch.empty((cfg.T, hs), dtype=torch.bfloat16, device=dev)
         torch.cuda.synchronize()
 
-    def step(self, main, side, ev=None):
+    def step(self, main, ev=None):
         """One forward; ev = (before gate_up, after gate_up, after down) events."""
         import sparse_moe_transformer_ffn_amd as moe
         b, sh, c = self.buf, self.buf.shape, self.cfg
-        side.wait_stream(main)
-        moe.moe_shared_swiglu(sh, self.x, self.ws_gu, self.ws_d, b.y_shared, b.workspace_shared, side)
         moe.moe_route(sh, self.x, self.wr, self.b, self.c, b.topk_ids, b.topk_weights, b.expert_counts, b.topk_gap,
                       b.workspace, main)
         moe.moe_permute(sh, b.topk_ids, b.expert_offsets, b.perm_pairs, b.pair_pos, b.workspace, main)
         if ev:
             ev[0].record(main)
-        moe.moe_expert_gate_up(sh, self.x, b.expert_offsets, b.perm_pairs, self.w_gu, self.hid, main)
+        moe.moe_expert_gate_up(sh, self.x, b.expert_offsets, b.perm_pairs, self.w_gu, self.hid, main,
+                               ws_gate_up=self.ws_gu, hid_shared=self.hid_shared)
         if ev:
             ev[1].record(main)
-        moe.moe_expert_down(sh, b.expert_offsets, self.hid, self.w_d, b.y_perm, main)
+        moe.moe_expert_down(sh, b.expert_offsets, self.hid, self.w_d, b.y_perm, main, hid_shared=self.hid_shared,
+                            ws_down=self.ws_d, y_shared=b.y_shared)
         if ev:
             ev[2].record(main)
-        main.wait_stream(side)
         moe.moe_combine(sh, b.y_perm, b.pair_pos, b.topk_weights, b.y_shared, c.routed_scale, b.y, main)
 
 
@@ -108,10 +108,11 @@ def algorithmic(cfg, n_touched):
     w_expert = 3 * d * h * 2
     step_bytes = n_touched * w_expert + 3 * d * hs * 2 + E * d * 2 + T * d * 2 * 2 + T * k * 4 * 4
     step_flops = 2 * T * k * 3 * d * h + 2 * T * 3 * d * hs + 2 * T * d * E
-    gate_up_bytes = n_touched * 2 * h * d * 2 + T * d * 2 + T * k * h * 2
-    gate_up_flops = 2 * T * k * 2 * h * d
-    down_bytes = n_touched * d * h * 2 + T * k * h * 2 + T * k * d * 2
-    down_flops = 2 * T * k * h * d
+    # The grouped launches include the shared expert (one more group).
+    gate_up_bytes = (n_touched * 2 * h + 2 * hs) * d * 2 + T * d * 2 + T * (k * h + hs) * 2
+    gate_up_flops = 2 * T * (k * 2 * h + 2 * hs) * d
+    down_bytes = (n_touched * h + hs) * d * 2 + T * (k * h + hs) * 2 + T * k * d * 2 + T * d * 4
+    down_flops = 2 * T * (k * h + hs) * d
     return dict(step_bytes=step_bytes, step_flops=step_flops, gate_up_bytes=gate_up_bytes,
                 gate_up_flops=gate_up_flops, down_bytes=down_bytes, down_flops=down_flops)
 
@@ -121,9 +122,8 @@ def time_workload(cfg, steps, warmup, dev):
     import torch
     wl = Workload(cfg, dev)
     main = torch.cuda.current_stream()
-    side = torch.cuda.Stream(dev)
     for _ in range(warmup):
-        wl.step(main, side)
+        wl.step(main)
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
@@ -132,7 +132,7 @@ def time_workload(cfg, steps, warmup, dev):
     wall0 = time.perf_counter()
     t0.record(main)
     for i in range(steps):
-        wl.step(main, side, evs[i])
+        wl.step(main, evs[i])
     t1.record(main)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0

@@ -134,17 +134,27 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t*
  *      w_gate_up [E, 2h, d] bf16 (rows 0..h-1 gate, h..2h-1 up);
  *      w_down [E, d, h] bf16.
  * Out: y_perm [T*k, d] bf16, unweighted expert outputs in permuted order.
+ * Optionally the shared expert runs inside the same grouped launches (one
+ * more group holding every token): pass ws_gate_up [2h_s, d], ws_down
+ * [d, h_s] and y_shared [T,d] f32 together (all three or none; d_shared > 0),
+ * with the result of moe_shared_swiglu.
  * hid is rounded to bf16 between the two GEMMs; accumulation is f32.        */
 moe_status moe_expert_swiglu(const moe_shape* shape, const uint16_t* x, const int32_t* expert_offsets,
                              const int32_t* perm_pairs, const uint16_t* w_gate_up, const uint16_t* w_down,
-                             uint16_t* y_perm, void* workspace, size_t ws_bytes, void* stream);
+                             const uint16_t* ws_gate_up, const uint16_t* ws_down, uint16_t* y_perm, float* y_shared,
+                             void* workspace, size_t ws_bytes, void* stream);
 
 /* The two phases of moe_expert_swiglu, for callers that keep the hidden
- * activations themselves.  hid [T*k, h] bf16 (permuted order).             */
+ * activations themselves: hid [T*k, h] bf16 (permuted order) and, with the
+ * shared expert, hid_shared [T, h_s] bf16.  Shared-expert pointers come as a
+ * set (gate/up: ws_gate_up + hid_shared; down: hid_shared + ws_down +
+ * y_shared), all given or all NULL.                                        */
 moe_status moe_expert_gate_up(const moe_shape* shape, const uint16_t* x, const int32_t* expert_offsets,
-                              const int32_t* perm_pairs, const uint16_t* w_gate_up, uint16_t* hid, void* stream);
+                              const int32_t* perm_pairs, const uint16_t* w_gate_up, const uint16_t* ws_gate_up,
+                              uint16_t* hid, uint16_t* hid_shared, void* stream);
 moe_status moe_expert_down(const moe_shape* shape, const int32_t* expert_offsets, const uint16_t* hid,
-                           const uint16_t* w_down, uint16_t* y_perm, void* stream);
+                           const uint16_t* hid_shared, const uint16_t* w_down, const uint16_t* ws_down,
+                           uint16_t* y_perm, float* y_shared, void* stream);
 
 /* Shared expert ([Blog] §2.2: one shared expert, always active):
  *   y_shared[t,:] = W_d^s (SiLU(W_g^s x[t]) * (W_u^s x[t]))

@@ -66,25 +66,30 @@ class LayerBuffers:
         )
 
     def forward(self, x, w_router, sel_bias, logit_bias, w_gate_up, w_down, ws_gate_up=None, ws_down=None,
-                routed_scale=1.0, stream=None, shared_stream=None):
-        """route -> permute -> experts -> (shared) -> combine, enqueued on
-        `stream` (default: current).  With `shared_stream`, the shared expert
-        runs there concurrently and `stream` waits for it before combining."""
+                routed_scale=1.0, stream=None, shared="fused", shared_stream=None):
+        """route -> permute -> experts -> combine, enqueued on `stream`
+        (default: current).  The shared expert runs
+          "fused":  as one more group inside the grouped expert launches;
+          "stream": as moe_shared_swiglu on `shared_stream`, concurrently,
+                    joined before the combine;
+          "serial": as moe_shared_swiglu on `stream` after the experts."""
         import torch
         s = stream if stream is not None else torch.cuda.current_stream()
         sh = self.shape
         use_shared = sh.d_shared > 0 and ws_gate_up is not None
-        if use_shared and shared_stream is not None:
+        if use_shared and shared == "stream":
             shared_stream.wait_stream(s)
             moe_shared_swiglu(sh, x, ws_gate_up, ws_down, self.y_shared, self.workspace_shared, shared_stream)
         moe_route(sh, x, w_router, sel_bias, logit_bias, self.topk_ids, self.topk_weights, self.expert_counts,
                   self.topk_gap, self.workspace, s)
         moe_permute(sh, self.topk_ids, self.expert_offsets, self.perm_pairs, self.pair_pos, self.workspace, s)
+        fused = use_shared and shared == "fused"
         moe_expert_swiglu(sh, x, self.expert_offsets, self.perm_pairs, w_gate_up, w_down, self.y_perm,
-                          self.workspace, s)
-        if use_shared and shared_stream is None:
+                          self.workspace, s, ws_gate_up=ws_gate_up if fused else None,
+                          ws_down=ws_down if fused else None, y_shared=self.y_shared if fused else None)
+        if use_shared and shared == "serial":
             moe_shared_swiglu(sh, x, ws_gate_up, ws_down, self.y_shared, self.workspace, s)
-        if use_shared and shared_stream is not None:
+        if use_shared and shared == "stream":
             s.wait_stream(shared_stream)
         moe_combine(sh, self.y_perm, self.pair_pos, self.topk_weights, self.y_shared if use_shared else None,
                     routed_scale, self.y, s)

@@ -21,14 +21,17 @@ hipError_t launch_permute(int T, int E, int k, const int32_t* topk_ids, int32_t*
                           int32_t* perm_pairs, int32_t* pair_pos, void* workspace, hipStream_t stream);
 size_t permute_workspace_bytes(int T, int E);
 
-hipError_t launch_gate_up(int T, int d, int E, int k, int h, const uint16_t* x, const int32_t* offsets,
-                          const int32_t* perm, const uint16_t* w_gu, uint16_t* hid, hipStream_t stream);
-hipError_t launch_down(int T, int d, int E, int k, int h, const int32_t* offsets, const uint16_t* hid,
-                       const uint16_t* w_down, uint16_t* y_perm, hipStream_t stream);
-hipError_t launch_shared(int T, int d, int hs, const uint16_t* x, const uint16_t* ws_gu, const uint16_t* ws_d,
-                         float* y_shared, uint16_t* hid, hipStream_t stream);
-size_t expert_workspace_bytes(int T, int k, int h);
-size_t shared_workspace_bytes(int T, int hs);
+// Grouped expert GEMMs.  Routed groups come from expert_offsets/perm (NULL
+// offsets: none); the shared expert is one more group when its weights are
+// given (ws_gu / ws_down non-NULL).
+hipError_t launch_gate_up(int T, int d, int E, int k, int h, int hs, const uint16_t* x, const int32_t* offsets,
+                          const int32_t* perm, const uint16_t* w_gu, const uint16_t* ws_gu, uint16_t* hid,
+                          uint16_t* hid_shared, hipStream_t stream);
+hipError_t launch_down(int T, int d, int E, int k, int h, int hs, const int32_t* offsets, const uint16_t* hid,
+                       const uint16_t* hid_shared, const uint16_t* w_down, const uint16_t* ws_down, uint16_t* y_perm,
+                       float* y_shared, hipStream_t stream);
+size_t expert_hid_bytes(int T, int k, int h);
+size_t shared_hid_bytes(int T, int hs);
 
 hipError_t launch_combine(int T, int d, int k, const uint16_t* y_perm, const int32_t* pair_pos,
                           const float* topk_weights, const float* y_shared, float routed_scale, uint16_t* y,

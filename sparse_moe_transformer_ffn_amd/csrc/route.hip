@@ -52,18 +52,47 @@ __global__ __launch_bounds__(256) void k_route_logits(const uint16_t* __restrict
 
 namespace {
 
-// (score, expert) ordering of the selection: higher biased score first, equal
-// scores go to the lower expert index.
-__device__ __forceinline__ bool better(float b1, int e1, float b2, int e2) {
-  return b1 > b2 || (b1 == b2 && e1 < e2);
+// Order-preserving map of a float to uint32 (larger float -> larger key).
+// -0 is first folded onto +0 so that equal floats get equal keys.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t b = __float_as_uint(f + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// Number of keys >= tau over the wave (EPL keys per lane; invalid slots hold 0).
+template <int EPL>
+__device__ __forceinline__ int count_at_least(const uint32_t (&key)[EPL], uint32_t tau) {
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) c += __popcll(__ballot(key[j] >= tau));
+  return c;
+}
+
+// Largest tau with at least `need` keys >= tau: the need-th largest key.
+template <int EPL>
+__device__ __forceinline__ uint32_t kth_largest(const uint32_t (&key)[EPL], int need) {
+  uint32_t tau = 0u;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = tau | (1u << b);
+    if (count_at_least<EPL>(key, cand) >= need) tau = cand;
+  }
+  return tau;
 }
 
 }  // namespace
 
 // Per-token selection.  One wave per token; lane l owns experts l, l+64, ...
-// (EPL = experts per lane, E <= 64*EPL).  A block of four waves handles 16
-// tokens and aggregates the expert histogram in LDS before one global atomic
-// add per touched expert (integer atomics: order-independent).
+// (EPL = experts per lane, E <= 64*EPL).  The k-th largest biased score is
+// found exactly by a 32-step radix search on order-preserving keys, counting
+// with wave ballots (no cross-lane data movement); the chosen set is every
+// expert above it plus, among those equal to it, the lowest indices.  A block
+// of four waves handles four tokens and aggregates the expert histogram in LDS
+// before one global atomic add per touched expert (integer atomics:
+// order-independent).
 template <int EPL>
 __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ partial, int ksplit, int T, int E,
                                                       int k, const float* __restrict__ sel_bias,
@@ -72,85 +101,104 @@ __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ 
                                                       float* __restrict__ topk_weights, float* __restrict__ topk_gap,
                                                       int32_t* __restrict__ counts) {
   __shared__ int hist[1024];
+  __shared__ float chosen_s[4][16];
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += 256) hist[e] = 0;
   __syncthreads();
   const int wave = tid / kWave, lane = tid % kWave;
-  const float neg_inf = -__builtin_huge_valf();
-  for (int it = 0; it < 4; ++it) {
-    const int t = blockIdx.x * 16 + it * 4 + wave;
-    if (t >= T) continue;  // wave-uniform; no barrier inside the loop
-    float beta[EPL], score[EPL];
+  const int t = blockIdx.x * 4 + wave;
+  if (t < T) {  // wave-uniform; no block barrier inside
+    // Logit = sum of the split-K partials in chunk order; loads are issued
+    // four chunks at a time so their latencies overlap.
+    float z[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) z[j] = 0.f;
+    const size_t stride = (size_t)T * E;
+    const float* base = partial + (size_t)t * E + lane;
+    int ks = 0;
+    for (; ks + 4 <= ksplit; ks += 4) {
+      float v[4][EPL];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < EPL; ++j)
+          v[q][j] = (lane + kWave * j < E) ? base[(ks + q) * stride + kWave * j] : 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) z[j] += v[q][j];
+    }
+    for (; ks < ksplit; ++ks)
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if (lane + kWave * j < E) z[j] += base[ks * stride + kWave * j];
+    float score[EPL];
+    uint32_t key[EPL];
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
       const int e = lane + kWave * j;
+      score[j] = 0.f;
+      key[j] = 0u;  // below every real key: never chosen
       if (e < E) {
-        float z = 0.f;
-        for (int ks = 0; ks < ksplit; ++ks) z += partial[((size_t)ks * T + t) * E + e];
-        if (logit_bias) z += logit_bias[e];
-        score[j] = 1.0f / (1.0f + __expf(-z));
-        beta[j] = score[j] + sel_bias[e];
-        if (beta[j] != beta[j]) beta[j] = neg_inf;  // NaN input: never preferred
-      } else {
-        score[j] = 0.f;
-        beta[j] = neg_inf;
+        const float zz = logit_bias ? z[j] + logit_bias[e] : z[j];
+        score[j] = 1.0f / (1.0f + __expf(-zz));
+        const float beta = score[j] + sel_bias[e];
+        // A NaN score sorts below every number; +1 keeps it above the padding.
+        key[j] = (beta == beta) ? order_key(beta) : 1u;
       }
     }
-    // Selection rounds: the wave-wide best untaken expert each round.  Only
-    // real experts (e < E) that are not yet taken are candidates, so the k ids
-    // are always distinct and in range.
-    unsigned taken = 0u;
-    int my_id = 0;
-    float my_s = 0.f, kth = 0.f, next = neg_inf;
-    const int rounds = k < E ? k + 1 : k;
-    for (int r = 0; r < rounds; ++r) {
-      float bb = neg_inf, bs = 0.f;
-      int be = 0x7fffffff;
+    const uint32_t tau = kth_largest<EPL>(key, k);
+    // Chosen: keys > tau, then the lowest-index experts with key == tau.
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int above = 0;
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) {
-        const int e = lane + kWave * j;
-        if (e < E && !((taken >> j) & 1u) && better(beta[j], e, bb, be)) {
-          bb = beta[j];
-          be = e;
-          bs = score[j];
-        }
-      }
+    for (int j = 0; j < EPL; ++j) above += __popcll(__ballot(key[j] > tau));
+    int ties_left = k - above;
+    unsigned long long chosen[EPL];
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ob = __shfl_xor(bb, off);
-        const int oe = __shfl_xor(be, off);
-        const float os = __shfl_xor(bs, off);
-        if (better(ob, oe, bb, be)) {
-          bb = ob;
-          be = oe;
-          bs = os;
-        }
+    for (int j = 0; j < EPL; ++j) {
+      unsigned long long m = __ballot(key[j] > tau);
+      unsigned long long tie = __ballot(key[j] == tau);
+      while (ties_left > 0 && tie) {  // wave-uniform: masks are scalars
+        const unsigned long long low = tie & (~tie + 1ull);
+        m |= low;
+        tie ^= low;
+        --ties_left;
       }
-      if (r < k) {
-        if (lane == r) {
-          my_id = be;
-          my_s = bs;
-        }
-        if (be < E && (be & (kWave - 1)) == lane) taken |= 1u << (be >> 6);
-        kth = bb;
-      } else {
-        next = bb;
-      }
+      chosen[j] = m;
     }
-    // Ascending expert order: rank of my id among the k chosen.
-    int rank = 0;
-    for (int q = 0; q < k; ++q) rank += (__shfl(my_id, q) < my_id) ? 1 : 0;
+    // Gap to the (k+1)-th largest: zero if a tied expert was left out.
+    float gap = __builtin_huge_valf();
+    if (k < E) {
+      const uint32_t tau2 = kth_largest<EPL>(key, k + 1);
+      gap = key_value(tau) - key_value(tau2);
+    }
+    // Rank of each chosen expert in ascending expert order (j major, then
+    // lane), its weight from the unbiased scores summed in that order.
+    int before = 0;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      if ((chosen[j] >> lane) & 1ull) chosen_s[wave][before + __popcll(chosen[j] & below)] = score[j];
+      before += __popcll(chosen[j]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     float total = 0.f;
-    for (int q = 0; q < k; ++q) {
-      const unsigned long long m = __ballot(lane < k && rank == q);
-      total += __shfl(my_s, __ffsll((long long)m) - 1);
+    for (int q = 0; q < k; ++q) total += chosen_s[wave][q];
+    before = 0;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      if ((chosen[j] >> lane) & 1ull) {
+        const int rank = before + __popcll(chosen[j] & below);
+        const int e = lane + kWave * j;
+        topk_ids[(size_t)t * k + rank] = e;
+        topk_weights[(size_t)t * k + rank] = score[j] / total;
+        atomicAdd(&hist[e], 1);
+      }
+      before += __popcll(chosen[j]);
     }
-    if (lane < k) {
-      topk_ids[(size_t)t * k + rank] = my_id;
-      topk_weights[(size_t)t * k + rank] = my_s / total;
-      atomicAdd(&hist[my_id], 1);
-    }
-    if (lane == 0 && topk_gap) topk_gap[t] = k < E ? kth - next : __builtin_huge_valf();
+    if (lane == 0 && topk_gap) topk_gap[t] = gap;
   }
   __syncthreads();
   for (int e = tid; e < E; e += 256)
@@ -167,6 +215,7 @@ RouteSplit route_split(int T, int d, int E) {
   int ks = 512 / (base > 0 ? base : 1);
   ks = ks < 1 ? 1 : ks;
   ks = ks > d / 256 ? d / 256 : ks;
+  ks = ks > 8 ? 8 : ks;
   ks = ks < 1 ? 1 : ks;
   int kchunk = (d + ks - 1) / ks;
   kchunk = (kchunk + 31) / 32 * 32;
@@ -187,7 +236,7 @@ hipError_t launch_route(int T, int d, int E, int k, const uint16_t* x, const uin
                      w_router, T, d, E, rs.kchunk, partial, counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const dim3 grid((T + 15) / 16), block(256);
+  const dim3 grid((T + 3) / 4), block(256);
   const int epl = (E + 63) / 64;
 #define MOE_SELECT(N)                                                                                             \
   hipLaunchKernelGGL(k_route_select<N>, grid, block, 0, stream, partial, rs.ksplit, T, E, k, sel_bias, logit_bias, \

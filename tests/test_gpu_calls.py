@@ -135,6 +135,7 @@ def test_expert_swiglu_parity(device, idx):
     s = moe.make_shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, cfg.hs)
     y_perm = torch.zeros((cfg.T * cfg.k, cfg.d), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(moe.moe_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    ys_fused = torch.zeros((cfg.T, cfg.d), dtype=torch.float32, device="cuda")
     moe.moe_expert_swiglu(s, dl.x, i32_dev(off), i32_dev(perm), dl.w_gu, dl.w_d, y_perm, ws)
     torch.cuda.synchronize()
     yp = moegen.bf16_to_f32(bf16_host(y_perm))
@@ -158,6 +159,16 @@ def test_expert_swiglu_parity(device, idx):
     moe.moe_expert_down(s, i32_dev(off), hid, dl.w_d, y2)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(bf16_host(y2), bf16_host(y_perm))
+    # With the shared expert fused into the same launches: routed rows
+    # unchanged, shared output equal to the standalone call's.
+    y3 = torch.zeros_like(y_perm)
+    moe.moe_expert_swiglu(s, dl.x, i32_dev(off), i32_dev(perm), dl.w_gu, dl.w_d, y3, ws, ws_gate_up=dl.ws_gu,
+                          ws_down=dl.ws_d, y_shared=ys_fused)
+    ys_alone = torch.zeros_like(ys_fused)
+    moe.moe_shared_swiglu(s, dl.x, dl.ws_gu, dl.ws_d, ys_alone, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bf16_host(y3), bf16_host(y_perm))
+    np.testing.assert_array_equal(ys_fused.cpu().numpy(), ys_alone.cpu().numpy())
 
 
 @pytest.mark.parametrize("idx", [0, 1])

@@ -1,5 +1,6 @@
-"""Whole-layer parity on the GPU: the five libmoe calls in the order and
-launch configuration the benchmark uses (shared expert on its own stream),
+"""Whole-layer parity on the GPU: the libmoe calls in the order and launch
+configuration the benchmark uses (shared expert fused into the grouped expert
+launches),
 against the CPU oracle's forward pass of the same generator inputs.
 
 Routing is compared for every token (bit-exact except near-ties); the output
@@ -21,10 +22,10 @@ from tests.gpu_harness import (DeviceLayer, bf16_dev, bf16_host, check_output, c
 pytestmark = pytest.mark.gpu
 
 
-def run_layer(dl, buf=None, concurrent_shared=True):
+def run_layer(dl, buf=None, shared="fused"):
     buf = buf or dl.buffers()
-    side = torch.cuda.Stream() if concurrent_shared else None
-    dl.forward(buf, shared_stream=side)
+    side = torch.cuda.Stream() if shared == "stream" else None
+    dl.forward(buf, shared=shared, shared_stream=side)
     torch.cuda.synchronize()
     return buf
 
@@ -61,17 +62,22 @@ def test_layer_all_tokens(device, idx):
     check_layer(dl, buf, np.arange(cfg.T))
 
 
-def test_layer_is_deterministic(device):
-    cfg = moegen.CONFIGS[1]
-    log("[determinism] config 1, twice, sequential and concurrent shared expert")
+@pytest.mark.parametrize("idx", [0, 1])
+def test_layer_is_deterministic(device, idx):
+    # Same inputs, same bits: fused shared expert, shared expert on a side
+    # stream, shared expert after the routed ones, and a rerun into the same
+    # buffers.
+    cfg = moegen.CONFIGS[idx]
+    log(f"[determinism] config {idx}")
     dl = DeviceLayer(cfg)
-    a = run_layer(dl, concurrent_shared=True)
+    a = run_layer(dl, shared="fused")
     ya = bf16_host(a.y).copy()
     ia = a.topk_ids.cpu().numpy().copy()
-    b = run_layer(dl, concurrent_shared=False)
-    np.testing.assert_array_equal(bf16_host(b.y), ya)
-    np.testing.assert_array_equal(b.topk_ids.cpu().numpy(), ia)
-    c = run_layer(dl, buf=a, concurrent_shared=True)
+    for mode in ("stream", "serial"):
+        b = run_layer(dl, shared=mode)
+        np.testing.assert_array_equal(bf16_host(b.y), ya)
+        np.testing.assert_array_equal(b.topk_ids.cpu().numpy(), ia)
+    c = run_layer(dl, buf=a, shared="fused")
     np.testing.assert_array_equal(bf16_host(c.y), ya)
 
 
@@ -124,9 +130,8 @@ def test_stack_layers_on_generated_inputs(device):
         log(f"[stack] building layer {l}")
         layers.append(DeviceLayer(cfg, layer=l))
     bufs = [dl.buffers() for dl in layers]
-    side = torch.cuda.Stream()
     for dl, b in zip(layers, bufs):
-        dl.forward(b, shared_stream=side)
+        dl.forward(b)
     torch.cuda.synchronize()
     for l, (dl, b) in enumerate(zip(layers, bufs)):
         log(f"[stack] checking layer {l}")
@@ -147,10 +152,8 @@ def test_stack_chained(device):
     xs = [layers[0].x] + [torch.empty_like(layers[0].x) for _ in range(cfg.layers - 1)]
 
     def chain():
-        side = torch.cuda.Stream()
         for l, (dl, b) in enumerate(zip(layers, bufs)):
-            b.forward(xs[l], dl.wr, dl.b, dl.c, dl.w_gu, dl.w_d, dl.ws_gu, dl.ws_d, cfg.routed_scale,
-                      shared_stream=side)
+            b.forward(xs[l], dl.wr, dl.b, dl.c, dl.w_gu, dl.w_d, dl.ws_gu, dl.ws_d, cfg.routed_scale)
             if l + 1 < cfg.layers:
                 moe.moe_rmsnorm(cfg.T, cfg.d, b.y, None, 1e-6, xs[l + 1])
         torch.cuda.synchronize()
