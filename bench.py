@@ -90,12 +90,12 @@ class Workload:
         moe.moe_permute(sh, b.topk_ids, b.expert_offsets, b.perm_pairs, b.pair_pos, b.workspace, main)
         if ev:
             ev[0].record(main)
-        moe.moe_expert_gate_up(sh, self.x, b.expert_offsets, b.perm_pairs, self.w_gu, self.hid, main,
+        moe.moe_expert_gate_up(sh, self.x, b.expert_offsets, b.perm_pairs, self.w_gu, self.hid, b.workspace, main,
                                ws_gate_up=self.ws_gu, hid_shared=self.hid_shared)
         if ev:
             ev[1].record(main)
-        moe.moe_expert_down(sh, b.expert_offsets, self.hid, self.w_d, b.y_perm, main, hid_shared=self.hid_shared,
-                            ws_down=self.ws_d, y_shared=b.y_shared)
+        moe.moe_expert_down(sh, b.expert_offsets, self.hid, self.w_d, b.y_perm, b.workspace, main,
+                            hid_shared=self.hid_shared, ws_down=self.ws_d, y_shared=b.y_shared)
         if ev:
             ev[2].record(main)
         moe.moe_combine(sh, b.y_perm, b.pair_pos, b.topk_weights, b.y_shared, c.routed_scale, b.y, main)
@@ -186,6 +186,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--only-prefill", action="store_true", help="time only the prefill workload (profiling)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a plain 1 GiB device copy (the known-size reference for HBM byte counters)")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=64)
@@ -200,6 +203,20 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.copy_probe:
+        src = torch.ones(1 << 29, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel() * 2, "copies": 3}), flush=True)
+        return
+    if args.only_prefill:
+        pcfg = moegen.CONFIGS[2]
+        _, p = time_workload(pcfg, args.steps, args.warmup, dev)
+        print(json.dumps({"workload": pcfg.workload, "ms_per_step": p["ms_per_step"],
+                          "gate_up_ms": p["gate_up_ms"], "down_ms": p["down_ms"]}), flush=True)
+        return
     cfg = moegen.CONFIGS[1]
     wl, r = time_workload(cfg, args.steps, args.warmup, dev)
     alg = r["alg"]

@@ -148,13 +148,14 @@ moe_status moe_expert_swiglu(const moe_shape* shape, const uint16_t* x, const in
  * activations themselves: hid [T*k, h] bf16 (permuted order) and, with the
  * shared expert, hid_shared [T, h_s] bf16.  Shared-expert pointers come as a
  * set (gate/up: ws_gate_up + hid_shared; down: hid_shared + ws_down +
- * y_shared), all given or all NULL.                                        */
+ * y_shared), all given or all NULL.  The workspace holds the kernels' work
+ * queue (the size rule is the one of every call).                          */
 moe_status moe_expert_gate_up(const moe_shape* shape, const uint16_t* x, const int32_t* expert_offsets,
                               const int32_t* perm_pairs, const uint16_t* w_gate_up, const uint16_t* ws_gate_up,
-                              uint16_t* hid, uint16_t* hid_shared, void* stream);
+                              uint16_t* hid, uint16_t* hid_shared, void* workspace, size_t ws_bytes, void* stream);
 moe_status moe_expert_down(const moe_shape* shape, const int32_t* expert_offsets, const uint16_t* hid,
                            const uint16_t* hid_shared, const uint16_t* w_down, const uint16_t* ws_down,
-                           uint16_t* y_perm, float* y_shared, void* stream);
+                           uint16_t* y_perm, float* y_shared, void* workspace, size_t ws_bytes, void* stream);
 
 /* Shared expert ([Blog] §2.2: one shared expert, always active):
  *   y_shared[t,:] = W_d^s (SiLU(W_g^s x[t]) * (W_u^s x[t]))

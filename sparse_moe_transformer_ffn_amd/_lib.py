@@ -57,8 +57,8 @@ def lib():
         L.moe_route.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_permute.argtypes = [_SP, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_expert_swiglu.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
-        L.moe_expert_gate_up.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P]
-        L.moe_expert_down.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P]
+        L.moe_expert_gate_up.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.moe_expert_down.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_shared_swiglu.argtypes = [_SP, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_combine.argtypes = [_SP, _P, _P, _P, _P, ctypes.c_float, _P, _P]
         L.moe_rmsnorm.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_float, _P, _P]
@@ -135,18 +135,20 @@ def moe_expert_swiglu(shape, x, expert_offsets, perm_pairs, w_gate_up, w_down, y
                                                         _ptr(y_shared), ws, nb, _stream(stream)))
 
 
-def moe_expert_gate_up(shape, x, expert_offsets, perm_pairs, w_gate_up, hid, stream=None, ws_gate_up=None,
-                       hid_shared=None):
+def moe_expert_gate_up(shape, x, expert_offsets, perm_pairs, w_gate_up, hid, workspace, stream=None,
+                       ws_gate_up=None, hid_shared=None):
+    ws, nb = _ws(workspace)
     _check("moe_expert_gate_up", lib().moe_expert_gate_up(ctypes.byref(shape), _ptr(x), _ptr(expert_offsets),
                                                           _ptr(perm_pairs), _ptr(w_gate_up), _ptr(ws_gate_up),
-                                                          _ptr(hid), _ptr(hid_shared), _stream(stream)))
+                                                          _ptr(hid), _ptr(hid_shared), ws, nb, _stream(stream)))
 
 
-def moe_expert_down(shape, expert_offsets, hid, w_down, y_perm, stream=None, hid_shared=None, ws_down=None,
-                    y_shared=None):
+def moe_expert_down(shape, expert_offsets, hid, w_down, y_perm, workspace, stream=None, hid_shared=None,
+                    ws_down=None, y_shared=None):
+    ws, nb = _ws(workspace)
     _check("moe_expert_down", lib().moe_expert_down(ctypes.byref(shape), _ptr(expert_offsets), _ptr(hid),
                                                     _ptr(hid_shared), _ptr(w_down), _ptr(ws_down), _ptr(y_perm),
-                                                    _ptr(y_shared), _stream(stream)))
+                                                    _ptr(y_shared), ws, nb, _stream(stream)))
 
 
 def moe_shared_swiglu(shape, x, ws_gate_up, ws_down, y_shared, workspace, stream=None):

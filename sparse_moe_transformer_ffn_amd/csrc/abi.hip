@@ -39,7 +39,7 @@ size_t workspace_bytes(const moe_shape* s) {
   const int T = s->num_tokens, d = s->d_model, E = s->num_experts, k = s->top_k, h = s->d_expert;
   size_t b = moe::route_workspace_bytes(T, d, E);
   b = b > moe::permute_workspace_bytes(T, E) ? b : moe::permute_workspace_bytes(T, E);
-  const size_t experts = moe::expert_hid_bytes(T, k, h) + moe::shared_hid_bytes(T, s->d_shared);
+  const size_t experts = moe::expert_hid_bytes(T, k, h) + moe::shared_hid_bytes(T, s->d_shared) + moe::kQueueBytes;
   b = b > experts ? b : experts;
   return round256(b > 256 ? b : 256);
 }
@@ -120,7 +120,7 @@ static moe_status shared_set(const moe_shape* s, std::initializer_list<const voi
 
 moe_status moe_expert_gate_up(const moe_shape* shape, const uint16_t* x, const int32_t* expert_offsets,
                               const int32_t* perm_pairs, const uint16_t* w_gate_up, const uint16_t* ws_gate_up,
-                              uint16_t* hid, uint16_t* hid_shared, void* stream) {
+                              uint16_t* hid, uint16_t* hid_shared, void* workspace, size_t ws_bytes, void* stream) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
   if (!x || !expert_offsets || !perm_pairs || !w_gate_up || !hid) return MOE_ERR_INVALID_ARGUMENT;
@@ -129,14 +129,16 @@ moe_status moe_expert_gate_up(const moe_shape* shape, const uint16_t* x, const i
   if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(hid) || !aligned4(expert_offsets) ||
       !aligned4(perm_pairs) || (shared && (!aligned16(ws_gate_up) || !aligned16(hid_shared))))
     return MOE_ERR_MISALIGNED;
+  if ((st = check_workspace(shape, workspace, ws_bytes)) != MOE_OK) return st;
   return hip_status(moe::launch_gate_up(shape->num_tokens, shape->d_model, shape->num_experts, shape->top_k,
                                         shape->d_expert, shape->d_shared, x, expert_offsets, perm_pairs, w_gate_up,
-                                        shared ? ws_gate_up : nullptr, hid, hid_shared, (hipStream_t)stream));
+                                        shared ? ws_gate_up : nullptr, hid, hid_shared,
+                                        static_cast<int32_t*>(workspace), (hipStream_t)stream));
 }
 
 moe_status moe_expert_down(const moe_shape* shape, const int32_t* expert_offsets, const uint16_t* hid,
                            const uint16_t* hid_shared, const uint16_t* w_down, const uint16_t* ws_down,
-                           uint16_t* y_perm, float* y_shared, void* stream) {
+                           uint16_t* y_perm, float* y_shared, void* workspace, size_t ws_bytes, void* stream) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
   if (!expert_offsets || !hid || !w_down || !y_perm) return MOE_ERR_INVALID_ARGUMENT;
@@ -145,9 +147,11 @@ moe_status moe_expert_down(const moe_shape* shape, const int32_t* expert_offsets
   if (!aligned16(hid) || !aligned16(w_down) || !aligned16(y_perm) || !aligned4(expert_offsets) ||
       (shared && (!aligned16(hid_shared) || !aligned16(ws_down) || !aligned16(y_shared))))
     return MOE_ERR_MISALIGNED;
+  if ((st = check_workspace(shape, workspace, ws_bytes)) != MOE_OK) return st;
   return hip_status(moe::launch_down(shape->num_tokens, shape->d_model, shape->num_experts, shape->top_k,
                                      shape->d_expert, shape->d_shared, expert_offsets, hid, hid_shared, w_down,
-                                     shared ? ws_down : nullptr, y_perm, y_shared, (hipStream_t)stream));
+                                     shared ? ws_down : nullptr, y_perm, y_shared, static_cast<int32_t*>(workspace),
+                                     (hipStream_t)stream));
 }
 
 moe_status moe_expert_swiglu(const moe_shape* shape, const uint16_t* x, const int32_t* expert_offsets,
@@ -164,14 +168,18 @@ moe_status moe_expert_swiglu(const moe_shape* shape, const uint16_t* x, const in
       (shared && (!aligned16(ws_gate_up) || !aligned16(ws_down) || !aligned16(y_shared))))
     return MOE_ERR_MISALIGNED;
   if ((st = check_workspace(shape, workspace, ws_bytes)) != MOE_OK) return st;
-  uint16_t* hid = static_cast<uint16_t*>(workspace);
-  uint16_t* hid_shared =
-      shared ? hid + moe::expert_hid_bytes(shape->num_tokens, shape->top_k, shape->d_expert) / 2 : nullptr;
-  st = moe_expert_gate_up(shape, x, expert_offsets, perm_pairs, w_gate_up, shared ? ws_gate_up : nullptr, hid,
-                          hid_shared, stream);
-  if (st != MOE_OK) return st;
-  return moe_expert_down(shape, expert_offsets, hid, hid_shared, w_down, shared ? ws_down : nullptr, y_perm,
-                         shared ? y_shared : nullptr, stream);
+  // Workspace: [work queue | hid | hid_shared].
+  const int T = shape->num_tokens, d = shape->d_model, E = shape->num_experts, k = shape->top_k;
+  const int h = shape->d_expert, hs = shape->d_shared;
+  int32_t* queue = static_cast<int32_t*>(workspace);
+  uint16_t* hid = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + moe::kQueueBytes);
+  uint16_t* hid_shared = shared ? hid + moe::expert_hid_bytes(T, k, h) / 2 : nullptr;
+  hipError_t err = moe::launch_gate_up(T, d, E, k, h, hs, x, expert_offsets, perm_pairs, w_gate_up,
+                                       shared ? ws_gate_up : nullptr, hid, hid_shared, queue, (hipStream_t)stream);
+  if (err == hipSuccess)
+    err = moe::launch_down(T, d, E, k, h, hs, expert_offsets, hid, hid_shared, w_down, shared ? ws_down : nullptr,
+                           y_perm, shared ? y_shared : nullptr, queue, (hipStream_t)stream);
+  return hip_status(err);
 }
 
 moe_status moe_shared_swiglu(const moe_shape* shape, const uint16_t* x, const uint16_t* ws_gate_up,
@@ -186,12 +194,14 @@ moe_status moe_shared_swiglu(const moe_shape* shape, const uint16_t* x, const ui
   if ((st = check_workspace(shape, workspace, ws_bytes)) != MOE_OK) return st;
   const int T = shape->num_tokens, d = shape->d_model, E = shape->num_experts, k = shape->top_k;
   const int h = shape->d_expert, hs = shape->d_shared;
-  uint16_t* hid_shared = static_cast<uint16_t*>(workspace);
+  // Workspace: [work queue | hid_shared].
+  int32_t* queue = static_cast<int32_t*>(workspace);
+  uint16_t* hid_shared = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + moe::kQueueBytes);
   hipError_t err = moe::launch_gate_up(T, d, E, k, h, hs, x, nullptr, nullptr, nullptr, ws_gate_up, nullptr,
-                                       hid_shared, (hipStream_t)stream);
+                                       hid_shared, queue, (hipStream_t)stream);
   if (err == hipSuccess)
     err = moe::launch_down(T, d, E, k, h, hs, nullptr, nullptr, hid_shared, nullptr, ws_down, nullptr, y_shared,
-                           (hipStream_t)stream);
+                           queue, (hipStream_t)stream);
   return hip_status(err);
 }
 

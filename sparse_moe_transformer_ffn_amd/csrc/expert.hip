@@ -6,21 +6,17 @@
 // [Blog] "Step 3.5 Flash: Open Frontier-Level Intelligence with 11B Active
 // Parameters" §3.2.4 (fused MoE gather/scatter with grouped GEMM).
 //
-// Work decomposition.  A "group" is one expert's rows of the permuted order
-// (or all T tokens for the shared expert).  Each group is cut into M-tiles of
-// BM rows; an item is (group, N-tile, M-tile) with the M-tile index fastest,
-// so items that run side by side on one XCD read the same weight slab and the
-// same group's activation rows through that XCD's L2.  Blocks are persistent:
-// each builds the per-group tile prefix in LDS once from expert_offsets (no
-// host round trip for the data-dependent group sizes) and strides over the
-// items.  Block b's first item is chosen so that every XCD owns a contiguous
-// range of items at each step.
+// These are the streaming-regime kernels (few rows per expert: decode-sized
+// batches), where the weights are read once and the MFMA work is small: every
+// wave loads its operands straight from HBM/L2 into registers, keeping eight
+// K-steps of weight rows in flight.  The item decomposition is in grouped.h.
 //
 // Phase 1 (gate/up): item = BM rows x 64 hidden units; each of the 4 waves
 // owns 16 hidden units j and computes both G = X W_g[j]^T and U = X W_u[j]^T
 // so that SwiGLU (SiLU(G) * U) is applied in registers before the bf16 store.
 // Phase 2 (down): item = BM rows x 64 output columns, reduction over h.
 #include "common.h"
+#include "grouped.h"
 #include "kernels.h"
 
 namespace moe {
@@ -28,101 +24,6 @@ namespace moe {
 namespace {
 
 constexpr int kUnroll = 8;  // K steps (of 32) per batch of loads
-constexpr int kMaxGroups = 1280;
-
-// The groups of one grouped launch: routed experts 0..E-1 (rows
-// expert_offsets[g] .. expert_offsets[g+1] of the permuted order, token =
-// perm_pairs[row] / k) and, if `shared`, one more group E holding every token
-// in order (the shared expert, hidden size hs).
-struct Groups {
-  const int32_t* offsets;  // [E+1], NULL: no routed groups
-  const int32_t* perm;
-  int E, k, T;
-  bool shared;
-  __host__ __device__ int count() const { return (offsets ? E : 0) + (shared ? 1 : 0); }
-};
-
-struct GroupView {
-  bool shared;
-  int row0, nrows;
-};
-
-__device__ __forceinline__ GroupView group_view(const Groups& gs, int g) {
-  GroupView v;
-  v.shared = !gs.offsets || g >= gs.E;
-  v.row0 = v.shared ? 0 : gs.offsets[g];
-  v.nrows = v.shared ? gs.T : gs.offsets[g + 1] - v.row0;
-  return v;
-}
-
-// ip[g] = number of items of the groups before g (an item is one BM-row
-// M-tile times one N-tile; N-tiles per group: nt_routed or nt_shared), in
-// LDS; ip[G] = total.  256 threads, G <= kMaxGroups.  Returns the total.
-template <int BM>
-__device__ int item_prefix(int* ip, int* wsum, const Groups& gs, int nt_routed, int nt_shared) {
-  constexpr int PER = (kMaxGroups + 255) / 256;
-  const int G = gs.count();
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  int cnt[PER], local = 0;
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    const int g = tid * PER + q;
-    cnt[q] = 0;
-    if (g < G) {
-      const GroupView v = group_view(gs, g);
-      cnt[q] = (v.nrows + BM - 1) / BM * (v.shared ? nt_shared : nt_routed);
-    }
-    local += cnt[q];
-  }
-  int incl = local;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int v = __shfl_up(incl, off);
-    if (lane >= off) incl += v;
-  }
-  if (lane == kWave - 1) wsum[wave] = incl;
-  __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += wsum[w];
-  const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-  int run = base + incl - local;
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    const int g = tid * PER + q;
-    if (g < G) ip[g] = run;
-    run += cnt[q];
-  }
-  if (tid == 0) ip[G] = total;
-  __syncthreads();
-  return total;
-}
-
-struct Item {
-  int group, nt, m0, row0, nrows;
-  bool shared;
-};
-
-// Item w -> (group, N-tile, first row), M-tile index fastest inside a group.
-// Groups without items are skipped by taking the largest g with ip[g] <= w.
-__device__ __forceinline__ Item decode_item(const int* ip, const Groups& gs, int BM, int w) {
-  int lo = 0, hi = gs.count() - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (ip[mid] <= w) lo = mid;
-    else hi = mid - 1;
-  }
-  const GroupView v = group_view(gs, lo);
-  Item it;
-  it.group = lo;
-  it.shared = v.shared;
-  it.row0 = v.row0;
-  it.nrows = v.nrows;
-  const int tiles = (v.nrows + BM - 1) / BM;
-  const int wl = w - ip[lo];
-  it.nt = wl / tiles;
-  it.m0 = (wl - it.nt * tiles) * BM;
-  return it;
-}
 
 }  // namespace
 
@@ -142,7 +43,7 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
   const int r16 = lane & 15, kq = lane >> 4;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   for (int w = xcd_contiguous(blockIdx.x, gridDim.x); w < items; w += gridDim.x) {
-    const Item it = decode_item(ip, gs, BM, w);
+    const Item it = decode_item<0>(ip, gs, BM, h / 64, hs / 64, w);
     const int H = it.shared ? hs : h;
     const int j = it.nt * 64 + wave * 16 + r16;
     const uint16_t* wbase = it.shared ? ws_gu : w_gu + (size_t)it.group * 2 * h * d;
@@ -228,7 +129,7 @@ __global__ __launch_bounds__(256) void k_down(Groups gs, int d, int h, int hs, c
   const int r16 = lane & 15, kq = lane >> 4;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   for (int w = xcd_contiguous(blockIdx.x, gridDim.x); w < items; w += gridDim.x) {
-    const Item it = decode_item(ip, gs, BM, w);
+    const Item it = decode_item<0>(ip, gs, BM, d / 64, d / 64, w);
     const int H = it.shared ? hs : h;
     const int n = it.nt * 64 + wave * 16 + r16;
     const uint16_t* pb = (it.shared ? ws_down : w_down + (size_t)it.group * d * h) + (size_t)n * H + kq * 8;
@@ -283,24 +184,13 @@ __global__ __launch_bounds__(256) void k_down(Groups gs, int d, int h, int hs, c
 
 namespace {
 
-constexpr int kMaxDevices = 64;
-
-// Persistent grid: as many blocks as can be resident at once on the current
-// device (occupancy x compute units), so that no block starts late and every
-// block strides over its share of the items.  Cached per kernel and device.
-template <class Kernel>
-int persistent_grid(Kernel kernel) {
-  static int cache[kMaxDevices] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
-  if (cache[dev] == 0) {
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu < 1)
-      per_cu = 1;
-    cache[dev] = cus * per_cu;
-  }
-  return cache[dev];
+// Average rows per routed group (or all T rows when only the shared expert
+// runs) decides the regime: >= 64 rows is compute-bound work for the tiled
+// kernels.
+bool use_tiled(int T, int k, int E, const int32_t* offsets) {
+  const long rows = offsets ? (long)T * k : (long)T;
+  const long groups = offsets ? E : 1;
+  return rows >= 64L * groups;
 }
 
 int pick_bm(int T, int k, int E) {
@@ -329,23 +219,15 @@ hipError_t down_bm(const Groups& gs, int d, int h, int hs, const uint16_t* hid, 
   return hipGetLastError();
 }
 
-Groups make_groups(int T, int E, int k, const int32_t* offsets, const int32_t* perm, bool shared) {
-  Groups gs;
-  gs.offsets = offsets;
-  gs.perm = perm;
-  gs.E = E;
-  gs.k = k;
-  gs.T = T;
-  gs.shared = shared;
-  return gs;
-}
-
 }  // namespace
 
 hipError_t launch_gate_up(int T, int d, int E, int k, int h, int hs, const uint16_t* x, const int32_t* offsets,
                           const int32_t* perm, const uint16_t* w_gu, const uint16_t* ws_gu, uint16_t* hid,
-                          uint16_t* hid_shared, hipStream_t stream) {
+                          uint16_t* hid_shared, int32_t* queue, hipStream_t stream) {
   if (T == 0) return hipSuccess;
+  // The tiled gate/up item covers 128 hidden units of each group.
+  if (use_tiled(T, k, E, offsets) && h % 128 == 0 && hs % 128 == 0)
+    return launch_gate_up_tiled(T, d, E, k, h, hs, x, offsets, perm, w_gu, ws_gu, hid, hid_shared, queue, stream);
   const Groups gs = make_groups(T, E, k, offsets, perm, ws_gu != nullptr);
   if (pick_bm(T, k, offsets ? E : 1) == 16)
     return gate_up_bm<16>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, stream);
@@ -354,8 +236,12 @@ hipError_t launch_gate_up(int T, int d, int E, int k, int h, int hs, const uint1
 
 hipError_t launch_down(int T, int d, int E, int k, int h, int hs, const int32_t* offsets, const uint16_t* hid,
                        const uint16_t* hid_shared, const uint16_t* w_down, const uint16_t* ws_down, uint16_t* y_perm,
-                       float* y_shared, hipStream_t stream) {
+                       float* y_shared, int32_t* queue, hipStream_t stream) {
   if (T == 0) return hipSuccess;
+  // The tiled down item covers 256 output columns.
+  if (use_tiled(T, k, E, offsets) && d % 256 == 0)
+    return launch_down_tiled(T, d, E, k, h, hs, offsets, hid, hid_shared, w_down, ws_down, y_perm, y_shared, queue,
+                             stream);
   const Groups gs = make_groups(T, E, k, offsets, nullptr, ws_down != nullptr);
   if (pick_bm(T, k, offsets ? E : 1) == 16)
     return down_bm<16>(gs, d, h, hs, hid, hid_shared, w_down, ws_down, y_perm, y_shared, stream);

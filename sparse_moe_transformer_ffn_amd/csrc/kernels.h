@@ -23,13 +23,23 @@ size_t permute_workspace_bytes(int T, int E);
 
 // Grouped expert GEMMs.  Routed groups come from expert_offsets/perm (NULL
 // offsets: none); the shared expert is one more group when its weights are
-// given (ws_gu / ws_down non-NULL).
+// given (ws_gu / ws_down non-NULL).  `queue` is kQueueBytes of device scratch
+// for the work queue of the compute-regime kernels.
+constexpr size_t kQueueBytes = 256;
 hipError_t launch_gate_up(int T, int d, int E, int k, int h, int hs, const uint16_t* x, const int32_t* offsets,
                           const int32_t* perm, const uint16_t* w_gu, const uint16_t* ws_gu, uint16_t* hid,
-                          uint16_t* hid_shared, hipStream_t stream);
+                          uint16_t* hid_shared, int32_t* queue, hipStream_t stream);
 hipError_t launch_down(int T, int d, int E, int k, int h, int hs, const int32_t* offsets, const uint16_t* hid,
                        const uint16_t* hid_shared, const uint16_t* w_down, const uint16_t* ws_down, uint16_t* y_perm,
-                       float* y_shared, hipStream_t stream);
+                       float* y_shared, int32_t* queue, hipStream_t stream);
+// The compute-regime (LDS-tiled, MFMA 32x32x16) versions of the same two
+// phases; the launchers above pick them when groups are large.
+hipError_t launch_gate_up_tiled(int T, int d, int E, int k, int h, int hs, const uint16_t* x, const int32_t* offsets,
+                                const int32_t* perm, const uint16_t* w_gu, const uint16_t* ws_gu, uint16_t* hid,
+                                uint16_t* hid_shared, int32_t* queue, hipStream_t stream);
+hipError_t launch_down_tiled(int T, int d, int E, int k, int h, int hs, const int32_t* offsets, const uint16_t* hid,
+                             const uint16_t* hid_shared, const uint16_t* w_down, const uint16_t* ws_down,
+                             uint16_t* y_perm, float* y_shared, int32_t* queue, hipStream_t stream);
 size_t expert_hid_bytes(int T, int k, int h);
 size_t shared_hid_bytes(int T, int hs);
 

@@ -129,14 +129,17 @@ def test_expert_and_shared_validation():
     assert L.moe_expert_swiglu(ctypes.byref(s), A, A, A, A, A, A, A, A, A + 8, A, nb, None) == MISALIGNED
     no_shared = shape(1, d_shared=0)
     assert L.moe_expert_swiglu(ctypes.byref(no_shared), A, A, A, A, A, A, A, A, A, A, nb, None) == INVALID
-    # moe_expert_gate_up(shape, x, off, perm, w_gu, ws_gu, hid, hid_shared, stream)
-    assert L.moe_expert_gate_up(ctypes.byref(s), A, A, A, A, None, None, None, None) == INVALID
-    assert L.moe_expert_gate_up(ctypes.byref(s), A, A, A, MIS, None, A, None, None) == MISALIGNED
-    assert L.moe_expert_gate_up(ctypes.byref(s), A, A, A, A, A, A, None, None) == INVALID
-    # moe_expert_down(shape, off, hid, hid_shared, w_d, ws_d, y_perm, y_shared, stream)
-    assert L.moe_expert_down(ctypes.byref(s), A, A, None, A, None, None, None, None) == INVALID
-    assert L.moe_expert_down(ctypes.byref(s), A, A, None, MIS, None, A, None, None) == MISALIGNED
-    assert L.moe_expert_down(ctypes.byref(s), A, A, A, A, A, A, None, None) == INVALID
+    # moe_expert_gate_up(shape, x, off, perm, w_gu, ws_gu, hid, hid_shared, ws, nb, stream)
+    assert L.moe_expert_gate_up(ctypes.byref(s), A, A, A, A, None, None, None, A, nb, None) == INVALID
+    assert L.moe_expert_gate_up(ctypes.byref(s), A, A, A, MIS, None, A, None, A, nb, None) == MISALIGNED
+    assert L.moe_expert_gate_up(ctypes.byref(s), A, A, A, A, A, A, None, A, nb, None) == INVALID
+    assert L.moe_expert_gate_up(ctypes.byref(s), A, A, A, A, None, A, None, None, nb, None) == INVALID
+    assert L.moe_expert_gate_up(ctypes.byref(s), A, A, A, A, None, A, None, A, 8, None) == WS_SMALL
+    # moe_expert_down(shape, off, hid, hid_shared, w_d, ws_d, y_perm, y_shared, ws, nb, stream)
+    assert L.moe_expert_down(ctypes.byref(s), A, A, None, A, None, None, None, A, nb, None) == INVALID
+    assert L.moe_expert_down(ctypes.byref(s), A, A, None, MIS, None, A, None, A, nb, None) == MISALIGNED
+    assert L.moe_expert_down(ctypes.byref(s), A, A, A, A, A, A, None, A, nb, None) == INVALID
+    assert L.moe_expert_down(ctypes.byref(s), A, A, None, A, None, A, None, A, 8, None) == WS_SMALL
     assert L.moe_shared_swiglu(ctypes.byref(s), A, A, None, A, A, nb, None) == INVALID
     assert L.moe_shared_swiglu(ctypes.byref(s), A, A, A, A + 4, A, nb, None) == MISALIGNED
     assert L.moe_shared_swiglu(ctypes.byref(s), A, A, A, A, A, 16, None) == WS_SMALL

@@ -155,8 +155,8 @@ def test_expert_swiglu_parity(device, idx):
     # The phase entry points give the same rows as the combined call.
     hid = torch.empty((cfg.T * cfg.k, cfg.h), dtype=torch.bfloat16, device="cuda")
     y2 = torch.zeros_like(y_perm)
-    moe.moe_expert_gate_up(s, dl.x, i32_dev(off), i32_dev(perm), dl.w_gu, hid)
-    moe.moe_expert_down(s, i32_dev(off), hid, dl.w_d, y2)
+    moe.moe_expert_gate_up(s, dl.x, i32_dev(off), i32_dev(perm), dl.w_gu, hid, ws)
+    moe.moe_expert_down(s, i32_dev(off), hid, dl.w_d, y2, ws)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(bf16_host(y2), bf16_host(y_perm))
     # With the shared expert fused into the same launches: routed rows

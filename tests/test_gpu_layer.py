@@ -90,6 +90,21 @@ def test_layer_edge_shapes(device, T, k, hs, scale):
     check_layer(dl, buf, np.arange(T))
 
 
+@pytest.mark.parametrize("T,d,E,k,h,hs", [
+    (2048, 256, 16, 2, 128, 128),    # ~256 rows per expert: the tiled kernels
+    (1000, 512, 16, 2, 256, 384),    # ragged M-tiles, shared hidden != routed
+    (1000, 256, 16, 2, 128, 192),    # hidden % 128 != 0: direct gate/up, tiled down
+    (700, 192, 8, 3, 64, 64),        # d % 256 != 0: direct kernels in the compute regime
+    (1536, 512, 6, 1, 256, 0),       # k = 1, no shared expert
+])
+def test_layer_compute_regime_small(device, T, d, E, k, h, hs):
+    cfg = moegen.custom(0, T=T, d=d, E=E, k=k, h=h, hs=hs, seed=900 + T)
+    log(f"[layer-tiled] T={T} d={d} E={E} k={k} h={h} hs={hs}")
+    dl = DeviceLayer(cfg)
+    buf = run_layer(dl)
+    check_layer(dl, buf, np.arange(T))
+
+
 def test_layer_all_tokens_one_expert(device):
     # A bias of +10 on one expert sends every token there (ties elsewhere
     # broken normally): one group of T rows, most experts idle.
