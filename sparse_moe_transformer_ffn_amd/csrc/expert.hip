@@ -27,10 +27,16 @@ constexpr int kUnroll = 8;  // K steps (of 32) per batch of loads
 
 }  // namespace
 
-// Phase 1: hid[row, j] = SiLU(x_row . W_g[j]) * (x_row . W_u[j]) for the
-// item's BM rows and 64 hidden units j.  Routed rows gather their token via
-// perm_pairs; shared rows are tokens in order.
-template <int BM>
+// Phase 1: hid[row, j] = SiLU(x_row . W_g[j]) * (x_row . W_u[j]).  Routed
+// rows gather their token via perm_pairs; shared rows are tokens in order.
+// KW = 1: an item is BM rows x 64 hidden units, wave w owns units 16w..16w+15
+//         over the whole reduction.
+// KW = 4: an item is BM rows x 16 hidden units and wave w owns the w-th
+//         quarter of the reduction; the four partial sums meet in LDS and are
+//         added in wave order (a fixed order: results do not depend on the
+//         schedule).  Items are four times smaller, so the last items of the
+//         launch, which run alone, take a quarter of the time.
+template <int BM, int KW>
 __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x, Groups gs, int d, int h, int hs,
                                                  const uint16_t* __restrict__ w_gu,
                                                  const uint16_t* __restrict__ ws_gu, uint16_t* __restrict__ hid,
@@ -38,18 +44,21 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
   __shared__ int ip[kMaxGroups + 1];
   __shared__ int wsum[4];
   constexpr int MB = BM / 16;
-  const int items = item_prefix<BM>(ip, wsum, gs, h / 64, hs / 64);
+  constexpr int UNITS = 64 / KW;  // hidden units per item
+  __shared__ float red[KW > 1 ? KW - 1 : 1][2 * MB * 4][kWave];
+  const int items = item_prefix<BM>(ip, wsum, gs, h / UNITS, hs / UNITS);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int r16 = lane & 15, kq = lane >> 4;
+  const int klen = d / KW, kbeg = KW > 1 ? wave * klen : 0;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   for (int w = xcd_contiguous(blockIdx.x, gridDim.x); w < items; w += gridDim.x) {
-    const Item it = decode_item<0>(ip, gs, BM, h / 64, hs / 64, w);
+    const Item it = decode_item<0>(ip, gs, BM, h / UNITS, hs / UNITS, w);
     const int H = it.shared ? hs : h;
-    const int j = it.nt * 64 + wave * 16 + r16;
+    const int j = it.nt * UNITS + (KW > 1 ? 0 : wave * 16) + r16;
     const uint16_t* wbase = it.shared ? ws_gu : w_gu + (size_t)it.group * 2 * h * d;
     uint16_t* out = it.shared ? hid_shared : hid;
-    const uint16_t* pg = wbase + (size_t)j * d + kq * 8;
-    const uint16_t* pu = wbase + (size_t)(H + j) * d + kq * 8;
+    const uint16_t* pg = wbase + (size_t)j * d + kbeg + kq * 8;
+    const uint16_t* pu = wbase + (size_t)(H + j) * d + kbeg + kq * 8;
     const uint16_t* pa[MB];
     bool va[MB];
 #pragma unroll
@@ -58,7 +67,7 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
       va[mb] = r < it.nrows;
       int tok = 0;
       if (va[mb]) tok = it.shared ? r : gs.perm[it.row0 + r] / gs.k;
-      pa[mb] = x + (size_t)tok * d + kq * 8;
+      pa[mb] = x + (size_t)tok * d + kbeg + kq * 8;
     }
     f32x4 ag[MB], au[MB];
 #pragma unroll
@@ -70,7 +79,7 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
     // its MFMAs, so each wave keeps kUnroll weight rows' worth of requests in
     // flight (the streaming regime is latency x bandwidth bound).
     int kk = 0;
-    for (; kk + 32 * kUnroll <= d; kk += 32 * kUnroll) {
+    for (; kk + 32 * kUnroll <= klen; kk += 32 * kUnroll) {
       u32x4 bg[kUnroll], bu[kUnroll], a[MB][kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
@@ -89,7 +98,7 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
           au[mb] = mfma_16x16x32(a[mb][u], bu[u], au[mb]);
         }
     }
-    for (; kk < d; kk += 32) {
+    for (; kk < klen; kk += 32) {
       const u32x4 bg = load16(pg + kk);
       const u32x4 bu = load16(pu + kk);
 #pragma unroll
@@ -98,6 +107,32 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
         ag[mb] = mfma_16x16x32(a, bg, ag[mb]);
         au[mb] = mfma_16x16x32(a, bu, au[mb]);
       }
+    }
+    if (KW > 1) {
+      // Waves 1..KW-1 hand their partial sums to wave 0.
+      if (wave > 0) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            red[wave - 1][mb * 8 + i][lane] = ag[mb][i];
+            red[wave - 1][mb * 8 + 4 + i][lane] = au[mb][i];
+          }
+      }
+      __syncthreads();
+      if (wave == 0) {
+#pragma unroll
+        for (int q = 0; q < KW - 1; ++q)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              ag[mb][i] += red[q][mb * 8 + i][lane];
+              au[mb][i] += red[q][mb * 8 + 4 + i][lane];
+            }
+      }
+      __syncthreads();  // red[] free for the next item
+      if (wave > 0) continue;
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -200,10 +235,10 @@ int pick_bm(int T, int k, int E) {
   return rows <= 16L * E ? 16 : 32;
 }
 
-template <int BM>
+template <int BM, int KW>
 hipError_t gate_up_bm(const uint16_t* x, const Groups& gs, int d, int h, int hs, const uint16_t* w_gu,
                       const uint16_t* ws_gu, uint16_t* hid, uint16_t* hid_shared, hipStream_t stream) {
-  const auto kern = k_gate_up<BM>;
+  const auto kern = k_gate_up<BM, KW>;
   hipLaunchKernelGGL(kern, dim3(persistent_grid(kern)), dim3(256), 0, stream, x, gs, d, h, hs, w_gu, ws_gu, hid,
                      hid_shared);
   return hipGetLastError();
@@ -229,9 +264,14 @@ hipError_t launch_gate_up(int T, int d, int E, int k, int h, int hs, const uint1
   if (use_tiled(T, k, E, offsets) && h % 128 == 0 && hs % 128 == 0)
     return launch_gate_up_tiled(T, d, E, k, h, hs, x, offsets, perm, w_gu, ws_gu, hid, hid_shared, queue, stream);
   const Groups gs = make_groups(T, E, k, offsets, perm, ws_gu != nullptr);
-  if (pick_bm(T, k, offsets ? E : 1) == 16)
-    return gate_up_bm<16>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, stream);
-  return gate_up_bm<32>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, stream);
+  // Reduction split over the waves when every quarter is whole 32-wide steps.
+  const bool split = d % 128 == 0;
+  if (pick_bm(T, k, offsets ? E : 1) == 16) {
+    if (split) return gate_up_bm<16, 4>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, stream);
+    return gate_up_bm<16, 1>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, stream);
+  }
+  if (split) return gate_up_bm<32, 4>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, stream);
+  return gate_up_bm<32, 1>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, stream);
 }
 
 hipError_t launch_down(int T, int d, int E, int k, int h, int hs, const int32_t* offsets, const uint16_t* hid,
@@ -243,6 +283,8 @@ hipError_t launch_down(int T, int d, int E, int k, int h, int hs, const int32_t*
     return launch_down_tiled(T, d, E, k, h, hs, offsets, hid, hid_shared, w_down, ws_down, y_perm, y_shared, queue,
                              stream);
   const Groups gs = make_groups(T, E, k, offsets, nullptr, ws_down != nullptr);
+  // The down reduction (the expert hidden size) is short enough already:
+  // quarters of it are too few steps to keep loads in flight.
   if (pick_bm(T, k, offsets ? E : 1) == 16)
     return down_bm<16>(gs, d, h, hs, hid, hid_shared, w_down, ws_down, y_perm, y_shared, stream);
   return down_bm<32>(gs, d, h, hs, hid, hid_shared, w_down, ws_down, y_perm, y_shared, stream);

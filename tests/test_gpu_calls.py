@@ -12,8 +12,8 @@ import torch
 import moegen
 import oracle
 import sparse_moe_transformer_ffn_amd as moe
-from tests.gpu_harness import (DeviceLayer, bf16_dev, bf16_host, check_output, check_routing, f32_dev, i32_dev, log,
-                               oracle_route_all, stream_ptr)
+from tests.gpu_harness import (DeviceLayer, assert_same_up_to_order, bf16_dev, bf16_host, check_output, check_routing,
+                               f32_dev, i32_dev, log, oracle_route_all, stream_ptr)
 
 pytestmark = pytest.mark.gpu
 
@@ -168,7 +168,8 @@ def test_expert_swiglu_parity(device, idx):
     moe.moe_shared_swiglu(s, dl.x, dl.ws_gu, dl.ws_d, ys_alone, ws)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(bf16_host(y3), bf16_host(y_perm))
-    np.testing.assert_array_equal(ys_fused.cpu().numpy(), ys_alone.cpu().numpy())
+    # The standalone call may pick another kernel (another reduction split).
+    assert_same_up_to_order(ys_fused.cpu().numpy(), ys_alone.cpu().numpy(), "fused vs standalone shared")
 
 
 @pytest.mark.parametrize("idx", [0, 1])

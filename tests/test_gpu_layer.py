@@ -16,8 +16,8 @@ import torch
 import moegen
 import oracle
 import sparse_moe_transformer_ffn_amd as moe
-from tests.gpu_harness import (DeviceLayer, bf16_dev, bf16_host, check_output, check_routing, log,
-                               oracle_layer_tokens, oracle_route_all)
+from tests.gpu_harness import (DeviceLayer, assert_same_up_to_order, bf16_dev, bf16_host, check_output, check_routing,
+                               log, oracle_layer_tokens, oracle_route_all)
 
 pytestmark = pytest.mark.gpu
 
@@ -64,21 +64,25 @@ def test_layer_all_tokens(device, idx):
 
 @pytest.mark.parametrize("idx", [0, 1])
 def test_layer_is_deterministic(device, idx):
-    # Same inputs, same bits: fused shared expert, shared expert on a side
-    # stream, shared expert after the routed ones, and a rerun into the same
-    # buffers.
+    # A rerun into the same buffers gives the same bits.  Running the shared
+    # expert on a side stream or after the routed ones gives the same routing
+    # and, since the standalone shared call may split its reductions
+    # differently, the same output up to summation order.
     cfg = moegen.CONFIGS[idx]
     log(f"[determinism] config {idx}")
     dl = DeviceLayer(cfg)
     a = run_layer(dl, shared="fused")
     ya = bf16_host(a.y).copy()
     ia = a.topk_ids.cpu().numpy().copy()
-    for mode in ("stream", "serial"):
-        b = run_layer(dl, shared=mode)
-        np.testing.assert_array_equal(bf16_host(b.y), ya)
-        np.testing.assert_array_equal(b.topk_ids.cpu().numpy(), ia)
     c = run_layer(dl, buf=a, shared="fused")
     np.testing.assert_array_equal(bf16_host(c.y), ya)
+    for mode in ("stream", "serial"):
+        b = run_layer(dl, shared=mode)
+        np.testing.assert_array_equal(b.topk_ids.cpu().numpy(), ia)
+        assert_same_up_to_order(bf16_host(b.y), ya, f"shared {mode} vs fused")
+    s1 = run_layer(dl, shared="serial")
+    s2 = run_layer(dl, shared="serial")
+    np.testing.assert_array_equal(bf16_host(s1.y), bf16_host(s2.y))
 
 
 @pytest.mark.parametrize("T,k,hs,scale", [(1, 8, 1280, 1.0), (3, 1, 1280, 1.0), (97, 8, 0, 0.5), (130, 8, 1280, 2.0)])
