@@ -14,6 +14,7 @@ after it and reported in the "prefill" object.  Prints one JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill]
                        [--no-cpu-baseline] [--cpu-sample N]
+       python bench.py --write-traffic PMC_DIR   (HBM bytes from counter runs)
 """
 import argparse
 import hashlib
@@ -31,9 +32,22 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+# Sources of the two grouped expert kernels: counter readings are valid for
+# the build they were taken on only.
+EXPERT_SOURCES = ("expert.hip", "expert_tiled.hip", "grouped.h", "common.h")
+# Kernel-name patterns of each phase: the streaming kernels (decode) and the
+# LDS-tiled kernels (prefill).
+PHASE_KERNELS = {"gate_up": ("k_gate_up<", "k_expert_tiled<0>"), "down": ("k_down<", "k_expert_tiled<1>")}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 1 << 30            # the --copy-probe copy: bytes read, and bytes written, per copy
+
+
 def kernel_source_hash() -> str:
-    src = os.path.join(ROOT, "sparse_moe_transformer_ffn_amd", "csrc", "expert.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in EXPERT_SOURCES:
+        with open(os.path.join(ROOT, "sparse_moe_transformer_ffn_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload: str, kernel: str):
@@ -42,10 +56,62 @@ def load_traffic(workload: str, kernel: str):
     path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path))
+    with open(path) as f:
+        rec = json.load(f)
     if rec.get("source_hash") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _counter_means(pmc_dir, run, counter, patterns):
+    """Mean counter value (KiB) per dispatch of the kernels matching any of
+    `patterns` in one rocprofv3 --pmc run, and the number of dispatches."""
+    import csv
+    path = os.path.join(pmc_dir, run, f"{run}_counter_collection.csv")
+    with open(path) as f:
+        vals = [float(r["Counter_Value"]) for r in csv.DictReader(f)
+                if r["Counter_Name"] == counter and any(p in r["Kernel_Name"] for p in patterns)]
+    if not vals:
+        raise SystemExit(f"{path}: no {counter} rows for {patterns}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def write_traffic(pmc_dir):
+    """Turn rocprofv3 counter runs into per-launch HBM bytes of the expert
+    kernels: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by the
+    ratio of known bytes to what the same counter reads for a plain device
+    copy of COPY_BYTES.  Expects runs named copy_fetch, copy_write (this
+    script with --copy-probe) and {dec,pre}_{fetch,write} (the decode and
+    prefill workloads), each made with one counter:
+
+      rocprofv3 --pmc FETCH_SIZE -f csv -d <pmc_dir>/copy_fetch -o copy_fetch -- python3 bench.py --copy-probe
+      rocprofv3 --pmc FETCH_SIZE -f csv -d <pmc_dir>/dec_fetch -o dec_fetch -- \
+          python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-prefill
+      rocprofv3 --pmc FETCH_SIZE -f csv -d <pmc_dir>/pre_fetch -o pre_fetch -- \
+          python3 bench.py --steps 2 --warmup 1 --only-prefill
+      (and the same three with WRITE_SIZE into *_write)
+    """
+    copy_fetch, _ = _counter_means(pmc_dir, "copy_fetch", "FETCH_SIZE", (COPY_KERNEL,))
+    copy_write, _ = _counter_means(pmc_dir, "copy_write", "WRITE_SIZE", (COPY_KERNEL,))
+    f_fetch = COPY_BYTES / (copy_fetch * 1024)
+    f_write = COPY_BYTES / (copy_write * 1024)
+    src = kernel_source_hash()
+    for workload, run in (("decode", "dec"), ("prefill", "pre")):
+        for kernel, patterns in PHASE_KERNELS.items():
+            fetch, n = _counter_means(pmc_dir, f"{run}_fetch", "FETCH_SIZE", patterns)
+            write, _ = _counter_means(pmc_dir, f"{run}_write", "WRITE_SIZE", patterns)
+            rec = {"workload": workload, "kernel": kernel, "source_hash": src,
+                   "hbm_bytes_per_launch": fetch * 1024 * f_fetch + write * 1024 * f_write,
+                   "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write, "dispatches": n,
+                   "fetch_factor": f_fetch, "write_factor": f_write,
+                   "copy_probe": {"bytes": COPY_BYTES, "fetch_kib": copy_fetch, "write_kib": copy_write},
+                   "made_by": "python bench.py --write-traffic <pmc_dir> over the rocprofv3 runs listed in "
+                              "bench.write_traffic's docstring"}
+            with open(os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json"), "w") as f:
+                json.dump(rec, f, indent=1)
+                f.write("\n")
+            print(f"{workload:8s} {kernel:8s} {rec['hbm_bytes_per_launch'] / 1e9:8.3f} GB per launch "
+                  f"(fetch {fetch:.0f} KiB x {f_fetch:.3f}, write {write:.0f} KiB x {f_write:.3f}, {n} dispatches)")
 
 
 class Workload:
@@ -192,7 +258,12 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=64)
+    ap.add_argument("--write-traffic", metavar="PMC_DIR",
+                    help="no GPU work: write profiles/traffic_*.json from rocprofv3 counter runs in PMC_DIR")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(args.write_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer's hot path is built and timed on a single MI355X "
               "(no expert parallelism across GPUs in this library). Run with --gpus 1.", file=sys.stderr)
