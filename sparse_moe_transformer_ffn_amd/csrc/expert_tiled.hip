@@ -71,9 +71,10 @@ constexpr int kLoadsPerChunk = kLoadsA + kLoadsB;  // 12
 constexpr int kWaitNextChunk = 0x0F70 | kLoadsPerChunk;
 constexpr int kWaitAll = 0x0F70;  // vmcnt(0)
 
-// Cache policy of the direct loads: token rows are re-read by every N-tile of
-// their M-tile (default policy, kept in L2); weight rows are streamed
-// (non-temporal, so they do not push the token rows out of L2).
+// Cache policy of the direct loads: the default for both operands.  Token rows
+// are re-read by every N-tile of their M-tile and weight rows by every M-tile
+// of their band, both through L2 (a non-temporal hint on the weight rows
+// measured slower: it defeats the sharing within a band).
 constexpr int kPolicyReuse = 0;
 constexpr int kPolicyStream = 0;
 
