@@ -11,6 +11,8 @@
 // strides over the items; block b's first item is chosen so that every XCD
 // owns a contiguous range of items at each step.
 #pragma once
+#include <mutex>
+
 #include "common.h"
 
 namespace moe {
@@ -129,22 +131,38 @@ __device__ __forceinline__ Item decode_item(const int* ip, const Groups& gs, int
 
 // Persistent grid: as many blocks as can be resident at once on the current
 // device (occupancy x compute units), so that no block starts late and every
-// block strides over its share of the items.  Cached per kernel and device.
-constexpr int kMaxDevices = 64;
+// block strides over its share of the items.  Cached per kernel (by address:
+// instances of one kernel template share a type but not their occupancy) and
+// device.
+struct GridCacheEntry {
+  const void* kernel;
+  int device;
+  int block_threads;
+  int grid;
+};
+
+inline int persistent_grid_of(const void* kernel, int block_threads) {
+  static std::mutex mu;
+  static GridCacheEntry cache[64];
+  static int used = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < used; ++i)
+    if (cache[i].kernel == kernel && cache[i].device == dev && cache[i].block_threads == block_threads)
+      return cache[i].grid;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block_threads, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int grid = cus * per_cu;
+  if (used < 64) cache[used++] = GridCacheEntry{kernel, dev, block_threads, grid};
+  return grid;
+}
 
 template <class Kernel>
 int persistent_grid(Kernel kernel, int block_threads = 256) {
-  static int cache[kMaxDevices] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
-  if (cache[dev] == 0) {
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block_threads, 0) != hipSuccess || per_cu < 1)
-      per_cu = 1;
-    cache[dev] = cus * per_cu;
-  }
-  return cache[dev];
+  return persistent_grid_of(reinterpret_cast<const void*>(kernel), block_threads);
 }
 
 inline Groups make_groups(int T, int E, int k, const int32_t* offsets, const int32_t* perm, bool shared) {
