@@ -7,8 +7,12 @@
 
 namespace moe {
 
+// How the router's logits are computed: the split of the d-long reduction
+// into ksplit chunks of kchunk, and whether the LDS-staged kernel (large
+// batches) is used.
 struct RouteSplit {
   int ksplit, kchunk;
+  bool tiled;
 };
 RouteSplit route_split(int T, int d, int E);
 

@@ -50,6 +50,150 @@ __global__ __launch_bounds__(256) void k_route_logits(const uint16_t* __restrict
   }
 }
 
+// Large batches: the same partial logits from an LDS-staged GEMM.  A block
+// covers 128 tokens x all E experts (E a multiple of 32, at most 288) over one
+// reduction chunk [k0, k0 + kchunk).  Operands go HBM/L2 -> LDS with direct
+// loads (global_load_lds_dwordx4) through three stages of 64-wide K slices;
+// wave w multiplies tokens [32 w, 32 w + 32) by every expert with MFMA
+// 32x32x16 (E/32 accumulator tiles), so each router slice read from LDS
+// serves 32 tokens and each token slice E experts.  Rows of a slice are eight
+// 16-byte segments stored at slot seg ^ ((row >> 1) & 7) (conflict-free
+// reads of one segment of 32 consecutive rows).
+namespace {
+
+constexpr int kRtM = 128;                    // tokens per block
+constexpr int kRtMaxE = 288;                 // experts held per stage
+constexpr int kRtChunk = 64;                 // K elements per stage
+constexpr int kRtStageA = kRtM * kRtChunk;   // bf16 elements
+constexpr int kRtStage = kRtStageA + kRtMaxE * kRtChunk;  // 52 KiB
+constexpr int kRtLoadsA = kRtM / 8 / 4;      // direct loads per thread per chunk (8 rows each)
+constexpr int kRtLoadsB = kRtMaxE / 8 / 4;
+// s_waitcnt vmcnt(one chunk's loads), lgkmcnt and expcnt not waited on.
+constexpr int kRtWaitChunk = 0x0F70 | (kRtLoadsA + kRtLoadsB);
+static_assert(kRtLoadsA + kRtLoadsB < 16, "vmcnt field");
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ int rt_swz(int row) { return (row >> 1) & 7; }
+
+// Direct loads of one chunk: A regions q*4 + wave (q < kRtLoadsA), then B
+// regions q*4 + wave (q < kRtLoadsB); region r covers rows 8r .. 8r+7 of the
+// stage.  Every thread issues the same number of loads whatever T and E:
+// token rows past T re-read row T-1 and router rows past E re-read row E-1
+// (into stage rows nobody reads), so the in-flight count is a constant.
+__device__ __forceinline__ void rt_issue(const uint16_t* x, const uint16_t* w_router, int T, int d, int E, int t0,
+                                         int kk, uint16_t* stage, int wave, int lane) {
+  const int seg_row = lane / 8, slot = lane % 8;
+#pragma unroll
+  for (int q = 0; q < kRtLoadsA; ++q) {
+    const int row = (q * 4 + wave) * 8 + seg_row;
+    const int t = min(t0 + row, T - 1);
+    const int seg = slot ^ rt_swz(row);
+    __builtin_amdgcn_global_load_lds(x + (size_t)t * d + kk + seg * 8, stage + (q * 4 + wave) * 8 * kRtChunk, 16,
+                                     0, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < kRtLoadsB; ++q) {
+    const int r = q * 4 + wave;
+    const int row = r * 8 + seg_row;
+    const int seg = slot ^ rt_swz(row);
+    __builtin_amdgcn_global_load_lds(w_router + (size_t)min(row, E - 1) * d + kk + seg * 8,
+                                     stage + kRtStageA + r * 8 * kRtChunk, 16, 0, 0);
+  }
+}
+
+}  // namespace
+
+namespace {
+
+// Per-thread constants of the LDS-staged router kernel.
+struct RtLane {
+  const uint16_t* x;
+  const uint16_t* w_router;
+  int T, d, E, t0, k0, nch, wave, lane;
+  int arow;  // LDS row of this lane's token fragment
+  int lhi;   // lane / 32: which 8 of a 16-wide K step
+  int f;     // rt_swz of every row this lane reads
+  int ntile; // E / 32
+};
+
+// Chunk c (in `cur`): chunk c has landed for this thread once only the next
+// chunk's loads remain; the barrier (a bare s_barrier: a release fence would
+// drain the loads in flight) makes it visible to all and guarantees nobody
+// still reads `ahead`, the stage of chunk c-1, which chunk c+2 goes into.
+// Past the last chunk the loads repeat the last chunk into a stage nobody
+// reads, so the count of loads in flight stays the same.
+__device__ __forceinline__ void rt_chunk(const RtLane& ln, const uint16_t* cur, uint16_t* ahead, int c,
+                                         f32x16 (&acc)[kRtMaxE / 32]) {
+  __builtin_amdgcn_s_waitcnt(kRtWaitChunk);
+  __builtin_amdgcn_s_barrier();
+  rt_issue(ln.x, ln.w_router, ln.T, ln.d, ln.E, ln.t0, ln.k0 + min(c + 2, ln.nch - 1) * kRtChunk, ahead, ln.wave,
+           ln.lane);
+#pragma unroll
+  for (int s = 0; s < kRtChunk / 16; ++s) {
+    const int slot = ((2 * s + ln.lhi) ^ ln.f) * 8;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(&cur[ln.arow * kRtChunk + slot]);
+#pragma unroll
+    for (int j = 0; j < kRtMaxE / 32; ++j) {
+      if (j < ln.ntile) {
+        const u32x4 b = *reinterpret_cast<const u32x4*>(&cur[kRtStageA + (j * 32 + (ln.lane & 31)) * kRtChunk + slot]);
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                         acc[j], 0, 0, 0);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void k_route_logits_tiled(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ w_router, int T, int d,
+                                                            int E, int kchunk, float* __restrict__ partial,
+                                                            int32_t* __restrict__ counts) {
+  __shared__ __attribute__((aligned(16))) uint16_t st0[kRtStage];
+  __shared__ __attribute__((aligned(16))) uint16_t st1[kRtStage];
+  __shared__ __attribute__((aligned(16))) uint16_t st2[kRtStage];
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int e = tid; e < E; e += 256) counts[e] = 0;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int l32 = lane & 31, lhi = lane >> 5;
+  const int t0 = blockIdx.x * kRtM;
+  const int k0 = blockIdx.y * kchunk;
+  const int nch = (min(d, k0 + kchunk) - k0) / kRtChunk;  // the last split may be shorter
+  const int ntile = E / 32;
+  f32x16 acc[kRtMaxE / 32];
+#pragma unroll
+  for (int j = 0; j < kRtMaxE / 32; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[j][i] = 0.f;
+  rt_issue(x, w_router, T, d, E, t0, k0, st0, wave, lane);
+  rt_issue(x, w_router, T, d, E, t0, k0 + min(1, nch - 1) * kRtChunk, st1, wave, lane);
+  const RtLane ln{x, w_router, T, d, E, t0, k0, nch, wave, lane, wave * 32 + l32, lhi, rt_swz(l32), E / 32};
+  int c = 0;
+  for (; c + 3 <= nch; c += 3) {
+    rt_chunk(ln, st0, st2, c, acc);
+    rt_chunk(ln, st1, st0, c + 1, acc);
+    rt_chunk(ln, st2, st1, c + 2, acc);
+  }
+  if (c < nch) {
+    rt_chunk(ln, st0, st2, c, acc);
+    if (c + 1 < nch) rt_chunk(ln, st1, st0, c + 1, acc);
+  }
+  // No direct load may still be writing this block's LDS when it exits.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  // acc[j] element i: token 32 w + 8 (i/4) + 4 lhi + (i%4), expert 32 j + l32.
+#pragma unroll
+  for (int j = 0; j < kRtMaxE / 32; ++j) {
+    if (j >= ntile) continue;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = t0 + wave * 32 + 8 * (i / 4) + 4 * lhi + (i % 4);
+      if (t < T) partial[((size_t)blockIdx.y * T + t) * E + j * 32 + l32] = acc[j][i];
+    }
+  }
+}
+
 namespace {
 
 // Order-preserving map of a float to uint32 (larger float -> larger key).
@@ -211,6 +355,18 @@ __global__ void k_zero_i32(int32_t* p, int n) {
 }
 
 RouteSplit route_split(int T, int d, int E) {
+  if (T >= 1024 && E % 32 == 0 && E <= kRtMaxE && d % kRtChunk == 0) {
+    // LDS-staged kernel: split the reduction until there are >= 256 blocks,
+    // keeping chunks whole 64-wide slices.
+    const int mblocks = (T + kRtM - 1) / kRtM;
+    int ks = (256 + mblocks - 1) / mblocks;
+    ks = ks > 8 ? 8 : ks;
+    ks = ks > d / kRtChunk ? d / kRtChunk : ks;
+    ks = ks < 1 ? 1 : ks;
+    int kchunk = (d / kRtChunk + ks - 1) / ks * kRtChunk;
+    ks = (d + kchunk - 1) / kchunk;
+    return RouteSplit{ks, kchunk, true};
+  }
   const int base = ((E + 63) / 64) * ((T + 15) / 16);
   int ks = 512 / (base > 0 ? base : 1);
   ks = ks < 1 ? 1 : ks;
@@ -220,7 +376,7 @@ RouteSplit route_split(int T, int d, int E) {
   int kchunk = (d + ks - 1) / ks;
   kchunk = (kchunk + 31) / 32 * 32;
   ks = (d + kchunk - 1) / kchunk;
-  return RouteSplit{ks, kchunk};
+  return RouteSplit{ks, kchunk, false};
 }
 
 hipError_t launch_route(int T, int d, int E, int k, const uint16_t* x, const uint16_t* w_router,
@@ -232,8 +388,12 @@ hipError_t launch_route(int T, int d, int E, int k, const uint16_t* x, const uin
   }
   const RouteSplit rs = route_split(T, d, E);
   float* partial = static_cast<float*>(workspace);
-  hipLaunchKernelGGL(k_route_logits, dim3((E + 63) / 64, (T + 15) / 16, rs.ksplit), dim3(256), 0, stream, x,
-                     w_router, T, d, E, rs.kchunk, partial, counts);
+  if (rs.tiled)
+    hipLaunchKernelGGL(k_route_logits_tiled, dim3((T + kRtM - 1) / kRtM, rs.ksplit), dim3(256), 0, stream, x,
+                       w_router, T, d, E, rs.kchunk, partial, counts);
+  else
+    hipLaunchKernelGGL(k_route_logits, dim3((E + 63) / 64, (T + 15) / 16, rs.ksplit), dim3(256), 0, stream, x,
+                       w_router, T, d, E, rs.kchunk, partial, counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const dim3 grid((T + 3) / 4), block(256);

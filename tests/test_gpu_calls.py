@@ -88,6 +88,23 @@ def test_route_edge_cases(device, T, E, k, bias_mode):
         assert np.all(np.any(g_ids == E // 3, axis=1)) and g_cnt[E // 3] == T
 
 
+@pytest.mark.parametrize("T,d,E,k", [
+    (1024, 256, 64, 4),      # LDS-staged router logits, reduction split in four
+    (1100, 192, 32, 2),      # ragged last 128-token block, three splits
+    (2048, 512, 288, 8),     # the model's expert count
+    (8192, 448, 32, 2),      # last reduction split shorter than the others
+])
+def test_route_staged_logits(device, T, d, E, k):
+    # Batches of >= 1024 tokens take the LDS-staged logits kernel.
+    cfg = moegen.custom(0, T=T, d=d, E=E, k=k, seed=3000 + T + d + E)
+    log(f"[route-staged] T={T} d={d} E={E} k={k}")
+    x_h, wr_h, b_h = moegen.x(cfg), moegen.router(cfg), moegen.sel_bias(cfg)
+    g_ids, g_w, g_gap, g_cnt = run_route(cfg, x_h, wr_h, b_h, None)
+    o_ids, o_w, o_gap, _ = oracle.route(x_h, wr_h, b_h, k)
+    same, near = check_routing(g_ids, g_w, g_gap, g_cnt, o_ids, o_w, o_gap, E)
+    log(f"  near-tie tokens: {near}, differing: {int((~same).sum())}")
+
+
 def run_permute(T, E, k, ids_h):
     s = moe.make_shape(T, 64, E, k, 64, 0)
     off = torch.full((E + 1,), -3, dtype=torch.int32, device="cuda")
