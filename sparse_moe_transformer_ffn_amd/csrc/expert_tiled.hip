@@ -6,40 +6,47 @@
 // [Blog] "Step 3.5 Flash: Open Frontier-Level Intelligence with 11B Active
 // Parameters" §3.2.4).
 //
-// Block = 4 waves; item = 128 token rows x 256 weight rows:
+// Block = 8 waves (two per SIMD); item = up to 256 token rows x 256 weight
+// rows of one group:
 //   gate/up: 128 gate rows j0.. and the 128 matching up rows h+j0.. of W_gu;
 //   down:    256 rows n0.. of W_d.
-// Wave (wm, wn) = (wave % 2, wave / 2) owns rows [64 wm, 64 wm + 64) of the
-// M-tile and 128 of the columns: gate/up units [64 wn, 64 wn + 64) of both
-// halves (so SiLU(G) * U pairs sit in the same lane), or down columns
-// [128 wn, 128 wn + 128).  That is 2 x 4 MFMA 32x32x16 tiles, 128 f32
-// accumulators per lane, 0.75 KiB of LDS reads per MFMA.
+// Per 64-wide K chunk the block moves 64 KiB from L2 into LDS for 8.4 MFLOP:
+// the operand traffic per flop is what bounds these kernels (the L2 -> CU
+// path delivers ~16.5 TB/s on this chip), and a 256 x 256 item needs a third
+// less of it than a 128 x 256 one.  A group's last M-tile is a half item when
+// at most 128 rows remain.
 //
-// Work order (grouped.h): M-tiles fastest in bands of up to 4, so the blocks
-// that run side by side on one XCD share a weight slab (one HBM read, the
-// band's other M-tiles hit L2) while the token rows they touch stay within a
-// few MiB of the XCD's 4 MiB L2.  Blocks take items from a per-XCD queue.
+// Wave w = (wm, wn) = (w / 2, w % 2) owns rows [64 wm, 64 wm + 64) of the
+// M-tile and 128 weight rows: gate/up units [64 wn, 64 wn + 64) of both halves
+// (so SiLU(G) * U pairs sit in the same lane), or down columns
+// [128 wn, 128 wn + 128).  That is 2 x 4 MFMA 32x32x16 tiles, 128 f32
+// accumulators per lane, 0.75 KiB of LDS reads per MFMA.  SIMD s runs waves s
+// and s + 4, whose M-slices are s / 2 and s / 2 + 2: in a half item (rows
+// 0..127 only) waves 4..7 skip their multiplies and every SIMD still has one
+// wave multiplying, so a half item costs about half a full one.
+//
+// Work order (grouped.h): M-tiles fastest in bands of up to 4; blocks take
+// items from a per-XCD queue, so the items in flight on an XCD are a window of
+// consecutive items sharing their groups' token rows and weights through L2.
 //
 // Operand staging.  Both operands go from HBM/L2 straight into LDS with the
 // gfx950 direct-to-LDS load (global_load_lds_dwordx4: lane l of a wave writes
-// its 16 bytes at LDS base + 16*l) through a ring of three stages of K chunks
-// (Cfg: 64 wide for gate/up, one block per CU; 32 wide for down, two blocks
-// per CU), with no register staging.  A row of a chunk is kSegs 16-byte
-// segments; segment s of row r is stored at slot s ^ swz(r), so a wave's
-// 16-byte reads of one segment of 16 consecutive rows cover all LDS banks.
-// The direct loads choose their source segment to produce that layout.
+// its 16 bytes at LDS base + 16*l), whole 128-byte rows per 64-wide chunk
+// (half rows cost a third of the L2 throughput), through two stages of
+// A 256x64 + B 256x64 bf16 = 64 KiB each, with no register staging.  Segment s
+// of row r is stored at slot s ^ ((r >> 1) & 7), so a wave's 16-byte reads of
+// one segment of 16 consecutive rows cover all LDS banks.  The direct loads
+// choose their source segment to produce that layout.
 //
-// Software pipeline (pipe_chunk): each 16-wide K step issues its eight
-// MFMAs one by one, and after each one the next step's fragment read from
-// LDS and a share of the direct loads of the chunk two ahead, in a pinned
-// order, so LDS and memory latency hide behind the matrix pipe.  One block
-// barrier per chunk, before its last step, after each thread has waited for
-// its own loads of the next chunk (vmcnt) and its reads of this one
-// (lgkmcnt): a bare s_barrier, no release fence, which would drain the loads
-// in flight.  The three stages are distinct LDS arrays and the chunk loop is
-// unrolled by three so the compiler sees which stage each access uses.  Token
+// Software pipeline (pipe_chunk): chunk c's first K step issues all of chunk
+// c+1's direct loads into the other stage, one after each MFMA; steps 0-2
+// each follow every MFMA with one LDS read of the next step's fragments.
+// After step 3 each thread waits for its loads of chunk c+1, then the block
+// barrier (a bare s_barrier: no release fence, which would drain the loads in
+// flight) makes chunk c+1 visible; reading its first fragments is the only
+// exposed LDS latency per chunk, which the SIMD's other wave covers.  Token
 // rows past the group's end load the group's first row (their results are
-// never stored); every wave multiplies, so items cost the same.
+// never stored).
 //
 // MFMA 32x32x16 operands: lane l supplies row (l % 32) of A / column (l % 32)
 // of B for the 8 reduction elements 8*(l/32) .. +7 of the 16; result element
@@ -54,96 +61,66 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kTileM = 128;
-constexpr int kTileN = 256;                  // weight rows per item
-constexpr int kBand = 4;                     // M-tiles per band of the work order
-// Chunk geometry per phase.  Gate/up (K = d, long items) uses 64-wide chunks:
-// every direct load moves whole 128-byte lines, three 48 KiB stages, one block
-// of four waves per CU.  Down (K = hidden, items a third as long) uses 32-wide
-// chunks: three 24 KiB stages, so two blocks share a CU and each one's
-// barrier waits and item start-up are covered by the other's multiplies.
-template <int PHASE>
-struct Cfg {
-  static constexpr int kChunk = PHASE == 0 ? 64 : 32;          // K elements per stage
-  static constexpr int kBlocksPerCU = 64 / kChunk;
-  static constexpr int kSegs = kChunk / 8;                     // 16-byte segments per row
-  static constexpr int kStageA = kTileM * kChunk;              // bf16 elements
-  static constexpr int kStageB = kTileN * kChunk;
-  static constexpr int kStage = kStageA + kStageB;
-  static constexpr int kSteps = kChunk / 16;                   // MFMA K steps per chunk
-  static constexpr int kRegionRows = 64 / kSegs;               // rows written by one wave-wide direct load
-  static constexpr int kLoadsA = kTileM / kRegionRows / 4;     // per thread per chunk
-  static constexpr int kLoadsB = kTileN / kRegionRows / 4;
-  static constexpr int kLoadsPerChunk = kLoadsA + kLoadsB;
-  // K steps over which a chunk's direct loads are spread: gate/up (one wave
-  // per SIMD) spreads them over the whole chunk to keep the issue slots of
-  // each step light; down (two waves per SIMD, latency-bound) sends them all
-  // in the first step.
-  static constexpr int kLoadSteps = PHASE == 0 ? kSteps : 1;
-  static constexpr int kLoadsPerStep = kLoadsPerChunk / kLoadSteps;
-  // Loads of chunk c+2 issued before the wait that precedes the last step.
-  static constexpr int kLoadsBeforeWait = kLoadSteps < kSteps ? kLoadsPerChunk : (kSteps - 1) * kLoadsPerStep;  // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
-  // 6:4, lgkmcnt 11:8).  kWaitChunk0: vmcnt(kLoadsPerChunk) -- an item's
-  // first chunk landed while its second is in flight; kWaitNextChunk: only
-  // the loads of chunk c+2 issued so far may remain, and lgkmcnt(0)
-  // (pipe_chunk).
-  static constexpr int kWaitChunk0 = 0x0F70 | kLoadsPerChunk;
-  static constexpr int kWaitNextChunk = 0x0070 | kLoadsBeforeWait;
-  // Rows sharing one 256-byte window of the 64 LDS banks.
-  static constexpr int kRowsPerWindow = 256 / (2 * kChunk);
-  static_assert(kSteps % 2 == 0 && kLoadsPerChunk < 16 && kLoadsPerStep * kLoadSteps == kLoadsPerChunk,
-                "pipeline shape, vmcnt field");
-  // Slot of 16-byte segment `seg` of LDS row `row`: the rows of a window get
-  // distinct XOR masks, so a wave's reads of one segment of 16 consecutive
-  // rows cover all banks.
-  __device__ static __forceinline__ int swz(int row) { return (row / kRowsPerWindow) & (kSegs - 1); }
-};
-constexpr int kWaitAll = 0x0F70;  // vmcnt(0)
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kTileM = 256;                       // token rows of a full item
+constexpr int kHalfM = 128;                       // at most this many rows left: a half item
+constexpr int kTileN = 256;                       // weight rows per item
+constexpr int kBand = 4;                          // M-tiles per band of the work order
+constexpr int kChunk = 64;                        // K elements per stage
+constexpr int kSegs = kChunk / 8;                 // 16-byte segments per row
+constexpr int kStageA = kTileM * kChunk;          // bf16 elements
+constexpr int kStageB = kTileN * kChunk;
+constexpr int kStage = kStageA + kStageB;         // 64 KiB
+constexpr int kSteps = kChunk / 16;               // MFMA K steps per chunk
+constexpr int kRegionRows = 64 / kSegs;           // rows written by one wave-wide direct load
+constexpr int kLoadsA = kTileM / kRegionRows / kWaves;  // per thread per chunk
+constexpr int kLoadsB = kTileN / kRegionRows / kWaves;
+constexpr int kLoads = kLoadsA + kLoadsB;         // 8: one after each MFMA of a step
+static_assert(kLoads == 8 && kSteps == 4, "pipeline shape");
 
-// Cache policy of the direct loads: the default for both operands.  Token rows
-// are re-read by every N-tile of their M-tile and weight rows by every M-tile
-// of their band, both through L2 (a non-temporal hint on the weight rows
-// measured slower: it defeats the sharing within a band).
-constexpr int kPolicy = 0;
+// s_waitcnt vmcnt(0) (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4 and lgkmcnt 11:8 not waited on).
+constexpr int kWaitAll = 0x0F70;
+
+constexpr int kPolicy = 0;  // default cache policy for both operands
 
 __device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                  0, 0, 0);
 }
 
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & (kSegs - 1); }
+
 enum Phase { kGateUp = 0, kDown = 1 };
 
+// Row of N-subtile ns (0..3) of wave column wn inside the 256-row B tile.
+// Gate/up: gate rows [64 wn, +64) (ns 0, 1) and up rows [128 + 64 wn, +64)
+// (ns 2, 3); down: columns [128 wn + 32 ns, +32).
 template <int PHASE>
+__device__ __forceinline__ constexpr int b_row0(int wn, int ns) {
+  return PHASE == kGateUp ? (ns / 2) * (kTileN / 2) + wn * 64 + (ns % 2) * 32 : wn * 128 + ns * 32;
+}
+
 struct Pipe {
-  const uint16_t* src[Cfg<PHASE>::kLoadsPerChunk];  // per-thread source of each direct load (chunk 0)
-  int lds_off[Cfg<PHASE>::kLoadsPerChunk];          // wave-uniform LDS element offset inside a stage
+  const uint16_t* src[kLoads];  // per-thread source of each direct load (chunk 0)
+  int lds_off[kLoads];          // wave-uniform LDS element offset inside a stage
 };
 
-template <int PHASE>
-__device__ __forceinline__ void issue_chunk(const Pipe<PHASE>& p, uint16_t* stage, int c) {
-  using C = Cfg<PHASE>;
+__device__ __forceinline__ void issue_chunk(const Pipe& p, uint16_t* stage, int c) {
 #pragma unroll
-  for (int q = 0; q < C::kLoadsPerChunk; ++q)
-    __builtin_amdgcn_global_load_lds(p.src[q] + c * C::kChunk, stage + p.lds_off[q], 16, 0, kPolicy);
+  for (int q = 0; q < kLoads; ++q)
+    __builtin_amdgcn_global_load_lds(p.src[q] + c * kChunk, stage + p.lds_off[q], 16, 0, kPolicy);
 }
 
-// LDS element offsets of this lane's fragment reads inside a stage, per K
-// step s: A row 64 wm + l32 (M-subtile 0; subtile 1 is 32 rows further) and
-// B row b_first + l32 (N-subtile 0; the others at kBDelta rows further), each
-// at the step's swizzled slot.  All rows a lane reads have swz(row) = swz(l32).
-template <int PHASE>
+// LDS element offsets of this lane's fragment reads, per K step s: A row
+// 64 wm + l32 (M-subtile 0; subtile 1 is 32 rows further) and B row
+// b_row0(wn, 0) + l32 (N-subtile 0; subtile ns at b_row0(wn, ns) -
+// b_row0(wn, 0) further), each at the step's swizzled slot.  All rows a lane
+// reads have swz(row) = swz(l32).
 struct ReadMap {
-  int a[Cfg<PHASE>::kSteps], b[Cfg<PHASE>::kSteps];
+  int a[kSteps], b[kSteps];
 };
-
-// Row offsets of the N-subtiles within the 256-row B tile.  Gate/up: wave wn
-// owns units [64 wn, 64 wn + 64) of the gate half (tile rows 0..127) and the
-// same units of the up half (rows 128..255).  Down: columns [128 wn, +128).
-template <int PHASE>
-__device__ __forceinline__ constexpr int b_delta(int ns) {
-  return PHASE == 0 ? (ns < 2 ? 0 : kTileN / 2) + (ns % 2) * 32 : ns * 32;
-}
 
 // Fragments of one 16-wide K step: v[0..1] = A of M-subtiles 0..1,
 // v[2..5] = B of N-subtiles 0..3.
@@ -152,64 +129,80 @@ struct Frags {
 };
 
 template <int PHASE>
-__device__ __forceinline__ u32x4 read_frag(const uint16_t* stage, const ReadMap<PHASE>& m, int s, int q) {
-  constexpr int kc = Cfg<PHASE>::kChunk;
-  const int off = q < 2 ? m.a[s] + q * 32 * kc : m.b[s] + b_delta<PHASE>(q - 2) * kc;
+__device__ __forceinline__ u32x4 read_frag(const uint16_t* stage, const ReadMap& m, int s, int q) {
+  const int off = q < 2 ? m.a[s] + q * 32 * kChunk
+                        : m.b[s] + (b_row0<PHASE>(0, q - 2) - b_row0<PHASE>(0, 0)) * kChunk;
   return *reinterpret_cast<const u32x4*>(&stage[off]);
 }
 
-// One K step: the eight MFMAs of `cur`, each followed by one of the six LDS
-// reads of the next step's fragments (step `s` of `stage`, into `nxt`) and by
-// its share of direct loads q0 .. q0+nq-1 of chunk `cload` into `ahead`.
-// The order is pinned (sched_barrier): while an MFMA occupies the matrix pipe
-// the wave issues the next read and loads.
-template <int PHASE>
-__device__ __forceinline__ void mma_step(const Frags& cur, Frags& nxt, const uint16_t* stage,
-                                         const ReadMap<PHASE>& m, int s, const Pipe<PHASE>& p, uint16_t* ahead,
-                                         int cload, int q0, int nq, f32x16 (&acc)[2][4]) {
-  using C = Cfg<PHASE>;
+// One K step: the eight MFMAs of `cur` (if MUL), after MFMA i the LDS read i
+// of the next step's fragments (step `s` of `stage` into `nxt`, i < 6, if
+// READ) and, with LOADS, direct load i of chunk `cload` into `other`.  The
+// order is pinned (sched_barrier).
+template <int PHASE, bool MUL, bool READ, bool LOADS>
+__device__ __forceinline__ void mma_step(const Frags& cur, Frags& nxt, const uint16_t* stage, const ReadMap& m,
+                                         int s, const Pipe& p, uint16_t* other, int cload, f32x16 (&acc)[2][4]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    acc[i / 4][i % 4] = mfma_32x32x16(cur.v[i / 4], cur.v[2 + i % 4], acc[i / 4][i % 4]);
-    __builtin_amdgcn_sched_barrier(0);
-    if (i < 6) {
-      nxt.v[i] = read_frag<PHASE>(stage, m, s, i);
+    if (MUL) {
+      acc[i / 4][i % 4] = mfma_32x32x16(cur.v[i / 4], cur.v[2 + i % 4], acc[i / 4][i % 4]);
       __builtin_amdgcn_sched_barrier(0);
+      if (READ && i < 6) {
+        nxt.v[i] = read_frag<PHASE>(stage, m, s, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-#pragma unroll
-    for (int q = q0 + i * nq / 8; q < q0 + (i + 1) * nq / 8; ++q) {
-      __builtin_amdgcn_global_load_lds(p.src[q] + cload * C::kChunk, ahead + p.lds_off[q], 16, 0, kPolicy);
+    if (LOADS) {
+      __builtin_amdgcn_global_load_lds(p.src[i] + cload * kChunk, other + p.lds_off[i], 16, 0, kPolicy);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
-// Chunk c of an item, whose step-0 fragments are already in fr[0] (read from
-// `cur`).  The first kLoadSteps steps issue chunk c+2's direct loads into
-// `ahead` (the stage of chunk c-1, which every wave finished reading before
-// the previous barrier).  Steps 0 .. S-2 multiply and read steps 1 .. S-1 of
-// `cur`.  Before the last step: wait until this thread's loads of chunk c+1
-// have landed (only chunk c+2's may remain) and its reads of chunk c are
-// done, then the block barrier -- chunk c+1 is now visible to all and nobody
-// reads chunk c any more.  The last step multiplies and reads step 0 of chunk
-// c+1 from `next` into fr[0].  Past the last chunk the loads repeat the last
-// chunk (an L2 hit into a stage nobody reads) and the final step-0 reads
-// fetch unused data, so every chunk issues and waits the same way.
-template <int PHASE>
-__device__ __forceinline__ void pipe_chunk(const Pipe<PHASE>& p, const uint16_t* cur, const uint16_t* next,
-                                           uint16_t* ahead, int c, int nch, const ReadMap<PHASE>& m,
-                                           Frags (&fr)[2], f32x16 (&acc)[2][4]) {
-  using C = Cfg<PHASE>;
-  const int cl = min(c + 2, nch - 1);
-#pragma unroll
-  for (int st = 0; st + 1 < C::kSteps; ++st)
-    mma_step<PHASE>(fr[st & 1], fr[(st + 1) & 1], cur, m, st + 1, p, ahead, cl, st * C::kLoadsPerStep,
-                    st < C::kLoadSteps ? C::kLoadsPerStep : 0, acc);
-  __builtin_amdgcn_s_waitcnt(C::kWaitNextChunk);
+// Chunk c of an item (in `cur`), whose step-0 fragments are already in fr[0].
+// Step 0 issues chunk c+1's direct loads into `other` (the stage of chunk
+// c-1: every wave finished reading it before the previous barrier, its reads
+// having been consumed by that chunk's MFMAs).  Steps 0-2 read steps 1-3 of
+// `cur`; step 3 only multiplies.  Then each thread waits for its loads of
+// chunk c+1 and the block barrier makes them visible; its first fragments
+// are read last.  Past the last chunk the loads repeat it (an L2 hit into a
+// stage nobody reads) and the final reads fetch unused data, so every chunk
+// issues and waits the same way.  Waves without rows in the item (MUL =
+// false) only load and wait.
+template <int PHASE, bool MUL>
+__device__ __forceinline__ void pipe_chunk(const Pipe& p, const uint16_t* cur, uint16_t* other, int c, int nch,
+                                           const ReadMap& m, Frags (&fr)[2], f32x16 (&acc)[2][4]) {
+  const int cl = min(c + 1, nch - 1);
+  mma_step<PHASE, MUL, true, true>(fr[0], fr[1], cur, m, 1, p, other, cl, acc);
+  mma_step<PHASE, MUL, true, false>(fr[1], fr[0], cur, m, 2, p, other, cl, acc);
+  mma_step<PHASE, MUL, true, false>(fr[0], fr[1], cur, m, 3, p, other, cl, acc);
+  mma_step<PHASE, MUL, false, false>(fr[1], fr[0], cur, m, 0, p, other, cl, acc);
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
   __builtin_amdgcn_s_barrier();
-  constexpr int last = C::kSteps - 1;
-  mma_step<PHASE>(fr[1], fr[0], next, m, 0, p, ahead, cl, last * C::kLoadsPerStep,
-                  last < C::kLoadSteps ? C::kLoadsPerStep : 0, acc);
+  if (MUL) {
+#pragma unroll
+    for (int q = 0; q < 6; ++q) fr[0].v[q] = read_frag<PHASE>(other, m, 0, q);
+  }
+}
+
+// The K loop of one item over the two stages (unrolled by two).
+template <int PHASE, bool MUL>
+__device__ __forceinline__ void run_item(const Pipe& p, uint16_t* stage0, uint16_t* stage1, int nch,
+                                         const ReadMap& m, f32x16 (&acc)[2][4]) {
+  issue_chunk(p, stage0, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
+  __builtin_amdgcn_s_barrier();
+  Frags fr[2];
+  if (MUL) {
+#pragma unroll
+    for (int q = 0; q < 6; ++q) fr[0].v[q] = read_frag<PHASE>(stage0, m, 0, q);
+  }
+  int c = 0;
+  for (; c + 2 <= nch; c += 2) {
+    pipe_chunk<PHASE, MUL>(p, stage0, stage1, c, nch, m, fr, acc);
+    pipe_chunk<PHASE, MUL>(p, stage1, stage0, c + 1, nch, m, fr, acc);
+  }
+  if (c < nch) pipe_chunk<PHASE, MUL>(p, stage0, stage1, c, nch, m, fr, acc);
 }
 
 }  // namespace
@@ -219,39 +212,37 @@ __device__ __forceinline__ void pipe_chunk(const Pipe<PHASE>& p, const uint16_t*
 // PHASE kDown:   A = hid rows, B rows = W_d rows, K = H,
 //                out -> y_perm (bf16) / y_shared (f32), row stride d.
 template <int PHASE>
-__global__ __launch_bounds__(kThreads, Cfg<PHASE>::kBlocksPerCU) void k_expert_tiled(const uint16_t* __restrict__ a_src,
-                                                           const uint16_t* __restrict__ a_src_shared, Groups gs, int d,
-                                                           int h, int hs, const uint16_t* __restrict__ w,
-                                                           const uint16_t* __restrict__ ws,
-                                                           uint16_t* __restrict__ out, void* __restrict__ out_shared,
-                                                           int* __restrict__ queue) {
-  using C = Cfg<PHASE>;
+__global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __restrict__ a_src,
+                                                              const uint16_t* __restrict__ a_src_shared, Groups gs,
+                                                              int d, int h, int hs, const uint16_t* __restrict__ w,
+                                                              const uint16_t* __restrict__ ws,
+                                                              uint16_t* __restrict__ out,
+                                                              void* __restrict__ out_shared,
+                                                              int* __restrict__ queue) {
   __shared__ int ip[kMaxGroups + 1];
   __shared__ int next_item;
-  __shared__ int wsum[kThreads / kWave];
-  __shared__ __attribute__((aligned(16))) uint16_t stage0[C::kStage];
-  __shared__ __attribute__((aligned(16))) uint16_t stage1[C::kStage];
-  __shared__ __attribute__((aligned(16))) uint16_t stage2[C::kStage];
+  __shared__ int wsum[kWaves];
+  __shared__ __attribute__((aligned(16))) uint16_t stage0[kStage];
+  __shared__ __attribute__((aligned(16))) uint16_t stage1[kStage];
   const int nt_routed = PHASE == kGateUp ? h / (kTileN / 2) : d / kTileN;
   const int nt_shared = PHASE == kGateUp ? hs / (kTileN / 2) : d / kTileN;
   const int items = item_prefix<kTileM, kThreads>(ip, wsum, gs, nt_routed, nt_shared);
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform per wave
-  const int wm = wave % 2, wn = wave / 2;
+  const int wm = wave / 2, wn = wave % 2;
   const int l32 = lane & 31, lhi = lane >> 5;
-  const int f = C::swz(l32);
-  ReadMap<PHASE> m;
+  const int f = swz(l32);
+  ReadMap m;
 #pragma unroll
-  for (int st = 0; st < C::kSteps; ++st) {
+  for (int st = 0; st < kSteps; ++st) {
     const int slot = ((2 * st + lhi) ^ f) * 8;
-    m.a[st] = (wm * 64 + l32) * C::kChunk + slot;
-    m.b[st] = C::kStageA + ((PHASE == kGateUp ? wn * 64 : wn * 128) + l32) * C::kChunk + slot;
+    m.a[st] = (wm * 64 + l32) * kChunk + slot;
+    m.b[st] = kStageA + (b_row0<PHASE>(wn, 0) + l32) * kChunk + slot;
   }
 
   // Dynamic work queue per XCD: XCD x owns items [lo, hi) and its blocks take
-  // them in order, one atomic per item, so the items in flight on an XCD are
-  // always a contiguous window of the work order (the L2 sharing above relies
-  // on it).  Every block exits once its XCD's range is exhausted.
+  // them in order, one atomic per item.  Every block exits once its XCD's
+  // range is exhausted.
   const int xcd = blockIdx.x % kNumXcd;
   const int lo = (int)((long long)items * xcd / kNumXcd);
   const int hi = (int)((long long)items * (xcd + 1) / kNumXcd);
@@ -263,7 +254,7 @@ __global__ __launch_bounds__(kThreads, Cfg<PHASE>::kBlocksPerCU) void k_expert_t
     const Item it = decode_item<kBand>(ip, gs, kTileM, nt_routed, nt_shared, wi);
     const int H = it.shared ? hs : h;
     const int K = PHASE == kGateUp ? d : H;
-    const int nch = K / C::kChunk;
+    const int nch = K / kChunk;
     const uint16_t* wmat;
     int b_lo, b_hi;  // weight-matrix row of tile row r: b_lo + r (r < 128), b_hi + r (r >= 128)
     if (PHASE == kGateUp) {
@@ -275,38 +266,38 @@ __global__ __launch_bounds__(kThreads, Cfg<PHASE>::kBlocksPerCU) void k_expert_t
       b_lo = it.nt * kTileN;
       b_hi = it.nt * kTileN;
     }
-    // Direct-load plan.  Load q of wave `wave` fills one 1 KiB region
-    // (kRegionRows rows x kSegs slots) of the A (q < kLoadsA) or B part of a
-    // stage: region q' * 4 + wave, lane l -> row kRegionRows * region +
-    // l / kSegs, slot l % kSegs = segment ^ swz(row).
-    Pipe<PHASE> p;
+    // Direct-load plan.  Load q of wave `wave` fills one 1 KiB region (8 rows
+    // x 8 slots) of the A (q < kLoadsA) or B part of a stage: region
+    // q' * kWaves + wave, lane l -> row 8 * region + l / 8, slot l % 8 =
+    // segment ^ swz(row).
+    Pipe p;
     const uint16_t* abase = it.shared ? a_src_shared : a_src;
     const int astride = PHASE == kGateUp ? d : H;
-    size_t arow[C::kLoadsA];
+    size_t arow[kLoadsA];
 #pragma unroll
-    for (int q = 0; q < C::kLoadsA; ++q) {
-      const int r = it.m0 + (q * 4 + wave) * C::kRegionRows + lane / C::kSegs;
+    for (int q = 0; q < kLoadsA; ++q) {
+      const int r = it.m0 + (q * kWaves + wave) * kRegionRows + lane / kSegs;
       arow[q] = (size_t)(it.row0 + (r < it.nrows ? r : 0));
     }
     if (PHASE == kGateUp) {
       if (it.shared) {
 #pragma unroll
-        for (int q = 0; q < C::kLoadsA; ++q) arow[q] -= (size_t)it.row0;
+        for (int q = 0; q < kLoadsA; ++q) arow[q] -= (size_t)it.row0;
       } else {
-        int tok[C::kLoadsA];
+        int tok[kLoadsA];
 #pragma unroll
-        for (int q = 0; q < C::kLoadsA; ++q) tok[q] = gs.perm[arow[q]];
+        for (int q = 0; q < kLoadsA; ++q) tok[q] = gs.perm[arow[q]];
 #pragma unroll
-        for (int q = 0; q < C::kLoadsA; ++q) arow[q] = (size_t)(tok[q] / gs.k);
+        for (int q = 0; q < kLoadsA; ++q) arow[q] = (size_t)(tok[q] / gs.k);
       }
     }
 #pragma unroll
-    for (int q = 0; q < C::kLoadsPerChunk; ++q) {
-      const bool is_a = q < C::kLoadsA;
-      const int region = (is_a ? q : q - C::kLoadsA) * 4 + wave;
-      const int row = region * C::kRegionRows + lane / C::kSegs;
-      const int seg = (lane % C::kSegs) ^ C::swz(row);
-      p.lds_off[q] = (is_a ? 0 : C::kStageA) + region * C::kRegionRows * C::kChunk;
+    for (int q = 0; q < kLoads; ++q) {
+      const bool is_a = q < kLoadsA;
+      const int region = (is_a ? q : q - kLoadsA) * kWaves + wave;
+      const int row = region * kRegionRows + lane / kSegs;
+      const int seg = (lane % kSegs) ^ swz(row);
+      p.lds_off[q] = (is_a ? 0 : kStageA) + region * kRegionRows * kChunk;
       if (is_a) {
         p.src[q] = abase + arow[q] * astride + seg * 8;
       } else {
@@ -314,9 +305,10 @@ __global__ __launch_bounds__(kThreads, Cfg<PHASE>::kBlocksPerCU) void k_expert_t
         p.src[q] = wmat + (size_t)grow * K + seg * 8;
       }
     }
-    // Every wave multiplies, also on rows past the group's end: items then
-    // cost the same, so the blocks sharing operands through L2 stay in step.
     const int wave_row0 = it.m0 + wm * 64;
+    // A wave multiplies iff some of its 64 rows exist; in a half item that
+    // is waves 0..3 only (uniform per wave).
+    const bool mul = wave_row0 < it.nrows;
 
     f32x16 acc[2][4];
 #pragma unroll
@@ -329,23 +321,9 @@ __global__ __launch_bounds__(kThreads, Cfg<PHASE>::kBlocksPerCU) void k_expert_t
     // Every wave is past the previous item's reads and stores.
     __builtin_amdgcn_s_waitcnt(kWaitAll);
     __builtin_amdgcn_s_barrier();
-    issue_chunk<PHASE>(p, stage0, 0);
-    issue_chunk<PHASE>(p, stage1, min(1, nch - 1));
-    __builtin_amdgcn_s_waitcnt(C::kWaitChunk0);
-    __builtin_amdgcn_s_barrier();
-    Frags fr[2];
-#pragma unroll
-    for (int q = 0; q < 6; ++q) fr[0].v[q] = read_frag<PHASE>(stage0, m, 0, q);
-    int c = 0;
-    for (; c + 3 <= nch; c += 3) {
-      pipe_chunk<PHASE>(p, stage0, stage1, stage2, c, nch, m, fr, acc);
-      pipe_chunk<PHASE>(p, stage1, stage2, stage0, c + 1, nch, m, fr, acc);
-      pipe_chunk<PHASE>(p, stage2, stage0, stage1, c + 2, nch, m, fr, acc);
-    }
-    if (c < nch) {
-      pipe_chunk<PHASE>(p, stage0, stage1, stage2, c, nch, m, fr, acc);
-      if (c + 1 < nch) pipe_chunk<PHASE>(p, stage1, stage2, stage0, c + 1, nch, m, fr, acc);
-    }
+    if (mul) run_item<PHASE, true>(p, stage0, stage1, nch, m, acc);
+    else run_item<PHASE, false>(p, stage0, stage1, nch, m, acc);
+    if (!mul) continue;
 
     // Epilogue.  Element i of acc[ms][ns] is row 8*(i/4) + 4*lhi + (i%4) of
     // M-subtile ms, column l32 of N-subtile ns.
@@ -374,6 +352,8 @@ __global__ __launch_bounds__(kThreads, Cfg<PHASE>::kBlocksPerCU) void k_expert_t
       }
     }
   }
+  // No direct load may still be writing this block's LDS when it exits.
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
 }
 
 namespace {
