@@ -14,7 +14,6 @@ namespace {
 constexpr int kMaxTokens = 1 << 20;
 constexpr int kMaxDim = 65536;
 constexpr int kMaxExperts = 1024;
-constexpr int kMaxTopK = 16;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -26,7 +25,7 @@ moe_status check_shape(const moe_shape* s) {
   if (s->num_tokens < 0 || s->num_tokens > kMaxTokens) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (s->d_model < 64 || s->d_model > kMaxDim || s->d_model % 64) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (s->num_experts < 1 || s->num_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED_SHAPE;
-  if (s->top_k < 1 || s->top_k > kMaxTopK || s->top_k > s->num_experts) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (s->top_k < 1 || s->top_k > moe::kMaxTopK || s->top_k > s->num_experts) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (s->d_expert < 64 || s->d_expert > kMaxDim || s->d_expert % 64) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (s->d_shared != 0 && (s->d_shared < 64 || s->d_shared > kMaxDim || s->d_shared % 64))
     return MOE_ERR_UNSUPPORTED_SHAPE;

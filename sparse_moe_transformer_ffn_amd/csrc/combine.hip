@@ -28,14 +28,16 @@ __device__ __forceinline__ u32x4 pack8(const float* f) {
 }  // namespace
 
 // One block per token; each thread owns 8 consecutive columns per step.  The
-// k contributions are summed in slot order (ascending expert id), in f32.
+// k contributions are summed in slot order (ascending expert id), in f32;
+// the k rows' loads of a step are all issued before the sums, so a step waits
+// on one memory latency rather than k.
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y_perm,
                                                  const int32_t* __restrict__ pair_pos,
                                                  const float* __restrict__ topk_weights,
                                                  const float* __restrict__ y_shared, float routed_scale, int d,
                                                  int k, uint16_t* __restrict__ y) {
-  __shared__ int pos[16];
-  __shared__ float wt[16];
+  __shared__ int pos[kMaxTopK];
+  __shared__ float wt[kMaxTopK];
   const int t = blockIdx.x, tid = threadIdx.x;
   if (tid < k) {
     pos[tid] = pair_pos[(size_t)t * k + tid];
@@ -43,17 +45,28 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y_
   }
   __syncthreads();
   for (int c = tid * 8; c < d; c += 256 * 8) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      float v[8];
-      unpack8(load16(y_perm + (size_t)pos[j] * d + c), v);
+    u32x4 rows[kMaxTopK];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = fmaf(wt[j], v[q], acc[q]);
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (j < k) rows[j] = load16(y_perm + (size_t)pos[j] * d + c);
+    float4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    if (y_shared) {
+      const float4* s = reinterpret_cast<const float4*>(y_shared + (size_t)t * d + c);
+      s0 = s[0];
+      s1 = s[1];
+    }
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j < k) {
+        float v[8];
+        unpack8(rows[j], v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = fmaf(wt[j], v[q], acc[q]);
+      }
     }
     float o[8];
     if (y_shared) {
-      const float4* s = reinterpret_cast<const float4*>(y_shared + (size_t)t * d + c);
-      const float4 s0 = s[0], s1 = s[1];
       const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
       for (int q = 0; q < 8; ++q) o[q] = fmaf(routed_scale, acc[q], sv[q]);

@@ -7,6 +7,8 @@
 
 namespace moe {
 
+constexpr int kMaxTopK = 16;  // largest top_k the C ABI accepts
+
 // How the router's logits are computed: the split of the d-long reduction
 // into ksplit chunks of kchunk, and whether the LDS-staged kernel (large
 // batches) is used.

@@ -121,6 +121,8 @@ def run_permute(T, E, k, ids_h):
     (64, 16, 2, "random"), (1, 16, 2, "random"), (0, 16, 2, "random"), (65, 288, 8, "random"),
     (1000, 288, 8, "random"), (8192, 288, 8, "random"), (333, 1024, 16, "random"), (257, 288, 8, "one_expert"),
     (129, 16, 16, "random"), (200, 288, 8, "two_hot"),
+    # one-block path up to 16 chunks of 64 tokens and 8192 (chunk, expert) slots; three kernels beyond
+    (1024, 1024, 4, "random"), (1025, 16, 2, "random"),
 ])
 def test_permute_parity(device, T, E, k, pattern):
     log(f"[permute] T={T} E={E} k={k} {pattern}")
