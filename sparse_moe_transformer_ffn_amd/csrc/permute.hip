@@ -45,14 +45,24 @@ __global__ __launch_bounds__(256) void k_perm_count(const int32_t* __restrict__ 
     chunk_cnt[(size_t)blockIdx.x * E + e] = __popcll(mask[e]);
 }
 
-// One block of 1024 threads; thread e owns expert e.
+// One block of 1024 threads; thread e owns expert e.  Its column of chunk
+// counts is read kScanBatch chunks at a time (loads of a batch in flight
+// together), summed, then rewritten as running bases.
+constexpr int kScanBatch = 16;
+
 __global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ chunk_cnt, int nchunks, int E,
                                                     int32_t* __restrict__ offsets) {
   __shared__ int buf[2][1024];
   const int e = threadIdx.x;
   int total = 0;
   if (e < E)
-    for (int c = 0; c < nchunks; ++c) total += chunk_cnt[(size_t)c * E + e];
+    for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) v[i] = c0 + i < nchunks ? chunk_cnt[(size_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) total += v[i];
+    }
   // Inclusive Hillis-Steele scan over the 1024 expert totals.
   int cur = 0;
   buf[cur][e] = total;
@@ -67,10 +77,15 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ chunk_
   if (e < E) {
     offsets[e] = excl;
     int run = excl;
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = chunk_cnt[(size_t)c * E + e];
-      chunk_cnt[(size_t)c * E + e] = run;
-      run += v;
+    for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) v[i] = c0 + i < nchunks ? chunk_cnt[(size_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) {
+        if (c0 + i < nchunks) chunk_cnt[(size_t)(c0 + i) * E + e] = run;
+        run += v[i];
+      }
     }
     if (e == E - 1) offsets[E] = excl + total;
   }

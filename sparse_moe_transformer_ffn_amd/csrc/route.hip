@@ -217,6 +217,20 @@ __device__ __forceinline__ int count_at_least(const uint32_t (&key)[EPL], uint32
 }
 
 // Largest tau with at least `need` keys >= tau: the need-th largest key.
+// Largest key strictly below tau over the wave (0 if none).
+template <int EPL>
+__device__ __forceinline__ uint32_t max_below(const uint32_t (&key)[EPL], uint32_t tau) {
+  uint32_t m = 0u;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) m = (key[j] < tau && key[j] > m) ? key[j] : m;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)m, off, kWave);
+    m = o > m ? o : m;
+  }
+  return m;
+}
+
 template <int EPL>
 __device__ __forceinline__ uint32_t kth_largest(const uint32_t (&key)[EPL], int need) {
   uint32_t tau = 0u;
@@ -229,17 +243,17 @@ __device__ __forceinline__ uint32_t kth_largest(const uint32_t (&key)[EPL], int 
 
 }  // namespace
 
-// Per-token selection.  One wave per token; lane l owns experts l, l+64, ...
-// (EPL = experts per lane, E <= 64*EPL).  The k-th largest biased score is
-// found exactly by a 32-step radix search on order-preserving keys, counting
-// with wave ballots (no cross-lane data movement); the chosen set is every
-// expert above it plus, among those equal to it, the lowest indices.  A block
-// of four waves handles four tokens and aggregates the expert histogram in LDS
-// before one global atomic add per touched expert (integer atomics:
-// order-independent).
+// Per-token selection.  A wave handles tpw consecutive tokens, one at a time;
+// lane l owns experts l, l+64, ... (EPL = experts per lane, E <= 64*EPL).
+// The k-th largest biased score is found exactly by a 32-step radix search on
+// order-preserving keys, counting with wave ballots (no cross-lane data
+// movement); the chosen set is every expert above it plus, among those equal
+// to it, the lowest indices.  A block of four waves aggregates the expert
+// histogram of its 4 * tpw tokens in LDS before one global atomic add per
+// touched expert (integer atomics: order-independent).
 template <int EPL>
 __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ partial, int ksplit, int T, int E,
-                                                      int k, const float* __restrict__ sel_bias,
+                                                      int k, int tpw, const float* __restrict__ sel_bias,
                                                       const float* __restrict__ logit_bias,
                                                       int32_t* __restrict__ topk_ids,
                                                       float* __restrict__ topk_weights, float* __restrict__ topk_gap,
@@ -250,8 +264,9 @@ __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ 
   for (int e = tid; e < E; e += 256) hist[e] = 0;
   __syncthreads();
   const int wave = tid / kWave, lane = tid % kWave;
-  const int t = blockIdx.x * 4 + wave;
-  if (t < T) {  // wave-uniform; no block barrier inside
+  for (int tw = 0; tw < tpw; ++tw) {  // wave-uniform; no block barrier inside
+    const int t = (blockIdx.x * 4 + wave) * tpw + tw;
+    if (t >= T) break;
     // Logit = sum of the split-K partials in chunk order; loads are issued
     // four chunks at a time so their latencies overlap.
     float z[EPL];
@@ -311,10 +326,11 @@ __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ 
       }
       chosen[j] = m;
     }
-    // Gap to the (k+1)-th largest: zero if a tied expert was left out.
+    // Gap to the (k+1)-th largest key: tau again if at least k+1 keys reach
+    // tau (a tie; gap zero), else the largest key below tau.
     float gap = __builtin_huge_valf();
     if (k < E) {
-      const uint32_t tau2 = kth_largest<EPL>(key, k + 1);
+      const uint32_t tau2 = count_at_least<EPL>(key, tau) > k ? tau : max_below<EPL>(key, tau);
       gap = key_value(tau) - key_value(tau2);
     }
     // Rank of each chosen expert in ascending expert order (j major, then
@@ -343,6 +359,7 @@ __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ 
       before += __popcll(chosen[j]);
     }
     if (lane == 0 && topk_gap) topk_gap[t] = gap;
+    __builtin_amdgcn_wave_barrier();  // chosen_s is reused by the next token
   }
   __syncthreads();
   for (int e = tid; e < E; e += 256)
@@ -396,10 +413,14 @@ hipError_t launch_route(int T, int d, int E, int k, const uint16_t* x, const uin
                        w_router, T, d, E, rs.kchunk, partial, counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const dim3 grid((T + 3) / 4), block(256);
+  // Tokens per wave: one for small batches (latency), four for large ones,
+  // so each block's expert histogram covers 16 tokens and the global count
+  // atomics drop fourfold.
+  const int tpw = T >= 2048 ? 4 : 1;
+  const dim3 grid((T + 4 * tpw - 1) / (4 * tpw)), block(256);
   const int epl = (E + 63) / 64;
 #define MOE_SELECT(N)                                                                                             \
-  hipLaunchKernelGGL(k_route_select<N>, grid, block, 0, stream, partial, rs.ksplit, T, E, k, sel_bias, logit_bias, \
+  hipLaunchKernelGGL(k_route_select<N>, grid, block, 0, stream, partial, rs.ksplit, T, E, k, tpw, sel_bias, logit_bias, \
                      topk_ids, topk_weights, topk_gap, counts)
   if (epl <= 1) MOE_SELECT(1);
   else if (epl <= 2) MOE_SELECT(2);
