@@ -13,17 +13,18 @@
 // Per 64-wide K chunk the block moves 64 KiB from L2 into LDS for 8.4 MFLOP:
 // the operand traffic per flop is what bounds these kernels (the L2 -> CU
 // path delivers ~16.5 TB/s on this chip), and a 256 x 256 item needs a third
-// less of it than a 128 x 256 one.  A group's last M-tile is a half item when
-// at most 128 rows remain.
+// less of it than a 128 x 256 one.  A group's last M-tile may hold fewer
+// rows: it loads and multiplies only its 64-row slices, so its cost follows
+// its rows.
 //
 // Wave w = (wm, wn) = (w / 2, w % 2) owns rows [64 wm, 64 wm + 64) of the
 // M-tile and 128 weight rows: gate/up units [64 wn, 64 wn + 64) of both halves
 // (so SiLU(G) * U pairs sit in the same lane), or down columns
 // [128 wn, 128 wn + 128).  That is 2 x 4 MFMA 32x32x16 tiles, 128 f32
 // accumulators per lane, 0.75 KiB of LDS reads per MFMA.  SIMD s runs waves s
-// and s + 4, whose M-slices are s / 2 and s / 2 + 2: in a half item (rows
-// 0..127 only) waves 4..7 skip their multiplies and every SIMD still has one
-// wave multiplying, so a half item costs about half a full one.
+// and s + 4, whose M-slices are s / 2 and s / 2 + 2: in an item of at most
+// 128 rows waves 4..7 skip their multiplies and every SIMD still has one wave
+// multiplying.
 //
 // Work order (grouped.h): M-tiles fastest in bands of up to 4; blocks take
 // items from a per-XCD queue, so the items in flight on an XCD are a window of
@@ -64,7 +65,6 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kTileM = 256;                       // token rows of a full item
-constexpr int kHalfM = 128;                       // at most this many rows left: a half item
 constexpr int kTileN = 256;                       // weight rows per item
 constexpr int kBand = 4;                          // M-tiles per band of the work order
 constexpr int kChunk = 64;                        // K elements per stage
@@ -102,15 +102,26 @@ __device__ __forceinline__ constexpr int b_row0(int wn, int ns) {
   return PHASE == kGateUp ? (ns / 2) * (kTileN / 2) + wn * 64 + (ns % 2) * 32 : wn * 128 + ns * 32;
 }
 
+// Direct loads q < kLoadsA fill A slice q (token rows 64q .. 64q+63), the
+// rest the B tile.  An item with fewer than 256 rows loads only its NA
+// slices (a template parameter of its K loop, so full items run branch-free
+// code): the L2 -> CU operand traffic, which bounds these kernels, then
+// shrinks with the item.
 struct Pipe {
   const uint16_t* src[kLoads];  // per-thread source of each direct load (chunk 0)
   int lds_off[kLoads];          // wave-uniform LDS element offset inside a stage
 };
 
+template <int NA>
+__device__ __forceinline__ constexpr bool load_used(int q) {
+  return q >= kLoadsA || q < NA;
+}
+
+template <int NA>
 __device__ __forceinline__ void issue_chunk(const Pipe& p, uint16_t* stage, int c) {
 #pragma unroll
   for (int q = 0; q < kLoads; ++q)
-    __builtin_amdgcn_global_load_lds(p.src[q] + c * kChunk, stage + p.lds_off[q], 16, 0, kPolicy);
+    if (load_used<NA>(q)) __builtin_amdgcn_global_load_lds(p.src[q] + c * kChunk, stage + p.lds_off[q], 16, 0, kPolicy);
 }
 
 // LDS element offsets of this lane's fragment reads, per K step s: A row
@@ -139,7 +150,7 @@ __device__ __forceinline__ u32x4 read_frag(const uint16_t* stage, const ReadMap&
 // of the next step's fragments (step `s` of `stage` into `nxt`, i < 6, if
 // READ) and, with LOADS, direct load i of chunk `cload` into `other`.  The
 // order is pinned (sched_barrier).
-template <int PHASE, bool MUL, bool READ, bool LOADS>
+template <int PHASE, int NA, bool MUL, bool READ, bool LOADS>
 __device__ __forceinline__ void mma_step(const Frags& cur, Frags& nxt, const uint16_t* stage, const ReadMap& m,
                                          int s, const Pipe& p, uint16_t* other, int cload, f32x16 (&acc)[2][4]) {
 #pragma unroll
@@ -152,7 +163,7 @@ __device__ __forceinline__ void mma_step(const Frags& cur, Frags& nxt, const uin
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (LOADS) {
+    if (LOADS && load_used<NA>(i)) {
       __builtin_amdgcn_global_load_lds(p.src[i] + cload * kChunk, other + p.lds_off[i], 16, 0, kPolicy);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -169,14 +180,14 @@ __device__ __forceinline__ void mma_step(const Frags& cur, Frags& nxt, const uin
 // stage nobody reads) and the final reads fetch unused data, so every chunk
 // issues and waits the same way.  Waves without rows in the item (MUL =
 // false) only load and wait.
-template <int PHASE, bool MUL>
+template <int PHASE, int NA, bool MUL>
 __device__ __forceinline__ void pipe_chunk(const Pipe& p, const uint16_t* cur, uint16_t* other, int c, int nch,
                                            const ReadMap& m, Frags (&fr)[2], f32x16 (&acc)[2][4]) {
   const int cl = min(c + 1, nch - 1);
-  mma_step<PHASE, MUL, true, true>(fr[0], fr[1], cur, m, 1, p, other, cl, acc);
-  mma_step<PHASE, MUL, true, false>(fr[1], fr[0], cur, m, 2, p, other, cl, acc);
-  mma_step<PHASE, MUL, true, false>(fr[0], fr[1], cur, m, 3, p, other, cl, acc);
-  mma_step<PHASE, MUL, false, false>(fr[1], fr[0], cur, m, 0, p, other, cl, acc);
+  mma_step<PHASE, NA, MUL, true, true>(fr[0], fr[1], cur, m, 1, p, other, cl, acc);
+  mma_step<PHASE, NA, MUL, true, false>(fr[1], fr[0], cur, m, 2, p, other, cl, acc);
+  mma_step<PHASE, NA, MUL, true, false>(fr[0], fr[1], cur, m, 3, p, other, cl, acc);
+  mma_step<PHASE, NA, MUL, false, false>(fr[1], fr[0], cur, m, 0, p, other, cl, acc);
   __builtin_amdgcn_s_waitcnt(kWaitAll);
   __builtin_amdgcn_s_barrier();
   if (MUL) {
@@ -186,10 +197,10 @@ __device__ __forceinline__ void pipe_chunk(const Pipe& p, const uint16_t* cur, u
 }
 
 // The K loop of one item over the two stages (unrolled by two).
-template <int PHASE, bool MUL>
+template <int PHASE, int NA, bool MUL>
 __device__ __forceinline__ void run_item(const Pipe& p, uint16_t* stage0, uint16_t* stage1, int nch,
                                          const ReadMap& m, f32x16 (&acc)[2][4]) {
-  issue_chunk(p, stage0, 0);
+  issue_chunk<NA>(p, stage0, 0);
   __builtin_amdgcn_s_waitcnt(kWaitAll);
   __builtin_amdgcn_s_barrier();
   Frags fr[2];
@@ -199,10 +210,10 @@ __device__ __forceinline__ void run_item(const Pipe& p, uint16_t* stage0, uint16
   }
   int c = 0;
   for (; c + 2 <= nch; c += 2) {
-    pipe_chunk<PHASE, MUL>(p, stage0, stage1, c, nch, m, fr, acc);
-    pipe_chunk<PHASE, MUL>(p, stage1, stage0, c + 1, nch, m, fr, acc);
+    pipe_chunk<PHASE, NA, MUL>(p, stage0, stage1, c, nch, m, fr, acc);
+    pipe_chunk<PHASE, NA, MUL>(p, stage1, stage0, c + 1, nch, m, fr, acc);
   }
-  if (c < nch) pipe_chunk<PHASE, MUL>(p, stage0, stage1, c, nch, m, fr, acc);
+  if (c < nch) pipe_chunk<PHASE, NA, MUL>(p, stage0, stage1, c, nch, m, fr, acc);
 }
 
 }  // namespace
@@ -305,9 +316,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
         p.src[q] = wmat + (size_t)grow * K + seg * 8;
       }
     }
+    const int na = min(kLoadsA, (it.nrows - it.m0 + 63) / 64);  // A slices of this item
     const int wave_row0 = it.m0 + wm * 64;
-    // A wave multiplies iff some of its 64 rows exist; in a half item that
-    // is waves 0..3 only (uniform per wave).
+    // A wave multiplies iff some of its 64 rows exist (wm < na; uniform per
+    // wave).
     const bool mul = wave_row0 < it.nrows;
 
     f32x16 acc[2][4];
@@ -321,8 +333,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
     // Every wave is past the previous item's reads and stores.
     __builtin_amdgcn_s_waitcnt(kWaitAll);
     __builtin_amdgcn_s_barrier();
-    if (mul) run_item<PHASE, true>(p, stage0, stage1, nch, m, acc);
-    else run_item<PHASE, false>(p, stage0, stage1, nch, m, acc);
+    switch (na * 2 + (mul ? 1 : 0)) {  // uniform per wave
+      case 9: run_item<PHASE, 4, true>(p, stage0, stage1, nch, m, acc); break;
+      case 8: run_item<PHASE, 4, false>(p, stage0, stage1, nch, m, acc); break;
+      case 7: run_item<PHASE, 3, true>(p, stage0, stage1, nch, m, acc); break;
+      case 6: run_item<PHASE, 3, false>(p, stage0, stage1, nch, m, acc); break;
+      case 5: run_item<PHASE, 2, true>(p, stage0, stage1, nch, m, acc); break;
+      case 4: run_item<PHASE, 2, false>(p, stage0, stage1, nch, m, acc); break;
+      case 3: run_item<PHASE, 1, true>(p, stage0, stage1, nch, m, acc); break;
+      default: run_item<PHASE, 1, false>(p, stage0, stage1, nch, m, acc); break;
+    }
     if (!mul) continue;
 
     // Epilogue.  Element i of acc[ms][ns] is row 8*(i/4) + 4*lhi + (i%4) of
