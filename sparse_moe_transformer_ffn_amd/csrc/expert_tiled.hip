@@ -196,11 +196,11 @@ __device__ __forceinline__ void pipe_chunk(const Pipe& p, const uint16_t* cur, u
   }
 }
 
-// The K loop of one item over the two stages (unrolled by two).
+// The K loop of one item over the two stages (unrolled by two).  Chunk 0 was
+// issued into stage0 before the previous item's epilogue.
 template <int PHASE, int NA, bool MUL>
 __device__ __forceinline__ void run_item(const Pipe& p, uint16_t* stage0, uint16_t* stage1, int nch,
                                          const ReadMap& m, f32x16 (&acc)[2][4]) {
-  issue_chunk<NA>(p, stage0, 0);
   __builtin_amdgcn_s_waitcnt(kWaitAll);
   __builtin_amdgcn_s_barrier();
   Frags fr[2];
@@ -217,6 +217,87 @@ __device__ __forceinline__ void run_item(const Pipe& p, uint16_t* stage0, uint16
 }
 
 }  // namespace
+
+// Everything an item's K loop and epilogue need, built from its index.
+struct Plan {
+  Item it;
+  int H, nch, na;  // hidden size of its group, K chunks, A slices (1..4)
+  Pipe p;
+};
+
+template <int PHASE>
+__device__ __forceinline__ Plan make_plan(const int* ip, const Groups& gs, int nt_routed, int nt_shared, int wi,
+                                          int d, int h, int hs, const uint16_t* a_src,
+                                          const uint16_t* a_src_shared, const uint16_t* w, const uint16_t* ws,
+                                          int wave, int lane) {
+  Plan pl;
+  const Item it = decode_item<kBand>(ip, gs, kTileM, nt_routed, nt_shared, wi);
+  pl.it = it;
+  pl.H = it.shared ? hs : h;
+  const int K = PHASE == kGateUp ? d : pl.H;
+  pl.nch = K / kChunk;
+  pl.na = min(kLoadsA, (it.nrows - it.m0 + 63) / 64);
+  const uint16_t* wmat;
+  int b_lo, b_hi;  // weight-matrix row of tile row r: b_lo + r (r < 128), b_hi + r (r >= 128)
+  if (PHASE == kGateUp) {
+    wmat = it.shared ? ws : w + (size_t)it.group * 2 * h * d;
+    b_lo = it.nt * (kTileN / 2);
+    b_hi = pl.H + it.nt * (kTileN / 2) - kTileN / 2;
+  } else {
+    wmat = it.shared ? ws : w + (size_t)it.group * d * h;
+    b_lo = it.nt * kTileN;
+    b_hi = it.nt * kTileN;
+  }
+  // Direct-load plan.  Load q of wave `wave` fills one 1 KiB region (8 rows
+  // x 8 slots) of the A (q < kLoadsA) or B part of a stage: region
+  // q' * kWaves + wave, lane l -> row 8 * region + l / 8, slot l % 8 =
+  // segment ^ swz(row).
+  const uint16_t* abase = it.shared ? a_src_shared : a_src;
+  const int astride = PHASE == kGateUp ? d : pl.H;
+  size_t arow[kLoadsA];
+#pragma unroll
+  for (int q = 0; q < kLoadsA; ++q) {
+    const int r = it.m0 + (q * kWaves + wave) * kRegionRows + lane / kSegs;
+    arow[q] = (size_t)(it.row0 + (r < it.nrows ? r : 0));
+  }
+  if (PHASE == kGateUp) {
+    if (it.shared) {
+#pragma unroll
+      for (int q = 0; q < kLoadsA; ++q) arow[q] -= (size_t)it.row0;
+    } else {
+      int tok[kLoadsA];
+#pragma unroll
+      for (int q = 0; q < kLoadsA; ++q) tok[q] = gs.perm[arow[q]];
+#pragma unroll
+      for (int q = 0; q < kLoadsA; ++q) arow[q] = (size_t)(tok[q] / gs.k);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kLoads; ++q) {
+    const bool is_a = q < kLoadsA;
+    const int region = (is_a ? q : q - kLoadsA) * kWaves + wave;
+    const int row = region * kRegionRows + lane / kSegs;
+    const int seg = (lane % kSegs) ^ swz(row);
+    pl.p.lds_off[q] = (is_a ? 0 : kStageA) + region * kRegionRows * kChunk;
+    if (is_a) {
+      pl.p.src[q] = abase + arow[q] * astride + seg * 8;
+    } else {
+      const int grow = row < kTileN / 2 ? b_lo + row : b_hi + row;
+      pl.p.src[q] = wmat + (size_t)grow * K + seg * 8;
+    }
+  }
+  return pl;
+}
+
+// An item's first chunk, into stage0.
+__device__ __forceinline__ void issue_first(const Plan& pl, uint16_t* stage0) {
+  switch (pl.na) {
+    case 4: issue_chunk<4>(pl.p, stage0, 0); break;
+    case 3: issue_chunk<3>(pl.p, stage0, 0); break;
+    case 2: issue_chunk<2>(pl.p, stage0, 0); break;
+    default: issue_chunk<1>(pl.p, stage0, 0); break;
+  }
+}
 
 // PHASE kGateUp: A = x rows (gathered), B rows = gate/up rows, K = d,
 //                out = SiLU(G) * U -> hid / hid_shared (bf16, row stride H).
@@ -253,75 +334,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
 
   // Dynamic work queue per XCD: XCD x owns items [lo, hi) and its blocks take
   // them in order, one atomic per item.  Every block exits once its XCD's
-  // range is exhausted.
+  // range is exhausted.  The next item is taken, planned and its first chunk
+  // issued right after the current item's K loop, so that chunk's latency
+  // overlaps the current item's epilogue.
   const int xcd = blockIdx.x % kNumXcd;
   const int lo = (int)((long long)items * xcd / kNumXcd);
   const int hi = (int)((long long)items * (xcd + 1) / kNumXcd);
+  if (tid == 0) next_item = lo + atomicAdd(&queue[xcd], 1);
+  __syncthreads();
+  int wi = next_item;
+  if (wi >= hi) return;  // uniform across the block
+  Plan cur = make_plan<PHASE>(ip, gs, nt_routed, nt_shared, wi, d, h, hs, a_src, a_src_shared, w, ws, wave, lane);
+  issue_first(cur, stage0);
   for (;;) {
-    if (tid == 0) next_item = lo + atomicAdd(&queue[xcd], 1);
-    __syncthreads();
-    const int wi = next_item;
-    if (wi >= hi) break;  // uniform across the block
-    const Item it = decode_item<kBand>(ip, gs, kTileM, nt_routed, nt_shared, wi);
-    const int H = it.shared ? hs : h;
-    const int K = PHASE == kGateUp ? d : H;
-    const int nch = K / kChunk;
-    const uint16_t* wmat;
-    int b_lo, b_hi;  // weight-matrix row of tile row r: b_lo + r (r < 128), b_hi + r (r >= 128)
-    if (PHASE == kGateUp) {
-      wmat = it.shared ? ws : w + (size_t)it.group * 2 * h * d;
-      b_lo = it.nt * (kTileN / 2);
-      b_hi = H + it.nt * (kTileN / 2) - kTileN / 2;
-    } else {
-      wmat = it.shared ? ws : w + (size_t)it.group * d * h;
-      b_lo = it.nt * kTileN;
-      b_hi = it.nt * kTileN;
-    }
-    // Direct-load plan.  Load q of wave `wave` fills one 1 KiB region (8 rows
-    // x 8 slots) of the A (q < kLoadsA) or B part of a stage: region
-    // q' * kWaves + wave, lane l -> row 8 * region + l / 8, slot l % 8 =
-    // segment ^ swz(row).
-    Pipe p;
-    const uint16_t* abase = it.shared ? a_src_shared : a_src;
-    const int astride = PHASE == kGateUp ? d : H;
-    size_t arow[kLoadsA];
-#pragma unroll
-    for (int q = 0; q < kLoadsA; ++q) {
-      const int r = it.m0 + (q * kWaves + wave) * kRegionRows + lane / kSegs;
-      arow[q] = (size_t)(it.row0 + (r < it.nrows ? r : 0));
-    }
-    if (PHASE == kGateUp) {
-      if (it.shared) {
-#pragma unroll
-        for (int q = 0; q < kLoadsA; ++q) arow[q] -= (size_t)it.row0;
-      } else {
-        int tok[kLoadsA];
-#pragma unroll
-        for (int q = 0; q < kLoadsA; ++q) tok[q] = gs.perm[arow[q]];
-#pragma unroll
-        for (int q = 0; q < kLoadsA; ++q) arow[q] = (size_t)(tok[q] / gs.k);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < kLoads; ++q) {
-      const bool is_a = q < kLoadsA;
-      const int region = (is_a ? q : q - kLoadsA) * kWaves + wave;
-      const int row = region * kRegionRows + lane / kSegs;
-      const int seg = (lane % kSegs) ^ swz(row);
-      p.lds_off[q] = (is_a ? 0 : kStageA) + region * kRegionRows * kChunk;
-      if (is_a) {
-        p.src[q] = abase + arow[q] * astride + seg * 8;
-      } else {
-        const int grow = row < kTileN / 2 ? b_lo + row : b_hi + row;
-        p.src[q] = wmat + (size_t)grow * K + seg * 8;
-      }
-    }
-    const int na = min(kLoadsA, (it.nrows - it.m0 + 63) / 64);  // A slices of this item
-    const int wave_row0 = it.m0 + wm * 64;
+    const int wave_row0 = cur.it.m0 + wm * 64;
     // A wave multiplies iff some of its 64 rows exist (wm < na; uniform per
     // wave).
-    const bool mul = wave_row0 < it.nrows;
-
+    const bool mul = wave_row0 < cur.it.nrows;
     f32x16 acc[2][4];
 #pragma unroll
     for (int ms = 0; ms < 2; ++ms)
@@ -329,48 +358,62 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
       for (int ns = 0; ns < 4; ++ns)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[ms][ns][i] = 0.f;
-
-    // Every wave is past the previous item's reads and stores.
-    __builtin_amdgcn_s_waitcnt(kWaitAll);
-    __builtin_amdgcn_s_barrier();
-    switch (na * 2 + (mul ? 1 : 0)) {  // uniform per wave
-      case 9: run_item<PHASE, 4, true>(p, stage0, stage1, nch, m, acc); break;
-      case 8: run_item<PHASE, 4, false>(p, stage0, stage1, nch, m, acc); break;
-      case 7: run_item<PHASE, 3, true>(p, stage0, stage1, nch, m, acc); break;
-      case 6: run_item<PHASE, 3, false>(p, stage0, stage1, nch, m, acc); break;
-      case 5: run_item<PHASE, 2, true>(p, stage0, stage1, nch, m, acc); break;
-      case 4: run_item<PHASE, 2, false>(p, stage0, stage1, nch, m, acc); break;
-      case 3: run_item<PHASE, 1, true>(p, stage0, stage1, nch, m, acc); break;
-      default: run_item<PHASE, 1, false>(p, stage0, stage1, nch, m, acc); break;
+    switch (cur.na * 2 + (mul ? 1 : 0)) {  // uniform per wave
+      case 9: run_item<PHASE, 4, true>(cur.p, stage0, stage1, cur.nch, m, acc); break;
+      case 8: run_item<PHASE, 4, false>(cur.p, stage0, stage1, cur.nch, m, acc); break;
+      case 7: run_item<PHASE, 3, true>(cur.p, stage0, stage1, cur.nch, m, acc); break;
+      case 6: run_item<PHASE, 3, false>(cur.p, stage0, stage1, cur.nch, m, acc); break;
+      case 5: run_item<PHASE, 2, true>(cur.p, stage0, stage1, cur.nch, m, acc); break;
+      case 4: run_item<PHASE, 2, false>(cur.p, stage0, stage1, cur.nch, m, acc); break;
+      case 3: run_item<PHASE, 1, true>(cur.p, stage0, stage1, cur.nch, m, acc); break;
+      default: run_item<PHASE, 1, false>(cur.p, stage0, stage1, cur.nch, m, acc); break;
     }
-    if (!mul) continue;
+    // Every wave is past the K loop (its LDS reads done, its trailing loads
+    // landed: the release fence of this barrier drains both), so stage0 may
+    // take the next item's first chunk; next_item was last read before the
+    // K loop.
+    if (tid == 0) next_item = lo + atomicAdd(&queue[xcd], 1);
+    __syncthreads();
+    wi = next_item;
+    const bool more = wi < hi;  // uniform across the block
+    Plan nxt;
+    if (more) {
+      nxt = make_plan<PHASE>(ip, gs, nt_routed, nt_shared, wi, d, h, hs, a_src, a_src_shared, w, ws, wave, lane);
+      issue_first(nxt, stage0);
+    }
 
     // Epilogue.  Element i of acc[ms][ns] is row 8*(i/4) + 4*lhi + (i%4) of
     // M-subtile ms, column l32 of N-subtile ns.
+    if (mul) {
+      const Item& it = cur.it;
+      const int H = cur.H;
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms) {
+      for (int ms = 0; ms < 2; ++ms) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = wave_row0 + ms * 32 + 8 * (i / 4) + 4 * lhi + (i % 4);
-        if (r >= it.nrows) continue;
-        const size_t grow = (size_t)(it.row0 + r);
-        if (PHASE == kGateUp) {
-          uint16_t* o = it.shared ? static_cast<uint16_t*>(out_shared) : out;
+        for (int i = 0; i < 16; ++i) {
+          const int r = wave_row0 + ms * 32 + 8 * (i / 4) + 4 * lhi + (i % 4);
+          if (r >= it.nrows) continue;
+          const size_t grow = (size_t)(it.row0 + r);
+          if (PHASE == kGateUp) {
+            uint16_t* o = it.shared ? static_cast<uint16_t*>(out_shared) : out;
 #pragma unroll
-          for (int ns = 0; ns < 2; ++ns) {
-            const float g = acc[ms][ns][i], u = acc[ms][ns + 2][i];
-            o[grow * H + it.nt * (kTileN / 2) + wn * 64 + ns * 32 + l32] = (uint16_t)f32_to_bf16(silu(g) * u);
-          }
-        } else {
+            for (int ns = 0; ns < 2; ++ns) {
+              const float g = acc[ms][ns][i], u = acc[ms][ns + 2][i];
+              o[grow * H + it.nt * (kTileN / 2) + wn * 64 + ns * 32 + l32] = (uint16_t)f32_to_bf16(silu(g) * u);
+            }
+          } else {
 #pragma unroll
-          for (int ns = 0; ns < 4; ++ns) {
-            const size_t o = grow * d + it.nt * kTileN + wn * 128 + ns * 32 + l32;
-            if (it.shared) static_cast<float*>(out_shared)[o] = acc[ms][ns][i];
-            else out[o] = (uint16_t)f32_to_bf16(acc[ms][ns][i]);
+            for (int ns = 0; ns < 4; ++ns) {
+              const size_t o = grow * d + it.nt * kTileN + wn * 128 + ns * 32 + l32;
+              if (it.shared) static_cast<float*>(out_shared)[o] = acc[ms][ns][i];
+              else out[o] = (uint16_t)f32_to_bf16(acc[ms][ns][i]);
+            }
           }
         }
       }
     }
+    if (!more) break;
+    cur = nxt;
   }
   // No direct load may still be writing this block's LDS when it exits.
   __builtin_amdgcn_s_waitcnt(kWaitAll);
