@@ -35,8 +35,10 @@ def lib():
                                    _I, _P, _P, _P, _P, _P]
         L.oracle_rmsnorm.argtypes = [_I, _I, _P, _P, ctypes.c_float, _P]
         L.oracle_combine.argtypes = [_I, _I, _I, _P, _P, _P, _P, ctypes.c_float, _P]
+        L.oracle_route_diag.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P]
+        L.oracle_activation_rms.argtypes = [_I, _I, _P, _P]
         for f in (L.oracle_route, L.oracle_permute, L.oracle_expert, L.oracle_layer, L.oracle_rmsnorm,
-                  L.oracle_combine):
+                  L.oracle_combine, L.oracle_route_diag, L.oracle_activation_rms):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -167,3 +169,29 @@ def rmsnorm(v, gamma=None, eps=1e-6):
     out = np.zeros((T, d), np.uint16)
     _check(lib().oracle_rmsnorm(T, d, _ptr(v), _ptr(gamma), float(eps), _ptr(out)), "oracle_rmsnorm")
     return out
+
+
+def route_diag(scores, topk_ids, groups=1):
+    """Routing diagnostics from the unbiased scores [T,E] and chosen ids [T,k].
+    Returns (p_e [E], f_e [E], l_ep, confidence), all float64."""
+    scores = _c(scores, np.float32)
+    ids = _c(topk_ids, np.int32)
+    T, E = scores.shape
+    k = ids.shape[1]
+    p_e = np.zeros(E)
+    f_e = np.zeros(E)
+    l_ep = ctypes.c_double()
+    conf = ctypes.c_double()
+    rc = lib().oracle_route_diag(T, E, k, int(groups), _ptr(scores), _ptr(ids), _ptr(p_e), _ptr(f_e),
+                                 ctypes.addressof(l_ep), ctypes.addressof(conf))
+    _check(rc, "oracle_route_diag")
+    return p_e, f_e, l_ep.value, conf.value
+
+
+def activation_rms(rows):
+    """RMS over every element of one expert's output rows [n,d] (0 if n = 0)."""
+    rows = _c(rows, np.float32)
+    n, d = rows.shape
+    out = ctypes.c_double()
+    _check(lib().oracle_activation_rms(n, d, _ptr(rows), ctypes.addressof(out)), "oracle_activation_rms")
+    return out.value

@@ -241,6 +241,72 @@ int oracle_combine(int T, int d, int k, const uint16_t* y_perm, const int32_t* p
   return 0;
 }
 
+// Routing diagnostics ([Blog] §2.2.2, EP-level load balance: p_e, f_e, their
+// group sums p_g, f_g and L_EP = G * sum_g f_g p_g over G disjoint expert
+// groups; §5.2.3, routing confidence: the mean probability mass of the
+// activated experts).  Readings: the routing probability p_{t,e} of a sigmoid
+// router is the token's unbiased scores normalised over all E experts (so
+// that sum_e p_e = 1 and L_EP is 1 under uniform routing, as the loss
+// intends); the G groups are contiguous blocks of E/G experts (expert
+// parallelism placing consecutive experts on one rank).
+//   scores [T,E]  unbiased sigmoid scores s_{t,e} (oracle_route's output)
+//   topk_ids [T,k] the chosen set S_t
+//   p_e [E], f_e [E], l_ep, confidence: outputs (double)
+// f_e = |{t : e in S_t}| / (T k).  T = 0 gives zeros.
+int oracle_route_diag(int T, int E, int k, int G, const float* scores, const int32_t* topk_ids, double* p_e,
+                      double* f_e, double* l_ep, double* confidence) {
+  if (T < 0 || E <= 0 || k < 1 || k > E || G < 1 || E % G != 0 || !p_e || !f_e || !l_ep || !confidence) return -1;
+  if (T > 0 && (!scores || !topk_ids)) return -1;
+  for (int e = 0; e < E; ++e) p_e[e] = f_e[e] = 0.0;
+  double mass = 0.0;
+  std::vector<double> p(E);
+  for (int t = 0; t < T; ++t) {
+    double total = 0.0;
+    for (int e = 0; e < E; ++e) total += (double)scores[(size_t)t * E + e];
+    for (int e = 0; e < E; ++e) {
+      p[e] = (double)scores[(size_t)t * E + e] / total;
+      p_e[e] += p[e];
+    }
+    for (int j = 0; j < k; ++j) {
+      const int e = topk_ids[(size_t)t * k + j];
+      if (e < 0 || e >= E) return -2;
+      f_e[e] += 1.0;
+      mass += p[e];
+    }
+  }
+  *l_ep = 0.0;
+  *confidence = 0.0;
+  if (T == 0) return 0;
+  for (int e = 0; e < E; ++e) {
+    p_e[e] /= (double)T;
+    f_e[e] /= (double)T * k;
+  }
+  const int per = E / G;
+  for (int g = 0; g < G; ++g) {
+    double pg = 0.0, fg = 0.0;
+    for (int e = g * per; e < (g + 1) * per; ++e) {
+      pg += p_e[e];
+      fg += f_e[e];
+    }
+    *l_ep += fg * pg;
+  }
+  *l_ep *= G;
+  *confidence = mass / T;
+  return 0;
+}
+
+// Root mean square of one expert's activations ([Blog] §4.1.2, per-expert
+// activation norms as an expert-collapse signal; [Digest] expert collapse:
+// monitor each expert's activation RMS against the median): the expert's
+// output rows o_{t,e} [n, d] (f32) -> sqrt(mean of o^2), 0 for n = 0.
+int oracle_activation_rms(int n, int d, const float* rows, double* rms) {
+  if (n < 0 || d <= 0 || !rms || (n > 0 && !rows)) return -1;
+  double ss = 0.0;
+  for (int64_t i = 0; i < (int64_t)n * d; ++i) ss += (double)rows[i] * (double)rows[i];
+  *rms = n > 0 ? std::sqrt(ss / ((double)n * d)) : 0.0;
+  return 0;
+}
+
 // Zero-centred RMSNorm (pre-norm placement, [Blog] §2.2, Figure 2 caption): each
 // row v -> v / sqrt(mean(v^2) + eps) * (1 + gamma), gamma NULL meaning 0 (unit
 // gain).  in [T,d] bf16 -> out [T,d] bf16 (round to nearest even).

@@ -449,3 +449,117 @@ def test_rmsnorm_matches_library_and_is_scale_invariant():
     np.testing.assert_array_equal(from_bf16(out2), from_bf16(out) * 2.0)
     rms = np.sqrt((from_bf16(out).astype(np.float64) ** 2).mean(1))
     np.testing.assert_allclose(rms, 1.0, atol=4e-3)
+
+
+# ------------------------------------------------------------ diagnostics --
+# [Blog] §2.2.2 (p_e, f_e, group sums, L_EP over G expert groups), §5.2.3
+# (routing confidence), §4.1.2 / Figure 4 (per-expert activation norms).
+
+def _route_with_scores(x, wr, b, k, logit_bias=None):
+    ids, _, _, s = oracle.route(x, wr, b, k, logit_bias=logit_bias, want_scores=True)
+    return ids, s
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_diag_uniform_scores_closed_form(G):
+    # x = 0 makes every logit 0, every score 1/2 and every p_{t,e} = 1/E,
+    # whatever the selection bias picks; then p_g = 1/G and L_EP = sum_g f_g = 1.
+    rng = np.random.default_rng(40 + G)
+    T, d, E, k = 37, 64, 16, 3
+    x = np.zeros((T, d), np.uint16)
+    wr = rand_bf16(rng, (E, d), 0.05)
+    b = rng.uniform(-0.3, 0.3, E).astype(np.float32)
+    ids, s = _route_with_scores(x, wr, b, k)
+    p_e, f_e, l_ep, conf = oracle.route_diag(s, ids, G)
+    np.testing.assert_allclose(p_e, 1.0 / E, rtol=1e-14)
+    assert l_ep == pytest.approx(1.0, rel=1e-14)
+    assert conf == pytest.approx(k / E, rel=1e-14)
+    # f_e counts the bias-chosen set: ids are the same for every token here.
+    expect_f = np.zeros(E)
+    expect_f[ids[0]] = 1.0 / k
+    np.testing.assert_array_equal(f_e, expect_f)
+
+
+def test_diag_two_groups_closed_form_from_logit_bias():
+    # x = 0 and a per-expert logit term: s_e = expit(c_e) for every token, so
+    # p_e = expit(c_e) / sum expit(c).  A selection bias of +1 on expert 0 with
+    # k = 1 gives f = (1, 0, 0, 0).  With contiguous groups {0,1} {2,3},
+    # L_EP = 2 * (p_0 + p_1); p_1 != p_2 separates this from interleaved groups.
+    T, d, E, k = 9, 64, 4, 1
+    c = np.array([0.3, 1.5, -2.0, 0.7], np.float32)
+    x = np.zeros((T, d), np.uint16)
+    wr = to_bf16(np.ones((E, d)))
+    b = np.array([1.0, 0, 0, 0], np.float32)
+    ids, s = _route_with_scores(x, wr, b, k, logit_bias=c)
+    assert np.all(ids == 0)
+    p_e, f_e, l_ep, conf = oracle.route_diag(s, ids, 2)
+    sig = scipy.special.expit(c.astype(np.float64))
+    p = sig / sig.sum()
+    np.testing.assert_allclose(p_e, p, rtol=1e-7)
+    np.testing.assert_array_equal(f_e, [1.0, 0, 0, 0])
+    assert l_ep == pytest.approx(2 * (p[0] + p[1]), rel=1e-7)
+    assert conf == pytest.approx(p[0], rel=1e-7)
+    # One group: L_EP = 1 whatever f and p are.  E groups of one: E * f_0 p_0.
+    assert oracle.route_diag(s, ids, 1)[2] == pytest.approx(1.0, rel=1e-14)
+    assert oracle.route_diag(s, ids, E)[2] == pytest.approx(E * p[0], rel=1e-7)
+
+
+def test_diag_all_experts_chosen_has_full_confidence():
+    rng = np.random.default_rng(43)
+    T, d, E = 21, 64, 6
+    x = rand_bf16(rng, (T, d))
+    wr = rand_bf16(rng, (E, d), 0.1)
+    b = rng.uniform(-0.1, 0.1, E).astype(np.float32)
+    ids, s = _route_with_scores(x, wr, b, E)
+    p_e, f_e, _, conf = oracle.route_diag(s, ids, 3)
+    assert conf == pytest.approx(1.0, rel=1e-12)
+    np.testing.assert_allclose(f_e, 1.0 / E, rtol=1e-14)
+    # p_e is the token mean of the library sigmoids normalised per token.
+    z = from_bf16(x).astype(np.float64) @ from_bf16(wr).astype(np.float64).T
+    sg = scipy.special.expit(z)
+    np.testing.assert_allclose(p_e, (sg / sg.sum(1, keepdims=True)).mean(0), rtol=2e-6)
+
+
+@pytest.mark.parametrize("T,d,E,k,G", [(64, 256, 16, 2, 4), (48, 512, 288, 8, 8)])
+def test_diag_invariants(T, d, E, k, G):
+    rng = np.random.default_rng(T * E + G)
+    x = rand_bf16(rng, (T, d))
+    wr = rand_bf16(rng, (E, d), 0.05)
+    ids, s = _route_with_scores(x, wr, np.zeros(E, np.float32), k)
+    p_e, f_e, l_ep, conf = oracle.route_diag(s, ids, G)
+    assert p_e.sum() == pytest.approx(1.0, rel=1e-12)
+    assert f_e.sum() == pytest.approx(1.0, rel=1e-12)
+    assert np.all(p_e > 0) and np.all(f_e >= 0)
+    # f_e is the selection histogram over T k picks.
+    np.testing.assert_array_equal(f_e * T * k, np.bincount(ids.ravel(), minlength=E))
+    # Without a selection bias the chosen experts are each token's k largest
+    # p_{t,e}, so their mass is at least the uniform share k / E, and below 1.
+    assert k / E <= conf < 1.0
+    # Confidence is not the renormalised weight mass (which is 1).
+    assert conf < 0.99
+    assert l_ep > 0
+    # T = 0: everything is zero.
+    z = oracle.route_diag(np.zeros((0, E), np.float32), np.zeros((0, k), np.int32), G)
+    assert not z[0].any() and not z[1].any() and z[2] == 0.0 and z[3] == 0.0
+
+
+def test_diag_rejects_uneven_groups():
+    s = np.full((2, 6), 0.5, np.float32)
+    ids = np.array([[0], [1]], np.int32)
+    with pytest.raises(ValueError):
+        oracle.route_diag(s, ids, 4)
+
+
+def test_activation_rms_closed_forms():
+    rng = np.random.default_rng(44)
+    rows = rng.standard_normal((7, 96)).astype(np.float32)
+    r = oracle.activation_rms(rows)
+    assert r == pytest.approx(float(torch.linalg.vector_norm(torch.from_numpy(rows).double()) / np.sqrt(7 * 96)),
+                              rel=1e-14)
+    assert oracle.activation_rms(2 * rows) == pytest.approx(2 * r, rel=1e-14)
+    assert oracle.activation_rms(np.full((3, 8), -0.75, np.float32)) == pytest.approx(0.75, rel=1e-15)
+    assert oracle.activation_rms(np.zeros((0, 8), np.float32)) == 0.0
+    # Rows with equal mean squares: the RMS is that of any one of them.
+    one = rng.standard_normal(64).astype(np.float32)
+    assert oracle.activation_rms(np.stack([one, -one, one[::-1]])) == pytest.approx(
+        oracle.activation_rms(one[None]), rel=1e-14)
