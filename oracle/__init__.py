@@ -195,3 +195,28 @@ def activation_rms(rows):
     out = ctypes.c_double()
     _check(lib().oracle_activation_rms(n, d, _ptr(rows), ctypes.addressof(out)), "oracle_activation_rms")
     return out.value
+
+
+def expert_rms(y_perm, offsets, y_shared=None):
+    """Per-expert activation RMS of the permuted expert outputs y_perm [T*k,d]
+    (bf16 bits) grouped by offsets [E+1], plus the shared expert's y_shared
+    [T,d] f32 (entry E; 0 if None), and the spread (min, max) / median over
+    the experts with at least one row ([Blog] §4.1.3, Figure 4: maximum against
+    median expert output norm; [Digest] expert collapse: min-to-median).  An
+    even count's median is the mean of the two middle values (numpy's).
+    Returns (rms [E+1] float64, ratio [2] float64; (0, 0) without a row)."""
+    offsets = np.asarray(offsets, np.int64)
+    E = offsets.shape[0] - 1
+    rows = (np.asarray(y_perm, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    rms = np.zeros(E + 1)
+    for e in range(E):
+        rms[e] = activation_rms(rows[offsets[e]:offsets[e + 1]].reshape(-1, rows.shape[1]))
+    if y_shared is not None:
+        rms[E] = activation_rms(y_shared)
+    used = rms[:E][offsets[1:] > offsets[:-1]]
+    ratio = np.zeros(2)
+    if used.size:
+        med = float(np.median(used))
+        if med > 0:
+            ratio[:] = used.min() / med, used.max() / med
+    return rms, ratio

@@ -563,3 +563,27 @@ def test_activation_rms_closed_forms():
     one = rng.standard_normal(64).astype(np.float32)
     assert oracle.activation_rms(np.stack([one, -one, one[::-1]])) == pytest.approx(
         oracle.activation_rms(one[None]), rel=1e-14)
+
+
+def test_expert_rms_groups_rows_and_ratio_closed_form():
+    # Expert e's rows all hold the constant c_e, so its RMS is |c_e|; expert 2
+    # gets no rows and is left out of the median.  Used RMS (1, 2, 3, 4):
+    # median 2.5, ratios 0.4 and 1.6.
+    d = 16
+    counts = np.array([2, 1, 0, 3, 1])
+    c = np.array([-1.0, 2.0, 9.0, 3.0, -4.0])
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    rows = np.concatenate([np.full((n, d), v, np.float32) for n, v in zip(counts, c)])
+    shared = np.full((4, d), 0.5, np.float32)
+    rms, ratio = oracle.expert_rms(to_bf16(rows), offsets, shared)
+    np.testing.assert_allclose(rms, [1, 2, 0, 3, 4, 0.5], rtol=1e-15)
+    np.testing.assert_allclose(ratio, [0.4, 1.6], rtol=1e-15)
+    # Odd count: the middle value.  Drop expert 4's row.
+    counts2 = np.array([2, 1, 0, 3, 0])
+    offsets2 = np.concatenate([[0], np.cumsum(counts2)])
+    rms2, ratio2 = oracle.expert_rms(to_bf16(rows[:6]), offsets2)
+    np.testing.assert_allclose(ratio2, [0.5, 1.5], rtol=1e-15)
+    assert rms2[5] == 0.0
+    # No rows at all.
+    rms3, ratio3 = oracle.expert_rms(np.zeros((0, d), np.uint16), np.zeros(4, np.int64))
+    assert not rms3.any() and not ratio3.any()
