@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE layer tok/s; % HBM BW at T=64, % bf16 MFMA peak at T=8192"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+DIAG_GROUPS = 8                # expert groups of the load-balance statistic: EP8, 36 experts per rank
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -151,26 +152,47 @@ class Workload:
         self.buf = moe.LayerBuffers.allocate(cfg.T, d, E, cfg.k, h, hs, device=dev)
         self.hid = torch.empty((cfg.T * cfg.k, h), dtype=torch.bfloat16, device=dev)
         self.hid_shared = torch.empty((cfg.T, hs), dtype=torch.bfloat16, device=dev)
+        # Diagnostics outputs (routing statistics over DIAG_GROUPS expert
+        # groups, per-expert activation RMS and its spread).
+        self.p_e = torch.empty((E,), dtype=torch.float32, device=dev)
+        self.f_e = torch.empty((E,), dtype=torch.float32, device=dev)
+        self.route_summary = torch.empty((2,), dtype=torch.float32, device=dev)
+        self.expert_rms = torch.empty((E + 1,), dtype=torch.float32, device=dev)
+        self.rms_ratio = torch.empty((2,), dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
 
-    def step(self, main, ev=None):
-        """One forward; ev = (before gate_up, after gate_up, after down) events."""
+    def step(self, main, ev=None, diag=False):
+        """One forward; ev = (step start, before gate_up, after gate_up,
+        after down, step end) events; diag: the routing and combine calls
+        with their diagnostic side outputs."""
         import sparse_moe_transformer_ffn_amd as moe
         b, sh, c = self.buf, self.buf.shape, self.cfg
-        moe.moe_route(sh, self.x, self.wr, self.b, self.c, b.topk_ids, b.topk_weights, b.expert_counts, b.topk_gap,
-                      b.workspace, main)
-        moe.moe_permute(sh, b.topk_ids, b.expert_offsets, b.perm_pairs, b.pair_pos, b.workspace, main)
         if ev:
             ev[0].record(main)
+        if diag:
+            moe.moe_route_diag(sh, self.x, self.wr, self.b, self.c, b.topk_ids, b.topk_weights, b.expert_counts,
+                               b.topk_gap, DIAG_GROUPS, self.p_e, self.f_e, self.route_summary, b.workspace, main)
+        else:
+            moe.moe_route(sh, self.x, self.wr, self.b, self.c, b.topk_ids, b.topk_weights, b.expert_counts,
+                          b.topk_gap, b.workspace, main)
+        moe.moe_permute(sh, b.topk_ids, b.expert_offsets, b.perm_pairs, b.pair_pos, b.workspace, main)
+        if ev:
+            ev[1].record(main)
         moe.moe_expert_gate_up(sh, self.x, b.expert_offsets, b.perm_pairs, self.w_gu, self.hid, b.workspace, main,
                                ws_gate_up=self.ws_gu, hid_shared=self.hid_shared)
         if ev:
-            ev[1].record(main)
+            ev[2].record(main)
         moe.moe_expert_down(sh, b.expert_offsets, self.hid, self.w_d, b.y_perm, b.workspace, main,
                             hid_shared=self.hid_shared, ws_down=self.ws_d, y_shared=b.y_shared)
         if ev:
-            ev[2].record(main)
-        moe.moe_combine(sh, b.y_perm, b.pair_pos, b.topk_weights, b.y_shared, c.routed_scale, b.y, main)
+            ev[3].record(main)
+        if diag:
+            moe.moe_combine_diag(sh, b.y_perm, b.pair_pos, b.topk_weights, b.y_shared, c.routed_scale, b.y,
+                                 b.expert_offsets, self.expert_rms, self.rms_ratio, b.workspace, main)
+        else:
+            moe.moe_combine(sh, b.y_perm, b.pair_pos, b.topk_weights, b.y_shared, c.routed_scale, b.y, main)
+        if ev:
+            ev[4].record(main)
 
 
 def algorithmic(cfg, n_touched):
@@ -197,7 +219,7 @@ def time_workload(cfg, steps, warmup, dev):
     for _ in range(warmup):
         wl.step(main)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -209,13 +231,28 @@ def time_workload(cfg, steps, warmup, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = t0.elapsed_time(t1) / steps
-    gate_up_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    down_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    # The same steps with the diagnostic side outputs, timed separately (not
+    # part of the headline figure).
+    wl.step(main, diag=True)
+    dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for i in range(steps):
+        wl.step(main, dev_ev[i], diag=True)
+    torch.cuda.synchronize()
+    diag_step = np.array([e[0].elapsed_time(e[4]) for e in dev_ev])
+    diag = dict(ep_groups=DIAG_GROUPS, ms_per_step_median=float(np.median(diag_step)),
+                l_ep=float(wl.route_summary[0]), confidence=float(wl.route_summary[1]),
+                rms_min_to_median=float(wl.rms_ratio[0]), rms_max_to_median=float(wl.rms_ratio[1]))
+    gate_up_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    down_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    per_step = np.array([e[0].elapsed_time(e[4]) for e in evs])
     counts = wl.buf.expert_counts.cpu().numpy()
     n_touched = int((counts > 0).sum())
     alg = algorithmic(cfg, n_touched)
     res = dict(ms_per_step=ms, wall_ms_per_step=wall * 1e3 / steps, gate_up_ms=gate_up_ms, down_ms=down_ms,
+               ms_per_step_median=float(np.median(per_step)), ms_per_step_min=float(per_step.min()),
                n_touched=n_touched, max_load=int(counts.max()), idle_experts=int((counts == 0).sum()), alg=alg)
+    diag["overhead_ms"] = diag["ms_per_step_median"] - res["ms_per_step_median"]
+    res["diagnostics"] = diag
     return wl, res
 
 
@@ -234,14 +271,36 @@ def cpu_baseline(wl, n_sample):
     gu = [ew[e][0] if e in ew else None for e in range(cfg.E)]
     wd = [ew[e][1] if e in ew else None for e in range(cfg.E)]
     sgu, swd = moegen.shared_weights_host(cfg)
-    t = time.perf_counter()
-    oracle.layer(wl.x_h, wl.wr_h, wl.b_h, cfg.k, gu, wd, sgu, swd, cfg.routed_scale, logit_bias=wl.c_h,
-                 tokens=tokens)
-    dt = time.perf_counter() - t
+    # One thread, pinned to one core for the timed call.
+    saved = os.sched_getaffinity(0)
+    core = min(saved)
+    os.sched_setaffinity(0, {core})
+    try:
+        t = time.perf_counter()
+        oracle.layer(wl.x_h, wl.wr_h, wl.b_h, cfg.k, gu, wd, sgu, swd, cfg.routed_scale, logit_bias=wl.c_h,
+                     tokens=tokens)
+        dt = time.perf_counter() - t
+    finally:
+        os.sched_setaffinity(0, saved)
+    flops_per_token = 2 * cfg.d * cfg.E + 2 * 3 * cfg.d * (cfg.k * cfg.h + cfg.hs)
     return {"value": n_sample / dt, "unit": "tok/s", "cores": 1, "kind": "oracle",
+            "gflops": n_sample * flops_per_token / dt / 1e9,
+            "host": {"cpu": host_cpu_model(), "online_cores": os.cpu_count(), "affinity_cores": len(saved),
+                     "pinned_to": core},
             "sample": f"{n_sample} of the {cfg.T} tokens of the {cfg.name} workload, whole layer per token "
                       f"(route over {cfg.E} experts, {cfg.k} routed + 1 shared SwiGLU expert, combine); "
-                      f"{dt:.1f} s on one host thread"}
+                      f"{dt:.1f} s on one host thread pinned to one core"}
+
+
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def roofline(kind, achieved, traffic):
@@ -301,7 +360,8 @@ def main():
     gate_up_gbs = alg["gate_up_bytes"] / (r["gate_up_ms"] * 1e-3) / 1e9
     out = {
         "metric": METRIC, "value": tok_s, "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": r["ms_per_step"], "ms_per_step_median": r["ms_per_step_median"],
+        "ms_per_step_min": r["ms_per_step_min"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.workload, "tokens": cfg.T, "d_model": cfg.d, "experts": cfg.E, "top_k": cfg.k,
                    "expert_hidden": cfg.h, "shared_hidden": cfg.hs, "seed": cfg.seed},
@@ -313,6 +373,7 @@ def main():
         "kernels": {"gate_up_ms": r["gate_up_ms"], "down_ms": r["down_ms"],
                     "gate_up_gbs": gate_up_gbs,
                     "down_gbs": alg["down_bytes"] / (r["down_ms"] * 1e-3) / 1e9},
+        "diagnostics": r["diagnostics"],
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
@@ -327,11 +388,13 @@ def main():
         step_tf = palg["step_flops"] / (p["ms_per_step"] * 1e-3) / 1e12
         out["prefill"] = {
             "workload": pcfg.workload, "tok_s": pcfg.T / (p["ms_per_step"] * 1e-3), "ms_per_step": p["ms_per_step"],
+            "ms_per_step_median": p["ms_per_step_median"], "ms_per_step_min": p["ms_per_step_min"],
             "steps": args.prefill_steps, "step_tflops": step_tf, "step_mfma_frac": step_tf / BF16_PEAK_TFLOPS,
             "roofline": roofline("mfma", gate_up_tf, load_traffic("prefill", "gate_up")),
             "kernels": {"gate_up_ms": p["gate_up_ms"], "down_ms": p["down_ms"],
                         "down_tflops": palg["down_flops"] / (p["down_ms"] * 1e-3) / 1e12},
             "touched_experts": p["n_touched"], "max_load": p["max_load"], "idle_experts": p["idle_experts"],
+            "diagnostics": p["diagnostics"],
         }
         del pwl
     print(json.dumps(out), flush=True)

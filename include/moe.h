@@ -25,6 +25,10 @@
  *   moe_shared_swiglu  the always-on shared expert
  *   moe_combine        y = y_shared + routed_scale * sum_j w_j * y_perm[pos]
  *
+ * with diagnostic variants of two of them (same outputs, plus side outputs):
+ *   moe_route_diag     + load-balance and confidence statistics of the routing
+ *   moe_combine_diag   + per-expert activation RMS and its spread
+ *
  * plus moe_rmsnorm, the zero-centred RMSNorm that sits in front of every FFN
  * sub-layer ([Blog] §2.2, Figure 2 caption), used between stacked layers.
  *
@@ -113,6 +117,26 @@ moe_status moe_route(const moe_shape* shape, const uint16_t* x, const uint16_t* 
                      const float* logit_bias, int32_t* topk_ids, float* topk_weights, int32_t* expert_counts,
                      float* topk_gap, void* workspace, size_t ws_bytes, void* stream);
 
+/* moe_route plus routing statistics ([Blog] §2.2.2: routing probability
+ * p_{t,e}, dispatch fraction f_e, their per-group sums and the EP-level
+ * balance L_EP over G expert groups; §5.2.3: routing confidence, the
+ * probability mass of the activated experts).  With the unbiased scores s:
+ *   p_{t,e}  = s[t,e] / sum_e' s[t,e']       (normalised over all E experts)
+ *   p_e      = (1/T) sum_t p_{t,e}            f_e = expert_counts[e] / (T k)
+ *   L_EP     = G * sum_g (sum_{e in g} f_e) (sum_{e in g} p_e), the groups
+ *              being ep_groups contiguous blocks of E / G experts
+ *   Sigma_k  = (1/T) sum_t sum_{e in S_t} p_{t,e}
+ * In/out: as moe_route, plus ep_groups (1 <= G <= E, E % G == 0, else
+ * MOE_ERR_INVALID_ARGUMENT).
+ * Out: p_e [E] f32, f_e [E] f32, summary [2] f32 = (L_EP, Sigma_k); all zero
+ *      when T == 0.  Sums are formed in a fixed order (f32 per token, f64
+ *      across tokens): the same inputs give the same bits.  The workspace
+ *      rule is the one of every call.                                       */
+moe_status moe_route_diag(const moe_shape* shape, const uint16_t* x, const uint16_t* w_router, const float* sel_bias,
+                          const float* logit_bias, int32_t* topk_ids, float* topk_weights, int32_t* expert_counts,
+                          float* topk_gap, int32_t ep_groups, float* p_e, float* f_e, float* summary,
+                          void* workspace, size_t ws_bytes, void* stream);
+
 /* Token-to-expert permutation: the gather/scatter order of the grouped
  * expert GEMMs ([Blog] §3.2.4: fused MoE gather/scatter with grouped GEMM).
  * Pair p = t*k + j is token t's j-th chosen expert.
@@ -175,6 +199,24 @@ moe_status moe_shared_swiglu(const moe_shape* shape, const uint16_t* x, const ui
 moe_status moe_combine(const moe_shape* shape, const uint16_t* y_perm, const int32_t* pair_pos,
                        const float* topk_weights, const float* y_shared, float routed_scale, uint16_t* y,
                        void* stream);
+
+/* moe_combine plus the per-expert activation RMS ([Blog] §4.1.2: monitor
+ * per-expert activation norms; §4.1.3, Figure 4: maximum against median
+ * expert output norm; [Digest] expert collapse: min-to-median ratio):
+ *   expert_rms[e] = sqrt(mean of y_perm[r,i]^2 over the rows r of expert e
+ *                   and all i), 0 for an expert with no rows;
+ *   expert_rms[E] = the same over y_shared (0 when y_shared is NULL);
+ *   rms_ratio     = (min_e, max_e) expert_rms[e] / median_e expert_rms[e]
+ *                   over the routed experts with at least one row (median
+ *                   of an even count: mean of the two middle values);
+ *                   (0, 0) when there is none or the median is 0.
+ * In/out: as moe_combine, plus expert_offsets [E+1] int32 (moe_permute's),
+ * expert_rms [E+1] f32 out, rms_ratio [2] f32 out or NULL, and the
+ * workspace (the rule of every call).  y is bit-identical to moe_combine's.  */
+moe_status moe_combine_diag(const moe_shape* shape, const uint16_t* y_perm, const int32_t* pair_pos,
+                            const float* topk_weights, const float* y_shared, float routed_scale, uint16_t* y,
+                            const int32_t* expert_offsets, float* expert_rms, float* rms_ratio, void* workspace,
+                            size_t ws_bytes, void* stream);
 
 /* Zero-centred RMSNorm of bf16 rows ([Blog] §2.2, Figure 2 caption; the
  * [Digest] notes the pre-norm placement):

@@ -11,14 +11,14 @@ tensors one forward pass needs with torch and calls the entry points in order.
 from dataclasses import dataclass
 from typing import Optional
 
-from ._lib import (EXPORTS, LIB_PATH, MoeError, lib, make_shape, moe_check_shape, moe_combine, moe_expert_down,
-                   moe_expert_gate_up, moe_expert_swiglu, moe_permute, moe_rmsnorm, moe_route, moe_shape,
-                   moe_shared_swiglu, moe_status_str, moe_workspace_bytes)
+from ._lib import (EXPORTS, LIB_PATH, MoeError, lib, make_shape, moe_check_shape, moe_combine, moe_combine_diag,
+                   moe_expert_down, moe_expert_gate_up, moe_expert_swiglu, moe_permute, moe_rmsnorm, moe_route,
+                   moe_route_diag, moe_shape, moe_shared_swiglu, moe_status_str, moe_workspace_bytes)
 
 __all__ = [
-    "EXPORTS", "LIB_PATH", "MoeError", "lib", "make_shape", "moe_check_shape", "moe_combine", "moe_expert_down",
-    "moe_expert_gate_up", "moe_expert_swiglu", "moe_permute", "moe_rmsnorm", "moe_route", "moe_shape",
-    "moe_shared_swiglu", "moe_status_str", "moe_workspace_bytes", "LayerBuffers",
+    "EXPORTS", "LIB_PATH", "MoeError", "lib", "make_shape", "moe_check_shape", "moe_combine", "moe_combine_diag",
+    "moe_expert_down", "moe_expert_gate_up", "moe_expert_swiglu", "moe_permute", "moe_rmsnorm", "moe_route",
+    "moe_route_diag", "moe_shape", "moe_shared_swiglu", "moe_status_str", "moe_workspace_bytes", "LayerBuffers",
 ]
 
 
@@ -41,6 +41,11 @@ class LayerBuffers:
     y: "object"
     workspace: "object"
     workspace_shared: "object"
+    p_e: "object" = None            # diagnostics (forward with diag_groups)
+    f_e: "object" = None
+    route_summary: "object" = None  # (L_EP, routing confidence)
+    expert_rms: "object" = None     # [E+1], entry E the shared expert
+    rms_ratio: "object" = None      # (min, max) / median expert RMS
 
     @staticmethod
     def allocate(T, d, E, k, h, hs, device="cuda"):
@@ -63,16 +68,25 @@ class LayerBuffers:
             y=torch.empty((T, d), dtype=bf16, device=dev),
             workspace=torch.empty((nb,), dtype=torch.uint8, device=dev),
             workspace_shared=torch.empty((nb,), dtype=torch.uint8, device=dev),
+            p_e=torch.empty((E,), dtype=f32, device=dev),
+            f_e=torch.empty((E,), dtype=f32, device=dev),
+            route_summary=torch.empty((2,), dtype=f32, device=dev),
+            expert_rms=torch.empty((E + 1,), dtype=f32, device=dev),
+            rms_ratio=torch.empty((2,), dtype=f32, device=dev),
         )
 
     def forward(self, x, w_router, sel_bias, logit_bias, w_gate_up, w_down, ws_gate_up=None, ws_down=None,
-                routed_scale=1.0, stream=None, shared="fused", shared_stream=None):
+                routed_scale=1.0, stream=None, shared="fused", shared_stream=None, diag_groups=None):
         """route -> permute -> experts -> combine, enqueued on `stream`
         (default: current).  The shared expert runs
           "fused":  as one more group inside the grouped expert launches;
           "stream": as moe_shared_swiglu on `shared_stream`, concurrently,
                     joined before the combine;
-          "serial": as moe_shared_swiglu on `stream` after the experts."""
+          "serial": as moe_shared_swiglu on `stream` after the experts.
+        diag_groups = G: route and combine through moe_route_diag and
+        moe_combine_diag, filling p_e, f_e, route_summary (L_EP over G
+        contiguous expert groups, routing confidence), expert_rms and
+        rms_ratio; y is the same either way."""
         import torch
         s = stream if stream is not None else torch.cuda.current_stream()
         sh = self.shape
@@ -80,8 +94,13 @@ class LayerBuffers:
         if use_shared and shared == "stream":
             shared_stream.wait_stream(s)
             moe_shared_swiglu(sh, x, ws_gate_up, ws_down, self.y_shared, self.workspace_shared, shared_stream)
-        moe_route(sh, x, w_router, sel_bias, logit_bias, self.topk_ids, self.topk_weights, self.expert_counts,
-                  self.topk_gap, self.workspace, s)
+        if diag_groups is not None:
+            moe_route_diag(sh, x, w_router, sel_bias, logit_bias, self.topk_ids, self.topk_weights,
+                           self.expert_counts, self.topk_gap, diag_groups, self.p_e, self.f_e, self.route_summary,
+                           self.workspace, s)
+        else:
+            moe_route(sh, x, w_router, sel_bias, logit_bias, self.topk_ids, self.topk_weights, self.expert_counts,
+                      self.topk_gap, self.workspace, s)
         moe_permute(sh, self.topk_ids, self.expert_offsets, self.perm_pairs, self.pair_pos, self.workspace, s)
         fused = use_shared and shared == "fused"
         moe_expert_swiglu(sh, x, self.expert_offsets, self.perm_pairs, w_gate_up, w_down, self.y_perm,
@@ -91,6 +110,10 @@ class LayerBuffers:
             moe_shared_swiglu(sh, x, ws_gate_up, ws_down, self.y_shared, self.workspace, s)
         if use_shared and shared == "stream":
             s.wait_stream(shared_stream)
-        moe_combine(sh, self.y_perm, self.pair_pos, self.topk_weights, self.y_shared if use_shared else None,
-                    routed_scale, self.y, s)
+        y_shared = self.y_shared if use_shared else None
+        if diag_groups is not None:
+            moe_combine_diag(sh, self.y_perm, self.pair_pos, self.topk_weights, y_shared, routed_scale, self.y,
+                             self.expert_offsets, self.expert_rms, self.rms_ratio, self.workspace, s)
+        else:
+            moe_combine(sh, self.y_perm, self.pair_pos, self.topk_weights, y_shared, routed_scale, self.y, s)
         return self.y

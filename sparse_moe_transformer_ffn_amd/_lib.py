@@ -23,7 +23,8 @@ STATUS = {
 
 EXPORTS = (
     "moe_status_str", "moe_check_shape", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_swiglu",
-    "moe_expert_gate_up", "moe_expert_down", "moe_shared_swiglu", "moe_combine", "moe_rmsnorm",
+    "moe_expert_gate_up", "moe_expert_down", "moe_shared_swiglu", "moe_combine", "moe_rmsnorm", "moe_route_diag",
+    "moe_combine_diag",
 )
 
 
@@ -62,6 +63,10 @@ def lib():
         L.moe_shared_swiglu.argtypes = [_SP, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_combine.argtypes = [_SP, _P, _P, _P, _P, ctypes.c_float, _P, _P]
         L.moe_rmsnorm.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_float, _P, _P]
+        L.moe_route_diag.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P,
+                                     ctypes.c_size_t, _P]
+        L.moe_combine_diag.argtypes = [_SP, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                       _P]
         for name in EXPORTS[1:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -165,3 +170,21 @@ def moe_combine(shape, y_perm, pair_pos, topk_weights, y_shared, routed_scale, y
 def moe_rmsnorm(rows, cols, inp, gamma, eps, out, stream=None):
     _check("moe_rmsnorm", lib().moe_rmsnorm(int(rows), int(cols), _ptr(inp), _ptr(gamma), float(eps), _ptr(out),
                                             _stream(stream)))
+
+
+def moe_route_diag(shape, x, w_router, sel_bias, logit_bias, topk_ids, topk_weights, expert_counts, topk_gap,
+                   ep_groups, p_e, f_e, summary, workspace, stream=None):
+    ws, nb = _ws(workspace)
+    _check("moe_route_diag", lib().moe_route_diag(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(sel_bias),
+                                                  _ptr(logit_bias), _ptr(topk_ids), _ptr(topk_weights),
+                                                  _ptr(expert_counts), _ptr(topk_gap), int(ep_groups), _ptr(p_e),
+                                                  _ptr(f_e), _ptr(summary), ws, nb, _stream(stream)))
+
+
+def moe_combine_diag(shape, y_perm, pair_pos, topk_weights, y_shared, routed_scale, y, expert_offsets, expert_rms,
+                     rms_ratio, workspace, stream=None):
+    ws, nb = _ws(workspace)
+    _check("moe_combine_diag", lib().moe_combine_diag(ctypes.byref(shape), _ptr(y_perm), _ptr(pair_pos),
+                                                      _ptr(topk_weights), _ptr(y_shared), float(routed_scale),
+                                                      _ptr(y), _ptr(expert_offsets), _ptr(expert_rms),
+                                                      _ptr(rms_ratio), ws, nb, _stream(stream)))

@@ -40,6 +40,7 @@ size_t workspace_bytes(const moe_shape* s) {
   b = b > moe::permute_workspace_bytes(T, E) ? b : moe::permute_workspace_bytes(T, E);
   const size_t experts = moe::expert_hid_bytes(T, k, h) + moe::shared_hid_bytes(T, s->d_shared) + moe::kQueueBytes;
   b = b > experts ? b : experts;
+  b = b > moe::combine_diag_workspace_bytes(T, k) ? b : moe::combine_diag_workspace_bytes(T, k);
   return round256(b > 256 ? b : 256);
 }
 
@@ -91,7 +92,28 @@ moe_status moe_route(const moe_shape* shape, const uint16_t* x, const uint16_t* 
   if ((st = check_workspace(shape, workspace, ws_bytes)) != MOE_OK) return st;
   return hip_status(moe::launch_route(shape->num_tokens, shape->d_model, shape->num_experts, shape->top_k, x,
                                       w_router, sel_bias, logit_bias, topk_ids, topk_weights, expert_counts,
-                                      topk_gap, workspace, (hipStream_t)stream));
+                                      topk_gap, nullptr, workspace, (hipStream_t)stream));
+}
+
+moe_status moe_route_diag(const moe_shape* shape, const uint16_t* x, const uint16_t* w_router, const float* sel_bias,
+                          const float* logit_bias, int32_t* topk_ids, float* topk_weights, int32_t* expert_counts,
+                          float* topk_gap, int32_t ep_groups, float* p_e, float* f_e, float* summary,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!x || !w_router || !sel_bias || !topk_ids || !topk_weights || !expert_counts || !p_e || !f_e || !summary)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (ep_groups < 1 || ep_groups > shape->num_experts || shape->num_experts % ep_groups != 0)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned4(sel_bias) || !aligned4(topk_ids) ||
+      !aligned4(topk_weights) || !aligned4(expert_counts) || (logit_bias && !aligned4(logit_bias)) ||
+      (topk_gap && !aligned4(topk_gap)) || !aligned4(p_e) || !aligned4(f_e) || !aligned4(summary))
+    return MOE_ERR_MISALIGNED;
+  if ((st = check_workspace(shape, workspace, ws_bytes)) != MOE_OK) return st;
+  const moe::RouteDiag diag{ep_groups, p_e, f_e, summary};
+  return hip_status(moe::launch_route(shape->num_tokens, shape->d_model, shape->num_experts, shape->top_k, x,
+                                      w_router, sel_bias, logit_bias, topk_ids, topk_weights, expert_counts,
+                                      topk_gap, &diag, workspace, (hipStream_t)stream));
 }
 
 moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t* expert_offsets,
@@ -215,7 +237,27 @@ moe_status moe_combine(const moe_shape* shape, const uint16_t* y_perm, const int
       (y_shared && !aligned16(y_shared)))
     return MOE_ERR_MISALIGNED;
   return hip_status(moe::launch_combine(shape->num_tokens, shape->d_model, shape->top_k, y_perm, pair_pos,
-                                        topk_weights, y_shared, routed_scale, y, (hipStream_t)stream));
+                                        topk_weights, y_shared, routed_scale, y, nullptr, nullptr,
+                                        (hipStream_t)stream));
+}
+
+moe_status moe_combine_diag(const moe_shape* shape, const uint16_t* y_perm, const int32_t* pair_pos,
+                            const float* topk_weights, const float* y_shared, float routed_scale, uint16_t* y,
+                            const int32_t* expert_offsets, float* expert_rms, float* rms_ratio, void* workspace,
+                            size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!y_perm || !pair_pos || !topk_weights || !y || !expert_offsets || !expert_rms) return MOE_ERR_INVALID_ARGUMENT;
+  if (!isfinite(routed_scale)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(y_perm) || !aligned16(y) || !aligned4(pair_pos) || !aligned4(topk_weights) ||
+      (y_shared && !aligned16(y_shared)) || !aligned4(expert_offsets) || !aligned4(expert_rms) ||
+      (rms_ratio && !aligned4(rms_ratio)))
+    return MOE_ERR_MISALIGNED;
+  if ((st = check_workspace(shape, workspace, ws_bytes)) != MOE_OK) return st;
+  const moe::CombineDiag diag{shape->num_experts, expert_offsets, expert_rms, rms_ratio};
+  return hip_status(moe::launch_combine(shape->num_tokens, shape->d_model, shape->top_k, y_perm, pair_pos,
+                                        topk_weights, y_shared, routed_scale, y, &diag, workspace,
+                                        (hipStream_t)stream));
 }
 
 moe_status moe_rmsnorm(int32_t rows, int32_t cols, const uint16_t* in, const float* gamma, float eps, uint16_t* out,

@@ -31,19 +31,30 @@ __device__ __forceinline__ u32x4 pack8(const float* f) {
 // k contributions are summed in slot order (ascending expert id), in f32;
 // the k rows' loads of a step are all issued before the sums, so a step waits
 // on one memory latency rather than k.
+//
+// DIAG: the rows are already in registers, so the block also forms each
+// row's sum of squares (f32: per thread in column order, then a butterfly
+// over the wave and the four waves in order) and stores it by permuted row,
+// row_ss[pair_pos[t*k+j]], and for the shared expert's row, shared_ss[t].
+template <bool DIAG>
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y_perm,
                                                  const int32_t* __restrict__ pair_pos,
                                                  const float* __restrict__ topk_weights,
                                                  const float* __restrict__ y_shared, float routed_scale, int d,
-                                                 int k, uint16_t* __restrict__ y) {
+                                                 int k, uint16_t* __restrict__ y, float* __restrict__ row_ss,
+                                                 float* __restrict__ shared_ss) {
   __shared__ int pos[kMaxTopK];
   __shared__ float wt[kMaxTopK];
+  __shared__ float ss_part[DIAG ? 4 : 1][kMaxTopK + 1];
   const int t = blockIdx.x, tid = threadIdx.x;
   if (tid < k) {
     pos[tid] = pair_pos[(size_t)t * k + tid];
     wt[tid] = topk_weights[(size_t)t * k + tid];
   }
   __syncthreads();
+  float ss[kMaxTopK + 1];
+#pragma unroll
+  for (int j = 0; j <= kMaxTopK; ++j) ss[j] = 0.f;
   for (int c = tid * 8; c < d; c += 256 * 8) {
     u32x4 rows[kMaxTopK];
 #pragma unroll
@@ -63,6 +74,10 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y_
         unpack8(rows[j], v);
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[q] = fmaf(wt[j], v[q], acc[q]);
+        if constexpr (DIAG) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) ss[j] = fmaf(v[q], v[q], ss[j]);
+        }
       }
     }
     float o[8];
@@ -70,11 +85,95 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y_
       const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
       for (int q = 0; q < 8; ++q) o[q] = fmaf(routed_scale, acc[q], sv[q]);
+      if constexpr (DIAG) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) ss[kMaxTopK] = fmaf(sv[q], sv[q], ss[kMaxTopK]);
+      }
     } else {
 #pragma unroll
       for (int q = 0; q < 8; ++q) o[q] = routed_scale * acc[q];
     }
     *reinterpret_cast<u32x4*>(y + (size_t)t * d + c) = pack8(o);
+  }
+  if constexpr (DIAG) {
+    const int wave = tid / kWave, lane = tid % kWave;
+#pragma unroll
+    for (int j = 0; j <= kMaxTopK; ++j) {
+      if (j < k || (j == kMaxTopK && y_shared)) {
+        float v = ss[j];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+        if (lane == 0) ss_part[wave][j < k ? j : k] = v;
+      }
+    }
+    __syncthreads();
+    if (tid <= k) {
+      const float v = (ss_part[0][tid] + ss_part[1][tid]) + (ss_part[2][tid] + ss_part[3][tid]);
+      if (tid < k) row_ss[pos[tid]] = v;
+      else if (y_shared) shared_ss[t] = v;
+    }
+  }
+}
+
+// Per-expert activation RMS from the row sums of squares: wave e adds the
+// rows of expert e (entry E: the shared expert's T rows) in double, in a
+// fixed order, and takes sqrt(sum / (rows * d)); no rows gives 0.
+__global__ __launch_bounds__(64) void k_expert_rms(const float* __restrict__ row_ss,
+                                                   const float* __restrict__ shared_ss,
+                                                   const int32_t* __restrict__ offsets, int T, int E, int d,
+                                                   float* __restrict__ rms) {
+  const int e = blockIdx.x, lane = threadIdx.x;
+  const float* src;
+  int n;
+  if (e < E) {
+    src = row_ss + offsets[e];
+    n = offsets[e + 1] - offsets[e];
+  } else {
+    src = shared_ss;
+    n = shared_ss ? T : 0;
+  }
+  double s = 0.0;
+  for (int r = lane; r < n; r += kWave) s += (double)src[r];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  if (lane == 0) rms[e] = n > 0 ? (float)sqrt(s / ((double)n * d)) : 0.f;
+}
+
+// Spread of the routed experts' RMS ([Blog] §4.1.3, Figure 4: maximum against
+// median expert output norm; [Digest] expert collapse: min against median):
+// over the experts that received rows, ratio = (min, max) / median, the
+// median of an even count being the mean of the two middle values.  No such
+// expert, or a zero median, gives (0, 0).  One block; order statistics by
+// rank counting (ties broken by expert index).
+__global__ __launch_bounds__(1024) void k_rms_ratio(const float* __restrict__ rms,
+                                                    const int32_t* __restrict__ offsets, int E,
+                                                    float* __restrict__ ratio) {
+  __shared__ float val[1024];
+  __shared__ int used[1024];
+  __shared__ float sorted[1024];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 1024) {
+    used[e] = offsets[e + 1] > offsets[e];
+    val[e] = rms[e];
+  }
+  __syncthreads();
+  int m = 0;
+  for (int e = 0; e < E; ++e) m += used[e];
+  for (int e = tid; e < E; e += 1024) {
+    if (!used[e]) continue;
+    int rank = 0;
+    for (int j = 0; j < E; ++j) rank += used[j] && (val[j] < val[e] || (val[j] == val[e] && j < e));
+    sorted[rank] = val[e];
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const double med = m == 0 ? 0.0 : 0.5 * ((double)sorted[(m - 1) / 2] + (double)sorted[m / 2]);
+    if (m == 0 || !(med > 0.0)) {
+      ratio[0] = ratio[1] = 0.f;
+    } else {
+      ratio[0] = (float)((double)sorted[0] / med);
+      ratio[1] = (float)((double)sorted[m - 1] / med);
+    }
   }
 }
 
@@ -108,12 +207,34 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const uint16_t* __restrict__ in
 
 hipError_t launch_combine(int T, int d, int k, const uint16_t* y_perm, const int32_t* pair_pos,
                           const float* topk_weights, const float* y_shared, float routed_scale, uint16_t* y,
-                          hipStream_t stream) {
-  if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, stream, y_perm, pair_pos, topk_weights, y_shared,
-                     routed_scale, d, k, y);
-  return hipGetLastError();
+                          const CombineDiag* diag, void* workspace, hipStream_t stream) {
+  if (!diag) {
+    if (T == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_combine<false>, dim3(T), dim3(256), 0, stream, y_perm, pair_pos, topk_weights, y_shared,
+                       routed_scale, d, k, y, nullptr, nullptr);
+    return hipGetLastError();
+  }
+  float* row_ss = static_cast<float*>(workspace);
+  float* shared_ss = y_shared ? row_ss + (size_t)T * k : nullptr;
+  hipError_t err;
+  if (T > 0) {
+    hipLaunchKernelGGL(k_combine<true>, dim3(T), dim3(256), 0, stream, y_perm, pair_pos, topk_weights, y_shared,
+                       routed_scale, d, k, y, row_ss, shared_ss);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(k_expert_rms, dim3(diag->E + 1), dim3(64), 0, stream, row_ss, shared_ss, diag->offsets, T,
+                     diag->E, d, diag->rms);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (diag->ratio) {
+    hipLaunchKernelGGL(k_rms_ratio, dim3(1), dim3(1024), 0, stream, diag->rms, diag->offsets, diag->E,
+                       diag->ratio);
+    err = hipGetLastError();
+  }
+  return err;
 }
+
+// Row sums of squares: T*k routed rows, then T shared rows.
+size_t combine_diag_workspace_bytes(int T, int k) { return (size_t)T * (k + 1) * sizeof(float); }
 
 hipError_t launch_rmsnorm(int rows, int cols, const uint16_t* in, const float* gamma, float eps, uint16_t* out,
                           hipStream_t stream) {

@@ -18,9 +18,19 @@ struct RouteSplit {
 };
 RouteSplit route_split(int T, int d, int E);
 
+// Routing diagnostics produced beside the routing outputs: p_e [E], f_e [E]
+// and summary [2] = (L_EP over `groups` contiguous expert groups, routing
+// confidence).
+struct RouteDiag {
+  int groups;
+  float* p_e;
+  float* f_e;
+  float* summary;
+};
 hipError_t launch_route(int T, int d, int E, int k, const uint16_t* x, const uint16_t* w_router,
                         const float* sel_bias, const float* logit_bias, int32_t* topk_ids, float* topk_weights,
-                        int32_t* counts, float* topk_gap, void* workspace, hipStream_t stream);
+                        int32_t* counts, float* topk_gap, const RouteDiag* diag, void* workspace,
+                        hipStream_t stream);
 size_t route_workspace_bytes(int T, int d, int E);
 
 hipError_t launch_permute(int T, int E, int k, const int32_t* topk_ids, int32_t* expert_offsets,
@@ -49,9 +59,19 @@ hipError_t launch_down_tiled(int T, int d, int E, int k, int h, int hs, const in
 size_t expert_hid_bytes(int T, int k, int h);
 size_t shared_hid_bytes(int T, int hs);
 
+// Per-expert activation RMS produced by the combine: rms [E+1] (entry E:
+// the shared expert) and, if non-NULL, ratio [2] = (min, max) / median over
+// the routed experts that received rows.  Uses combine_diag_workspace_bytes.
+struct CombineDiag {
+  int E;
+  const int32_t* offsets;
+  float* rms;
+  float* ratio;
+};
 hipError_t launch_combine(int T, int d, int k, const uint16_t* y_perm, const int32_t* pair_pos,
                           const float* topk_weights, const float* y_shared, float routed_scale, uint16_t* y,
-                          hipStream_t stream);
+                          const CombineDiag* diag, void* workspace, hipStream_t stream);
+size_t combine_diag_workspace_bytes(int T, int k);
 hipError_t launch_rmsnorm(int rows, int cols, const uint16_t* in, const float* gamma, float eps, uint16_t* out,
                           hipStream_t stream);
 

@@ -251,19 +251,29 @@ __device__ __forceinline__ uint32_t kth_largest(const uint32_t (&key)[EPL], int 
 // to it, the lowest indices.  A block of four waves aggregates the expert
 // histogram of its 4 * tpw tokens in LDS before one global atomic add per
 // touched expert (integer atomics: order-independent).
-template <int EPL>
+//
+// DIAG: also the routing probabilities p_{t,e} = s_{t,e} / sum_e' s_{t,e'}
+// ([Blog] §2.2.2) summed over the wave's tokens, and the probability mass of
+// each token's chosen set ([Blog] §5.2.3, routing confidence), written as
+// wave partials diag[e * nw + w] (row E: the mass) for w < nw = ceil(T/tpw);
+// fixed summation order, so the result is deterministic.
+template <int EPL, bool DIAG>
 __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ partial, int ksplit, int T, int E,
                                                       int k, int tpw, const float* __restrict__ sel_bias,
                                                       const float* __restrict__ logit_bias,
                                                       int32_t* __restrict__ topk_ids,
                                                       float* __restrict__ topk_weights, float* __restrict__ topk_gap,
-                                                      int32_t* __restrict__ counts) {
+                                                      int32_t* __restrict__ counts, float* __restrict__ diag,
+                                                      int nw) {
   __shared__ int hist[1024];
   __shared__ float chosen_s[4][16];
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += 256) hist[e] = 0;
   __syncthreads();
   const int wave = tid / kWave, lane = tid % kWave;
+  float p_acc[EPL], mass_acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) p_acc[j] = 0.f;
   for (int tw = 0; tw < tpw; ++tw) {  // wave-uniform; no block barrier inside
     const int t = (blockIdx.x * 4 + wave) * tpw + tw;
     if (t >= T) break;
@@ -346,6 +356,17 @@ __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     float total = 0.f;
     for (int q = 0; q < k; ++q) total += chosen_s[wave][q];
+    if constexpr (DIAG) {
+      // Butterfly sum: every lane ends with the same bits.
+      float all = 0.f;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) all += score[j];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) all += __shfl_xor(all, off);
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) p_acc[j] += score[j] / all;
+      mass_acc += total / all;
+    }
     before = 0;
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
@@ -361,9 +382,74 @@ __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ 
     if (lane == 0 && topk_gap) topk_gap[t] = gap;
     __builtin_amdgcn_wave_barrier();  // chosen_s is reused by the next token
   }
+  if constexpr (DIAG) {
+    const int w = blockIdx.x * 4 + wave;
+    if (w < nw) {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if (lane + kWave * j < E) diag[(size_t)(lane + kWave * j) * nw + w] = p_acc[j];
+      if (lane == 0) diag[(size_t)E * nw + w] = mass_acc;
+    }
+  }
   __syncthreads();
   for (int e = tid; e < E; e += 256)
     if (hist[e]) atomicAdd(&counts[e], hist[e]);
+}
+
+// Column sums of the wave partials: block e adds diag[e * nw + w] over w in
+// a fixed order (thread-strided, then a tree), in double.
+__global__ __launch_bounds__(256) void k_diag_columns(const float* __restrict__ diag, int nw,
+                                                      double* __restrict__ col) {
+  __shared__ double red[256];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  double s = 0.0;
+  for (int w = tid; w < nw; w += 256) s += (double)diag[(size_t)e * nw + w];
+  red[tid] = s;
+  __syncthreads();
+  for (int half = 128; half >= 1; half >>= 1) {
+    if (tid < half) red[tid] += red[tid + half];
+    __syncthreads();
+  }
+  if (tid == 0) col[e] = red[0];
+}
+
+// p_e = (sum_t p_{t,e}) / T, f_e = counts_e / (T k); over G contiguous groups
+// of E/G experts, L_EP = G * sum_g f_g p_g ([Blog] §2.2.2); confidence =
+// (sum_t mass_t) / T ([Blog] §5.2.3).  T = 0 writes zeros.  One block.
+__global__ __launch_bounds__(256) void k_diag_finish(const double* __restrict__ col,
+                                                     const int32_t* __restrict__ counts, int T, int E, int k, int G,
+                                                     float* __restrict__ p_e, float* __restrict__ f_e,
+                                                     float* __restrict__ summary) {
+  __shared__ double pd[1024], fd[1024], prod[1024];
+  const int tid = threadIdx.x;
+  if (T == 0) {
+    for (int e = tid; e < E; e += 256) p_e[e] = f_e[e] = 0.f;
+    if (tid == 0) summary[0] = summary[1] = 0.f;
+    return;
+  }
+  for (int e = tid; e < E; e += 256) {
+    pd[e] = col[e] / (double)T;
+    fd[e] = (double)counts[e] / ((double)T * k);
+    p_e[e] = (float)pd[e];
+    f_e[e] = (float)fd[e];
+  }
+  __syncthreads();
+  const int per = E / G;
+  for (int g = tid; g < G; g += 256) {
+    double pg = 0.0, fg = 0.0;
+    for (int e = g * per; e < (g + 1) * per; ++e) {
+      pg += pd[e];
+      fg += fd[e];
+    }
+    prod[g] = fg * pg;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double l = 0.0;
+    for (int g = 0; g < G; ++g) l += prod[g];
+    summary[0] = (float)(G * l);
+    summary[1] = (float)(col[E] / (double)T);
+  }
 }
 
 __global__ void k_zero_i32(int32_t* p, int n) {
@@ -396,11 +482,30 @@ RouteSplit route_split(int T, int d, int E) {
   return RouteSplit{ks, kchunk, false};
 }
 
+namespace {
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+// Tokens per wave of the selection kernel: one for small batches (latency),
+// four for large ones, so each block's expert histogram covers 16 tokens and
+// the global count atomics drop fourfold.
+int select_tpw(int T) { return T >= 2048 ? 4 : 1; }
+
+size_t logits_bytes(int T, int d, int E) {
+  return round256((size_t)route_split(T, d, E).ksplit * (size_t)T * (size_t)E * sizeof(float));
+}
+
+}  // namespace
+
 hipError_t launch_route(int T, int d, int E, int k, const uint16_t* x, const uint16_t* w_router,
                         const float* sel_bias, const float* logit_bias, int32_t* topk_ids, float* topk_weights,
-                        int32_t* counts, float* topk_gap, void* workspace, hipStream_t stream) {
+                        int32_t* counts, float* topk_gap, const RouteDiag* diag, void* workspace,
+                        hipStream_t stream) {
   if (T == 0) {
     hipLaunchKernelGGL(k_zero_i32, dim3((E + 255) / 256), dim3(256), 0, stream, counts, E);
+    if (diag)
+      hipLaunchKernelGGL(k_diag_finish, dim3(1), dim3(256), 0, stream, nullptr, counts, 0, E, k, diag->groups,
+                         diag->p_e, diag->f_e, diag->summary);
     return hipGetLastError();
   }
   const RouteSplit rs = route_split(T, d, E);
@@ -413,15 +518,22 @@ hipError_t launch_route(int T, int d, int E, int k, const uint16_t* x, const uin
                        w_router, T, d, E, rs.kchunk, partial, counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // Tokens per wave: one for small batches (latency), four for large ones,
-  // so each block's expert histogram covers 16 tokens and the global count
-  // atomics drop fourfold.
-  const int tpw = T >= 2048 ? 4 : 1;
+  const int tpw = select_tpw(T);
+  const int nw = (T + tpw - 1) / tpw;
+  char* diag_base = static_cast<char*>(workspace) + logits_bytes(T, d, E);
+  float* wave_part = reinterpret_cast<float*>(diag_base);
+  double* col = reinterpret_cast<double*>(diag_base + round256((size_t)(E + 1) * nw * sizeof(float)));
   const dim3 grid((T + 4 * tpw - 1) / (4 * tpw)), block(256);
   const int epl = (E + 63) / 64;
-#define MOE_SELECT(N)                                                                                             \
-  hipLaunchKernelGGL(k_route_select<N>, grid, block, 0, stream, partial, rs.ksplit, T, E, k, tpw, sel_bias, logit_bias, \
-                     topk_ids, topk_weights, topk_gap, counts)
+#define MOE_SELECT(N)                                                                                          \
+  do {                                                                                                         \
+    if (diag)                                                                                                  \
+      hipLaunchKernelGGL((k_route_select<N, true>), grid, block, 0, stream, partial, rs.ksplit, T, E, k, tpw,  \
+                         sel_bias, logit_bias, topk_ids, topk_weights, topk_gap, counts, wave_part, nw);       \
+    else                                                                                                       \
+      hipLaunchKernelGGL((k_route_select<N, false>), grid, block, 0, stream, partial, rs.ksplit, T, E, k, tpw, \
+                         sel_bias, logit_bias, topk_ids, topk_weights, topk_gap, counts, nullptr, 0);          \
+  } while (0)
   if (epl <= 1) MOE_SELECT(1);
   else if (epl <= 2) MOE_SELECT(2);
   else if (epl <= 4) MOE_SELECT(4);
@@ -429,12 +541,22 @@ hipError_t launch_route(int T, int d, int E, int k, const uint16_t* x, const uin
   else if (epl <= 8) MOE_SELECT(8);
   else MOE_SELECT(16);
 #undef MOE_SELECT
+  if (!diag) return hipGetLastError();
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(k_diag_columns, dim3(E + 1), dim3(256), 0, stream, wave_part, nw, col);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(k_diag_finish, dim3(1), dim3(256), 0, stream, col, counts, T, E, k, diag->groups, diag->p_e,
+                     diag->f_e, diag->summary);
   return hipGetLastError();
 }
 
+// Logits partials, then (for the diagnostics) the wave partials [E+1][nw] f32
+// and the column sums [E+1] f64.
 size_t route_workspace_bytes(int T, int d, int E) {
-  const RouteSplit rs = route_split(T, d, E);
-  return (size_t)rs.ksplit * (size_t)T * (size_t)E * sizeof(float);
+  const int tpw = select_tpw(T);
+  const size_t nw = (size_t)(T + tpw - 1) / tpw;
+  return logits_bytes(T, d, E) + round256((size_t)(E + 1) * nw * sizeof(float)) +
+         round256((size_t)(E + 1) * sizeof(double));
 }
 
 }  // namespace moe

@@ -74,9 +74,10 @@ class DeviceLayer:
         c = self.cfg
         return moe.LayerBuffers.allocate(c.T if T is None else T, c.d, c.E, c.k, c.h, c.hs)
 
-    def forward(self, buf, shared="fused", shared_stream=None):
+    def forward(self, buf, shared="fused", shared_stream=None, diag_groups=None):
         return buf.forward(self.x, self.wr, self.b, self.c, self.w_gu, self.w_d, self.ws_gu, self.ws_d,
-                           self.cfg.routed_scale, shared=shared, shared_stream=shared_stream)
+                           self.cfg.routed_scale, shared=shared, shared_stream=shared_stream,
+                           diag_groups=diag_groups)
 
 
 def pool_size():

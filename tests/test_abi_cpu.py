@@ -168,3 +168,43 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros((64, 256), dtype=torch.uint16)
     with pytest.raises(ValueError):
         moe.moe_rmsnorm(64, 256, x, None, 1e-6, x.clone())
+
+
+def test_route_diag_validation():
+    s = shape(1)
+    L = moe.lib()
+    nb = moe.moe_workspace_bytes(s)
+
+    def call(G=8, p=A, f=A, summ=A, x=A, ws=A, nbytes=nb, shp=s):
+        # moe_route_diag(shape, x, w, b, c, ids, wts, cnt, gap, G, p_e, f_e, summary, ws, nb, stream)
+        return L.moe_route_diag(ctypes.byref(shp), x, A, A, None, A, A, A, None, G, p, f, summ, ws, nbytes, None)
+
+    for G in (0, -1, 7, 289, 576):
+        assert call(G=G) == INVALID, G
+    for kw in ({"p": None}, {"f": None}, {"summ": None}, {"x": None}, {"ws": None}):
+        assert call(**kw) == INVALID, kw
+    assert call(p=A + 2) == MISALIGNED
+    assert call(summ=A + 1) == MISALIGNED
+    assert call(x=MIS) == MISALIGNED
+    assert call(nbytes=nb - 256) == WS_SMALL
+    assert call(shp=shape(1, top_k=0)) == UNSUPPORTED
+
+
+def test_combine_diag_validation():
+    s = shape(1)
+    L = moe.lib()
+    nb = moe.moe_workspace_bytes(s)
+    one = ctypes.c_float(1.0)
+
+    def call(off=A, rms=A, ratio=A, scale=one, ysh=A, ws=A, nbytes=nb):
+        # moe_combine_diag(shape, y_perm, pos, wts, y_shared, scale, y, offsets, rms, ratio, ws, nb, stream)
+        return L.moe_combine_diag(ctypes.byref(s), A, A, A, ysh, scale, A + 4096, off, rms, ratio, ws, nbytes, None)
+
+    assert call(off=None) == INVALID
+    assert call(rms=None) == INVALID
+    assert call(ws=None) == INVALID
+    assert call(scale=ctypes.c_float(float("nan"))) == INVALID
+    assert call(off=A + 2) == MISALIGNED
+    assert call(ratio=A + 1) == MISALIGNED
+    assert call(ysh=A + 4) == MISALIGNED
+    assert call(nbytes=16) == WS_SMALL

@@ -85,6 +85,49 @@ def test_layer_is_deterministic(device, idx):
     np.testing.assert_array_equal(bf16_host(s1.y), bf16_host(s2.y))
 
 
+@pytest.mark.parametrize("idx", [1, 2])
+def test_layer_diagnostic_side_outputs(device, idx):
+    # The layer with the diagnostic calls, at the benchmark's sizes: the same
+    # routing and output bits as without, and statistics consistent with the
+    # GPU's own routing and expert outputs (per-call parity against the oracle
+    # is tested separately, on generator inputs).
+    cfg = moegen.CONFIGS[idx]
+    T, E, k, G = cfg.T, cfg.E, cfg.k, 8
+    log(f"[layer-diag] config {idx}: {cfg.workload}")
+    dl = DeviceLayer(cfg)
+    plain = run_layer(dl)
+    y0, ids0 = bf16_host(plain.y).copy(), plain.topk_ids.cpu().numpy().copy()
+    del plain
+    buf = dl.buffers()
+    dl.forward(buf, diag_groups=G)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(buf.topk_ids.cpu().numpy(), ids0)
+    np.testing.assert_array_equal(bf16_host(buf.y), y0)
+    cnt = buf.expert_counts.cpu().numpy()
+    p_e, f_e = buf.p_e.cpu().numpy(), buf.f_e.cpu().numpy()
+    l_ep, conf = (float(v) for v in buf.route_summary.cpu().numpy())
+    rms, ratio = buf.expert_rms.cpu().numpy(), buf.rms_ratio.cpu().numpy()
+    log(f"  L_EP {l_ep:.5f} confidence {conf:.5f} rms ratio {ratio}")
+    np.testing.assert_array_equal(f_e, (cnt / (T * k)).astype(np.float32))
+    assert abs(p_e.astype(np.float64).sum() - 1.0) < 1e-5
+    pg = p_e.astype(np.float64).reshape(G, -1).sum(1)
+    fg = f_e.astype(np.float64).reshape(G, -1).sum(1)
+    assert l_ep == pytest.approx(G * float((pg * fg).sum()), rel=1e-5)
+    assert 0.0 < conf < 1.0
+    np.testing.assert_array_equal(rms[:E] > 0, cnt > 0)
+    off = buf.expert_offsets.cpu().numpy()
+    # Sampled experts: the busiest, a median one and the least busy used one.
+    used = np.where(cnt > 0)[0]
+    order = used[np.argsort(cnt[used], kind="stable")]
+    for e in (order[-1], order[len(order) // 2], order[0]):
+        rows = moegen.bf16_to_f32(bf16_host(buf.y_perm[off[e]:off[e + 1]])).astype(np.float64)
+        assert rms[e] == pytest.approx(np.sqrt(np.mean(rows ** 2)), rel=1e-5)
+    ysh = buf.y_shared.cpu().numpy().astype(np.float64)
+    assert rms[E] == pytest.approx(np.sqrt(np.mean(ysh ** 2)), rel=1e-5)
+    med = np.median(rms[used].astype(np.float64))
+    np.testing.assert_allclose(ratio, [rms[used].min() / med, rms[used].max() / med], rtol=1e-6)
+
+
 @pytest.mark.parametrize("T,k,hs,scale", [(1, 8, 1280, 1.0), (3, 1, 1280, 1.0), (97, 8, 0, 0.5), (130, 8, 1280, 2.0)])
 def test_layer_edge_shapes(device, T, k, hs, scale):
     cfg = moegen.custom(1, T=T, k=k, hs=hs, routed_scale=scale, seed=500 + T)
