@@ -30,35 +30,36 @@ __device__ __forceinline__ u32x4 pack8(const float* f) {
 // One block per token; each thread owns 8 consecutive columns per step.  The
 // k contributions are summed in slot order (ascending expert id), in f32;
 // the k rows' loads of a step are all issued before the sums, so a step waits
-// on one memory latency rather than k.
+// on one memory latency rather than k.  KMAX >= k bounds the rows held in
+// registers (8 or kMaxTopK), which sets the occupancy.
 //
 // DIAG: the rows are already in registers, so the block also forms each
 // row's sum of squares (f32: per thread in column order, then a butterfly
 // over the wave and the four waves in order) and stores it by permuted row,
 // row_ss[pair_pos[t*k+j]], and for the shared expert's row, shared_ss[t].
-template <bool DIAG>
+template <int KMAX, bool DIAG>
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y_perm,
                                                  const int32_t* __restrict__ pair_pos,
                                                  const float* __restrict__ topk_weights,
                                                  const float* __restrict__ y_shared, float routed_scale, int d,
                                                  int k, uint16_t* __restrict__ y, float* __restrict__ row_ss,
                                                  float* __restrict__ shared_ss) {
-  __shared__ int pos[kMaxTopK];
-  __shared__ float wt[kMaxTopK];
-  __shared__ float ss_part[DIAG ? 4 : 1][kMaxTopK + 1];
+  __shared__ int pos[KMAX];
+  __shared__ float wt[KMAX];
+  __shared__ float ss_part[DIAG ? 4 : 1][KMAX + 1];
   const int t = blockIdx.x, tid = threadIdx.x;
   if (tid < k) {
     pos[tid] = pair_pos[(size_t)t * k + tid];
     wt[tid] = topk_weights[(size_t)t * k + tid];
   }
   __syncthreads();
-  float ss[kMaxTopK + 1];
+  float ss[KMAX + 1];
 #pragma unroll
-  for (int j = 0; j <= kMaxTopK; ++j) ss[j] = 0.f;
+  for (int j = 0; j <= KMAX; ++j) ss[j] = 0.f;
   for (int c = tid * 8; c < d; c += 256 * 8) {
-    u32x4 rows[kMaxTopK];
+    u32x4 rows[KMAX];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j)
+    for (int j = 0; j < KMAX; ++j)
       if (j < k) rows[j] = load16(y_perm + (size_t)pos[j] * d + c);
     float4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
     if (y_shared) {
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y_
     }
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
+    for (int j = 0; j < KMAX; ++j) {
       if (j < k) {
         float v[8];
         unpack8(rows[j], v);
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y_
       for (int q = 0; q < 8; ++q) o[q] = fmaf(routed_scale, acc[q], sv[q]);
       if constexpr (DIAG) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) ss[kMaxTopK] = fmaf(sv[q], sv[q], ss[kMaxTopK]);
+        for (int q = 0; q < 8; ++q) ss[KMAX] = fmaf(sv[q], sv[q], ss[KMAX]);
       }
     } else {
 #pragma unroll
@@ -98,8 +99,8 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y_
   if constexpr (DIAG) {
     const int wave = tid / kWave, lane = tid % kWave;
 #pragma unroll
-    for (int j = 0; j <= kMaxTopK; ++j) {
-      if (j < k || (j == kMaxTopK && y_shared)) {
+    for (int j = 0; j <= KMAX; ++j) {
+      if (j < k || (j == KMAX && y_shared)) {
         float v = ss[j];
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
@@ -115,14 +116,16 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y_
   }
 }
 
-// Per-expert activation RMS from the row sums of squares: wave e adds the
+// Per-expert activation RMS from the row sums of squares: block e adds the
 // rows of expert e (entry E: the shared expert's T rows) in double, in a
-// fixed order, and takes sqrt(sum / (rows * d)); no rows gives 0.
-__global__ __launch_bounds__(64) void k_expert_rms(const float* __restrict__ row_ss,
-                                                   const float* __restrict__ shared_ss,
-                                                   const int32_t* __restrict__ offsets, int T, int E, int d,
-                                                   float* __restrict__ rms) {
-  const int e = blockIdx.x, lane = threadIdx.x;
+// fixed order (thread-strided with four loads in flight, then a tree), and
+// takes sqrt(sum / (rows * d)); no rows gives 0.
+__global__ __launch_bounds__(256) void k_expert_rms(const float* __restrict__ row_ss,
+                                                    const float* __restrict__ shared_ss,
+                                                    const int32_t* __restrict__ offsets, int T, int E, int d,
+                                                    float* __restrict__ rms) {
+  __shared__ double red[256];
+  const int e = blockIdx.x, tid = threadIdx.x;
   const float* src;
   int n;
   if (e < E) {
@@ -133,10 +136,23 @@ __global__ __launch_bounds__(64) void k_expert_rms(const float* __restrict__ row
     n = shared_ss ? T : 0;
   }
   double s = 0.0;
-  for (int r = lane; r < n; r += kWave) s += (double)src[r];
+  for (int r0 = 0; r0 < n; r0 += 1024) {
+    float v[4];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-  if (lane == 0) rms[e] = n > 0 ? (float)sqrt(s / ((double)n * d)) : 0.f;
+    for (int q = 0; q < 4; ++q) {
+      const int r = r0 + q * 256 + tid;
+      v[q] = r < n ? src[r] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s += (double)v[q];
+  }
+  red[tid] = s;
+  __syncthreads();
+  for (int half = 128; half >= 1; half >>= 1) {
+    if (tid < half) red[tid] += red[tid + half];
+    __syncthreads();
+  }
+  if (tid == 0) rms[e] = n > 0 ? (float)sqrt(red[0] / ((double)n * d)) : 0.f;
 }
 
 // Spread of the routed experts' RMS ([Blog] §4.1.3, Figure 4: maximum against
@@ -144,26 +160,35 @@ __global__ __launch_bounds__(64) void k_expert_rms(const float* __restrict__ row
 // over the experts that received rows, ratio = (min, max) / median, the
 // median of an even count being the mean of the two middle values.  No such
 // expert, or a zero median, gives (0, 0).  One block; order statistics by
-// rank counting (ties broken by expert index).
+// rank counting (ties broken by expert index) over keys that are the RMS of
+// the experts with rows and +inf for the others and the padding.
 __global__ __launch_bounds__(1024) void k_rms_ratio(const float* __restrict__ rms,
                                                     const int32_t* __restrict__ offsets, int E,
                                                     float* __restrict__ ratio) {
-  __shared__ float val[1024];
-  __shared__ int used[1024];
+  __shared__ __attribute__((aligned(16))) float key[1024];
   __shared__ float sorted[1024];
+  __shared__ int used;
   const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += 1024) {
-    used[e] = offsets[e + 1] > offsets[e];
-    val[e] = rms[e];
+  const int E4 = (E + 3) / 4 * 4;
+  if (tid == 0) used = 0;
+  __syncthreads();
+  if (tid < E4) {
+    const bool has = tid < E && offsets[tid + 1] > offsets[tid];
+    key[tid] = has ? rms[tid] : __builtin_huge_valf();
+    if (has) atomicAdd(&used, 1);
   }
   __syncthreads();
-  int m = 0;
-  for (int e = 0; e < E; ++e) m += used[e];
-  for (int e = tid; e < E; e += 1024) {
-    if (!used[e]) continue;
+  const int m = used;
+  if (tid < E && key[tid] != __builtin_huge_valf()) {
+    const float ke = key[tid];
     int rank = 0;
-    for (int j = 0; j < E; ++j) rank += used[j] && (val[j] < val[e] || (val[j] == val[e] && j < e));
-    sorted[rank] = val[e];
+#pragma unroll 4
+    for (int j4 = 0; j4 < E4; j4 += 4) {
+      const float4 kj = *reinterpret_cast<const float4*>(&key[j4]);
+      rank += (kj.x < ke || (kj.x == ke && j4 < tid)) + (kj.y < ke || (kj.y == ke && j4 + 1 < tid)) +
+              (kj.z < ke || (kj.z == ke && j4 + 2 < tid)) + (kj.w < ke || (kj.w == ke && j4 + 3 < tid));
+    }
+    sorted[rank] = ke;
   }
   __syncthreads();
   if (tid == 0) {
@@ -208,29 +233,29 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const uint16_t* __restrict__ in
 hipError_t launch_combine(int T, int d, int k, const uint16_t* y_perm, const int32_t* pair_pos,
                           const float* topk_weights, const float* y_shared, float routed_scale, uint16_t* y,
                           const CombineDiag* diag, void* workspace, hipStream_t stream) {
-  if (!diag) {
-    if (T == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_combine<false>, dim3(T), dim3(256), 0, stream, y_perm, pair_pos, topk_weights, y_shared,
-                       routed_scale, d, k, y, nullptr, nullptr);
-    return hipGetLastError();
-  }
-  float* row_ss = static_cast<float*>(workspace);
-  float* shared_ss = y_shared ? row_ss + (size_t)T * k : nullptr;
+  float* row_ss = diag ? static_cast<float*>(workspace) : nullptr;
+  float* shared_ss = diag && y_shared ? row_ss + (size_t)T * k : nullptr;
   hipError_t err;
   if (T > 0) {
-    hipLaunchKernelGGL(k_combine<true>, dim3(T), dim3(256), 0, stream, y_perm, pair_pos, topk_weights, y_shared,
-                       routed_scale, d, k, y, row_ss, shared_ss);
+#define MOE_COMBINE(KMAX, DIAG)                                                                                   \
+  hipLaunchKernelGGL((k_combine<KMAX, DIAG>), dim3(T), dim3(256), 0, stream, y_perm, pair_pos, topk_weights, y_shared, \
+                     routed_scale, d, k, y, row_ss, shared_ss)
+    if (k <= 8) {
+      if (diag) MOE_COMBINE(8, true);
+      else MOE_COMBINE(8, false);
+    } else {
+      if (diag) MOE_COMBINE(kMaxTopK, true);
+      else MOE_COMBINE(kMaxTopK, false);
+    }
+#undef MOE_COMBINE
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(k_expert_rms, dim3(diag->E + 1), dim3(64), 0, stream, row_ss, shared_ss, diag->offsets, T,
+  if (!diag) return hipSuccess;
+  hipLaunchKernelGGL(k_expert_rms, dim3(diag->E + 1), dim3(256), 0, stream, row_ss, shared_ss, diag->offsets, T,
                      diag->E, d, diag->rms);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (diag->ratio) {
-    hipLaunchKernelGGL(k_rms_ratio, dim3(1), dim3(1024), 0, stream, diag->rms, diag->offsets, diag->E,
-                       diag->ratio);
-    err = hipGetLastError();
-  }
-  return err;
+  if ((err = hipGetLastError()) != hipSuccess || !diag->ratio) return err;
+  hipLaunchKernelGGL(k_rms_ratio, dim3(1), dim3(1024), 0, stream, diag->rms, diag->offsets, diag->E, diag->ratio);
+  return hipGetLastError();
 }
 
 // Row sums of squares: T*k routed rows, then T shared rows.

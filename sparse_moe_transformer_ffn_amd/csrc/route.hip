@@ -397,13 +397,23 @@ __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ 
 }
 
 // Column sums of the wave partials: block e adds diag[e * nw + w] over w in
-// a fixed order (thread-strided, then a tree), in double.
+// a fixed order (thread-strided with four loads in flight, then a tree), in
+// double.
 __global__ __launch_bounds__(256) void k_diag_columns(const float* __restrict__ diag, int nw,
                                                       double* __restrict__ col) {
   __shared__ double red[256];
   const int e = blockIdx.x, tid = threadIdx.x;
   double s = 0.0;
-  for (int w = tid; w < nw; w += 256) s += (double)diag[(size_t)e * nw + w];
+  for (int w0 = 0; w0 < nw; w0 += 1024) {
+    float v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int w = w0 + q * 256 + tid;
+      v[q] = w < nw ? diag[(size_t)e * nw + w] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s += (double)v[q];
+  }
   red[tid] = s;
   __syncthreads();
   for (int half = 128; half >= 1; half >>= 1) {
