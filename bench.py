@@ -256,6 +256,42 @@ def time_workload(cfg, steps, warmup, dev):
     return wl, res
 
 
+DENSE_HIDDEN = 11264   # dense FFN hidden size of the first blocks and the MTP heads
+
+
+def time_dense(T, steps, dev):
+    """The dense SwiGLU FFN (d = 4096, hidden 11,264) on T tokens through the
+    grouped kernels: median launch time, algorithmic bytes and flops."""
+    import numpy as np
+    import torch
+    import moegen
+    import sparse_moe_transformer_ffn_amd as moe
+    cfg = moegen.custom(1, T=T, hs=DENSE_HIDDEN)
+    d, H = cfg.d, DENSE_HIDDEN
+    x = torch.from_numpy(moegen.x(cfg).view(np.int16)).view(torch.bfloat16).to(dev)
+    w_gu = torch.empty((2 * H, d), dtype=torch.bfloat16, device=dev)
+    w_d = torch.empty((d, H), dtype=torch.bfloat16, device=dev)
+    moegen.fill_shared_device(cfg, 0, w_gu.data_ptr(), w_d.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    y = torch.empty((T, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(moe.moe_dense_workspace_bytes(T, d, H), dtype=torch.uint8, device=dev)
+    main = torch.cuda.current_stream()
+    for _ in range(2):
+        moe.moe_dense_swiglu(T, d, H, x, w_gu, w_d, y, ws, main)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(main)
+        moe.moe_dense_swiglu(T, d, H, x, w_gu, w_d, y, ws, main)
+        b.record(main)
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    nbytes = 3 * d * H * 2 + T * d * 2 + T * d * 4
+    flops = 2 * T * 3 * d * H
+    return {"tokens": T, "ms_median": ms, "tok_s": T / (ms * 1e-3),
+            "hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "tflops": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+
+
 def cpu_baseline(wl, n_sample):
     """The CPU oracle, single-threaded, on a bounded sample of the same
     workload's tokens (whole layer per token).  Weight generation is not
@@ -322,6 +358,7 @@ def main():
                     help="run only a plain 1 GiB device copy (the known-size reference for HBM byte counters)")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense SwiGLU FFN lines")
     ap.add_argument("--cpu-sample", type=int, default=64)
     ap.add_argument("--write-traffic", metavar="PMC_DIR",
                     help="no GPU work: write profiles/traffic_*.json from rocprofv3 counter runs in PMC_DIR")
@@ -379,6 +416,11 @@ def main():
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
     del wl
     torch.cuda.empty_cache()
+    if not args.no_dense:
+        out["dense_ffn"] = {"d_model": cfg.d, "hidden": DENSE_HIDDEN,
+                            "decode": time_dense(cfg.T, args.steps, dev),
+                            "prefill": None if args.no_prefill else time_dense(moegen.CONFIGS[2].T, 10, dev)}
+        torch.cuda.empty_cache()
 
     if not args.no_prefill:
         pcfg = moegen.CONFIGS[2]

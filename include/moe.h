@@ -218,6 +218,23 @@ moe_status moe_combine_diag(const moe_shape* shape, const uint16_t* y_perm, cons
                             const int32_t* expert_offsets, float* expert_rms, float* rms_ratio, void* workspace,
                             size_t ws_bytes, void* stream);
 
+/* Dense SwiGLU FFN ([Digest] architecture table: dense FFN hidden size
+ * 11,264; [Blog] §2.2, Figure 2 caption: the first three blocks and the MTP
+ * heads use a dense FFN), run by the grouped expert kernels as one group of
+ * all T tokens:
+ *   y[t,:] = W_d (SiLU(W_g x[t]) * (W_u x[t]))
+ * In:  x [T, d] bf16; w_gate_up [2H, d] bf16 (rows 0..H-1 gate, H..2H-1
+ *      up); w_down [d, H] bf16.
+ * Out: y [T, d] f32.  The hidden activation is rounded to bf16 between the
+ *      two GEMMs; accumulation is f32.
+ * Limits: 0 <= T <= 1048576; d, H in [64, 65536], multiples of 64
+ * (MOE_ERR_UNSUPPORTED_SHAPE).  The workspace (256-byte aligned) holds the
+ * hidden activations: moe_dense_workspace_bytes gives its size.            */
+moe_status moe_dense_workspace_bytes(int32_t num_tokens, int32_t d_model, int32_t d_hidden, size_t* bytes);
+moe_status moe_dense_swiglu(int32_t num_tokens, int32_t d_model, int32_t d_hidden, const uint16_t* x,
+                            const uint16_t* w_gate_up, const uint16_t* w_down, float* y, void* workspace,
+                            size_t ws_bytes, void* stream);
+
 /* Zero-centred RMSNorm of bf16 rows ([Blog] §2.2, Figure 2 caption; the
  * [Digest] notes the pre-norm placement):
  *   out[t,i] = in[t,i] / sqrt(mean_i(in[t,:]^2) + eps) * (1 + gamma[i])

@@ -24,7 +24,7 @@ STATUS = {
 EXPORTS = (
     "moe_status_str", "moe_check_shape", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_swiglu",
     "moe_expert_gate_up", "moe_expert_down", "moe_shared_swiglu", "moe_combine", "moe_rmsnorm", "moe_route_diag",
-    "moe_combine_diag",
+    "moe_combine_diag", "moe_dense_workspace_bytes", "moe_dense_swiglu",
 )
 
 
@@ -65,6 +65,10 @@ def lib():
         L.moe_rmsnorm.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_float, _P, _P]
         L.moe_route_diag.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P,
                                      ctypes.c_size_t, _P]
+        L.moe_dense_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                 ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_dense_swiglu.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P,
+                                       ctypes.c_size_t, _P]
         L.moe_combine_diag.argtypes = [_SP, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                        _P]
         for name in EXPORTS[1:]:
@@ -188,3 +192,17 @@ def moe_combine_diag(shape, y_perm, pair_pos, topk_weights, y_shared, routed_sca
                                                       _ptr(topk_weights), _ptr(y_shared), float(routed_scale),
                                                       _ptr(y), _ptr(expert_offsets), _ptr(expert_rms),
                                                       _ptr(rms_ratio), ws, nb, _stream(stream)))
+
+
+def moe_dense_workspace_bytes(num_tokens, d_model, d_hidden) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_dense_workspace_bytes", lib().moe_dense_workspace_bytes(int(num_tokens), int(d_model), int(d_hidden),
+                                                                        ctypes.byref(n)))
+    return n.value
+
+
+def moe_dense_swiglu(num_tokens, d_model, d_hidden, x, w_gate_up, w_down, y, workspace, stream=None):
+    ws, nb = _ws(workspace)
+    _check("moe_dense_swiglu", lib().moe_dense_swiglu(int(num_tokens), int(d_model), int(d_hidden), _ptr(x),
+                                                      _ptr(w_gate_up), _ptr(w_down), _ptr(y), ws, nb,
+                                                      _stream(stream)))

@@ -260,6 +260,39 @@ moe_status moe_combine_diag(const moe_shape* shape, const uint16_t* y_perm, cons
                                         (hipStream_t)stream));
 }
 
+moe_status moe_dense_workspace_bytes(int32_t num_tokens, int32_t d_model, int32_t d_hidden, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
+  if (num_tokens < 0 || num_tokens > kMaxTokens || d_model < 64 || d_model > kMaxDim || d_model % 64 ||
+      d_hidden < 64 || d_hidden > kMaxDim || d_hidden % 64)
+    return MOE_ERR_UNSUPPORTED_SHAPE;
+  *bytes = round256(moe::kQueueBytes + moe::shared_hid_bytes(num_tokens, d_hidden));
+  return MOE_OK;
+}
+
+moe_status moe_dense_swiglu(int32_t num_tokens, int32_t d_model, int32_t d_hidden, const uint16_t* x,
+                            const uint16_t* w_gate_up, const uint16_t* w_down, float* y, void* workspace,
+                            size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  moe_status st = moe_dense_workspace_bytes(num_tokens, d_model, d_hidden, &need);
+  if (st != MOE_OK) return st;
+  if (!x || !w_gate_up || !w_down || !y || !workspace) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(y)) return MOE_ERR_MISALIGNED;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MOE_ERR_MISALIGNED;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  // One group holding every token: the shared-expert group of the grouped
+  // launches, with no routed groups (the routed sizes are placeholders that
+  // no kernel reads).
+  const int T = num_tokens, d = d_model, H = d_hidden;
+  int32_t* queue = static_cast<int32_t*>(workspace);
+  uint16_t* hid = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + moe::kQueueBytes);
+  hipError_t err = moe::launch_gate_up(T, d, 1, 1, 128, H, x, nullptr, nullptr, nullptr, w_gate_up, nullptr, hid,
+                                       queue, (hipStream_t)stream);
+  if (err == hipSuccess)
+    err = moe::launch_down(T, d, 1, 1, 128, H, nullptr, nullptr, hid, nullptr, w_down, nullptr, y, queue,
+                           (hipStream_t)stream);
+  return hip_status(err);
+}
+
 moe_status moe_rmsnorm(int32_t rows, int32_t cols, const uint16_t* in, const float* gamma, float eps, uint16_t* out,
                        void* stream) {
   if (rows < 0 || rows > kMaxTokens || cols < 8 || cols > kMaxDim || cols % 8) return MOE_ERR_UNSUPPORTED_SHAPE;

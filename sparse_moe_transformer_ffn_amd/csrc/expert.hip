@@ -148,9 +148,15 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
   }
 }
 
-// Phase 2: out[row, n] = hid[row, :] . W_d[n, :] for the item's BM rows and 64
-// output columns n; routed rows -> y_perm (bf16), shared rows -> y_shared (f32).
-template <int BM>
+// Phase 2: out[row, n] = hid[row, :] . W_d[n, :]; routed rows -> y_perm
+// (bf16), shared rows -> y_shared (f32).
+// KW = 1: an item is BM rows x 64 output columns, wave w owns columns
+//         16w..16w+15 over the whole reduction (the routed experts' 1,280).
+// KW = 4: an item is BM rows x 16 columns and wave w owns the w-th quarter of
+//         the reduction, the partial sums added in LDS in wave order: for a
+//         long reduction (the dense FFN's 11,264) with few rows, four times
+//         as many items keep enough waves streaming.
+template <int BM, int KW>
 __global__ __launch_bounds__(256) void k_down(Groups gs, int d, int h, int hs, const uint16_t* __restrict__ hid,
                                               const uint16_t* __restrict__ hid_shared,
                                               const uint16_t* __restrict__ w_down,
@@ -159,15 +165,19 @@ __global__ __launch_bounds__(256) void k_down(Groups gs, int d, int h, int hs, c
   __shared__ int ip[kMaxGroups + 1];
   __shared__ int wsum[4];
   constexpr int MB = BM / 16;
-  const int items = item_prefix<BM>(ip, wsum, gs, d / 64, d / 64);
+  constexpr int COLS = 64 / KW;  // output columns per item
+  __shared__ float red[KW > 1 ? KW - 1 : 1][MB * 4][kWave];
+  const int items = item_prefix<BM>(ip, wsum, gs, d / COLS, d / COLS);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int r16 = lane & 15, kq = lane >> 4;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   for (int w = xcd_contiguous(blockIdx.x, gridDim.x); w < items; w += gridDim.x) {
-    const Item it = decode_item<0>(ip, gs, BM, d / 64, d / 64, w);
+    const Item it = decode_item<0>(ip, gs, BM, d / COLS, d / COLS, w);
     const int H = it.shared ? hs : h;
-    const int n = it.nt * 64 + wave * 16 + r16;
-    const uint16_t* pb = (it.shared ? ws_down : w_down + (size_t)it.group * d * h) + (size_t)n * H + kq * 8;
+    const int klen = H / KW, kbeg = KW > 1 ? wave * klen : 0;
+    const int n = it.nt * COLS + (KW > 1 ? 0 : wave * 16) + r16;
+    const uint16_t* pb =
+        (it.shared ? ws_down : w_down + (size_t)it.group * d * h) + (size_t)n * H + kbeg + kq * 8;
     const uint16_t* src = it.shared ? hid_shared : hid;
     const uint16_t* pa[MB];
     bool va[MB];
@@ -175,13 +185,13 @@ __global__ __launch_bounds__(256) void k_down(Groups gs, int d, int h, int hs, c
     for (int mb = 0; mb < MB; ++mb) {
       const int r = it.m0 + mb * 16 + r16;
       va[mb] = r < it.nrows;
-      pa[mb] = src + (size_t)(it.row0 + (va[mb] ? r : 0)) * H + kq * 8;
+      pa[mb] = src + (size_t)(it.row0 + (va[mb] ? r : 0)) * H + kbeg + kq * 8;
     }
     f32x4 acc[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
     int kk = 0;
-    for (; kk + 32 * kUnroll <= H; kk += 32 * kUnroll) {
+    for (; kk + 32 * kUnroll <= klen; kk += 32 * kUnroll) {
       u32x4 b[kUnroll], a[MB][kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) b[u] = load16(pb + kk + 32 * u);
@@ -194,13 +204,32 @@ __global__ __launch_bounds__(256) void k_down(Groups gs, int d, int h, int hs, c
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_16x16x32(a[mb][u], b[u], acc[mb]);
     }
-    for (; kk < H; kk += 32) {
+    for (; kk < klen; kk += 32) {
       const u32x4 b = load16(pb + kk);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const u32x4 a = va[mb] ? load16(pa[mb] + kk) : zero;
         acc[mb] = mfma_16x16x32(a, b, acc[mb]);
       }
+    }
+    if (KW > 1) {
+      if (wave > 0) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) red[wave - 1][mb * 4 + i][lane] = acc[mb][i];
+      }
+      __syncthreads();
+      if (wave == 0) {
+#pragma unroll
+        for (int q = 0; q < KW - 1; ++q)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mb][i] += red[q][mb * 4 + i][lane];
+      }
+      __syncthreads();  // red[] free for the next item
+      if (wave > 0) continue;
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -219,13 +248,14 @@ __global__ __launch_bounds__(256) void k_down(Groups gs, int d, int h, int hs, c
 
 namespace {
 
-// Average rows per routed group (or all T rows when only the shared expert
-// runs) decides the regime: >= 64 rows is compute-bound work for the tiled
-// kernels.
-bool use_tiled(int T, int k, int E, const int32_t* offsets) {
-  const long rows = offsets ? (long)T * k : (long)T;
-  const long groups = offsets ? E : 1;
-  return rows >= 64L * groups;
+// Average rows per routed group decides the regime: >= 64 rows is
+// compute-bound work for the tiled kernels.  A launch of the shared group
+// alone (no routed groups) goes tiled only when the tiled items of the phase,
+// ceil(T / 256) x (its 256-wide weight tiles), at least fill the chip;
+// otherwise the streaming kernels' finer items spread it over every CU.
+bool use_tiled(int T, int k, int E, const int32_t* offsets, int weight_rows) {
+  if (!offsets) return (long)((T + 255) / 256) * (weight_rows / 256) >= 256;
+  return (long)T * k >= 64L * E;
 }
 
 int pick_bm(int T, int k, int E) {
@@ -244,11 +274,11 @@ hipError_t gate_up_bm(const uint16_t* x, const Groups& gs, int d, int h, int hs,
   return hipGetLastError();
 }
 
-template <int BM>
+template <int BM, int KW>
 hipError_t down_bm(const Groups& gs, int d, int h, int hs, const uint16_t* hid, const uint16_t* hid_shared,
                    const uint16_t* w_down, const uint16_t* ws_down, uint16_t* y_perm, float* y_shared,
                    hipStream_t stream) {
-  const auto kern = k_down<BM>;
+  const auto kern = k_down<BM, KW>;
   hipLaunchKernelGGL(kern, dim3(persistent_grid(kern)), dim3(256), 0, stream, gs, d, h, hs, hid, hid_shared, w_down,
                      ws_down, y_perm, y_shared);
   return hipGetLastError();
@@ -261,7 +291,7 @@ hipError_t launch_gate_up(int T, int d, int E, int k, int h, int hs, const uint1
                           uint16_t* hid_shared, int32_t* queue, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   // The tiled gate/up item covers 128 hidden units of each group.
-  if (use_tiled(T, k, E, offsets) && h % 128 == 0 && hs % 128 == 0)
+  if (use_tiled(T, k, E, offsets, 2 * hs) && h % 128 == 0 && hs % 128 == 0)
     return launch_gate_up_tiled(T, d, E, k, h, hs, x, offsets, perm, w_gu, ws_gu, hid, hid_shared, queue, stream);
   const Groups gs = make_groups(T, E, k, offsets, perm, ws_gu != nullptr);
   // Reduction split over the waves when every quarter is whole 32-wide steps.
@@ -279,15 +309,20 @@ hipError_t launch_down(int T, int d, int E, int k, int h, int hs, const int32_t*
                        float* y_shared, int32_t* queue, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   // The tiled down item covers 256 output columns.
-  if (use_tiled(T, k, E, offsets) && d % 256 == 0)
+  if (use_tiled(T, k, E, offsets, d) && d % 256 == 0)
     return launch_down_tiled(T, d, E, k, h, hs, offsets, hid, hid_shared, w_down, ws_down, y_perm, y_shared, queue,
                              stream);
   const Groups gs = make_groups(T, E, k, offsets, nullptr, ws_down != nullptr);
-  // The down reduction (the expert hidden size) is short enough already:
-  // quarters of it are too few steps to keep loads in flight.
-  if (pick_bm(T, k, offsets ? E : 1) == 16)
-    return down_bm<16>(gs, d, h, hs, hid, hid_shared, w_down, ws_down, y_perm, y_shared, stream);
-  return down_bm<32>(gs, d, h, hs, hid, hid_shared, w_down, ws_down, y_perm, y_shared, stream);
+  // The routed experts' reduction (1,280) is short enough already: quarters
+  // of it are too few steps to keep loads in flight.  A long reduction of the
+  // shared group alone (the dense FFN) is split over the waves.
+  const bool split = !offsets && hs >= 4096 && hs % 128 == 0 && d % 16 == 0;
+  if (pick_bm(T, k, offsets ? E : 1) == 16) {
+    if (split) return down_bm<16, 4>(gs, d, h, hs, hid, hid_shared, w_down, ws_down, y_perm, y_shared, stream);
+    return down_bm<16, 1>(gs, d, h, hs, hid, hid_shared, w_down, ws_down, y_perm, y_shared, stream);
+  }
+  if (split) return down_bm<32, 4>(gs, d, h, hs, hid, hid_shared, w_down, ws_down, y_perm, y_shared, stream);
+  return down_bm<32, 1>(gs, d, h, hs, hid, hid_shared, w_down, ws_down, y_perm, y_shared, stream);
 }
 
 size_t expert_hid_bytes(int T, int k, int h) { return ((size_t)T * k * h * sizeof(uint16_t) + 255) / 256 * 256; }

@@ -208,3 +208,23 @@ def test_combine_diag_validation():
     assert call(ratio=A + 1) == MISALIGNED
     assert call(ysh=A + 4) == MISALIGNED
     assert call(nbytes=16) == WS_SMALL
+
+
+def test_dense_validation():
+    L = moe.lib()
+    n = ctypes.c_size_t(0)
+    assert L.moe_dense_workspace_bytes(64, 4096, 11264, ctypes.byref(n)) == OK and n.value % 256 == 0
+    assert n.value >= 64 * 11264 * 2
+    assert L.moe_dense_workspace_bytes(64, 4096, 11264, None) == INVALID
+    for T, d, H in ((-1, 256, 128), (8, 100, 128), (8, 256, 100), (8, 256, 32), (8, 131072, 128),
+                    ((1 << 20) + 1, 256, 128)):
+        assert L.moe_dense_workspace_bytes(T, d, H, ctypes.byref(n)) == UNSUPPORTED, (T, d, H)
+        assert L.moe_dense_swiglu(T, d, H, A, A, A, A, A, 1 << 30, None) == UNSUPPORTED, (T, d, H)
+    L.moe_dense_workspace_bytes(64, 256, 128, ctypes.byref(n))
+    nb = n.value
+    assert L.moe_dense_swiglu(64, 256, 128, None, A, A, A, A, nb, None) == INVALID
+    assert L.moe_dense_swiglu(64, 256, 128, A, A, A, A, None, nb, None) == INVALID
+    assert L.moe_dense_swiglu(64, 256, 128, MIS, A, A, A, A, nb, None) == MISALIGNED
+    assert L.moe_dense_swiglu(64, 256, 128, A, A, A, A + 4, A, nb, None) == MISALIGNED
+    assert L.moe_dense_swiglu(64, 256, 128, A, A, A, A, A + 16, nb, None) == MISALIGNED
+    assert L.moe_dense_swiglu(64, 256, 128, A, A, A, A, A, nb - 1, None) == WS_SMALL
