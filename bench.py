@@ -292,6 +292,43 @@ def time_dense(T, steps, dev):
             "tflops": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
 
 
+EP_SHARES = 8   # expert-parallel group size the pages deploy: 36 of 288 experts per GPU
+
+
+def time_share(wl, steps):
+    """One GPU's share of an 8-way expert-parallel layer: the grouped expert
+    kernels on experts [0, E/8) with their weights only, on the routing the
+    timed steps produced.  Median launch time next to the whole call's."""
+    import numpy as np
+    import torch
+    import sparse_moe_transformer_ffn_amd as moe
+    b, sh, c = wl.buf, wl.buf.shape, wl.cfg
+    e1 = c.E // EP_SHARES
+    main = torch.cuda.current_stream()
+
+    def share():
+        moe.moe_expert_swiglu_range(sh, 0, e1, wl.x, b.expert_offsets, b.perm_pairs, wl.w_gu[:e1], wl.w_d[:e1],
+                                    b.y_perm, b.workspace, main)
+
+    for _ in range(2):
+        share()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, z in ev:
+        a.record(main)
+        share()
+        z.record(main)
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(z) for a, z in ev]))
+    counts = b.expert_counts.cpu().numpy()[:e1]
+    rows = int(counts.sum())
+    touched = int((counts > 0).sum())
+    nbytes = touched * 3 * c.d * c.h * 2 + rows * c.d * 2 * 2
+    flops = 2 * rows * 3 * c.d * c.h
+    return {"experts": [0, e1], "rows": rows, "touched_experts": touched, "ms_median": ms,
+            "hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "tflops": flops / (ms * 1e-3) / 1e12}
+
+
 def cpu_baseline(wl, n_sample):
     """The CPU oracle, single-threaded, on a bounded sample of the same
     workload's tokens (whole layer per token).  Weight generation is not
@@ -412,6 +449,7 @@ def main():
                     "down_gbs": alg["down_bytes"] / (r["down_ms"] * 1e-3) / 1e9},
         "diagnostics": r["diagnostics"],
     }
+    out["ep_share"] = time_share(wl, args.steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
     del wl
@@ -437,6 +475,7 @@ def main():
                         "down_tflops": palg["down_flops"] / (p["down_ms"] * 1e-3) / 1e12},
             "touched_experts": p["n_touched"], "max_load": p["max_load"], "idle_experts": p["idle_experts"],
             "diagnostics": p["diagnostics"],
+            "ep_share": time_share(pwl, args.prefill_steps),
         }
         del pwl
     print(json.dumps(out), flush=True)

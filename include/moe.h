@@ -21,7 +21,8 @@
  *   moe_permute        stable (expert, token) permutation of the k*T pairs
  *   moe_expert_swiglu  grouped gate/up GEMM + SwiGLU, then grouped down GEMM
  *                      (also callable as its two phases, moe_expert_gate_up
- *                      and moe_expert_down)
+ *                      and moe_expert_down, and on a contiguous share of the
+ *                      experts, moe_expert_swiglu_range)
  *   moe_shared_swiglu  the always-on shared expert
  *   moe_combine        y = y_shared + routed_scale * sum_j w_j * y_perm[pos]
  *
@@ -167,6 +168,27 @@ moe_status moe_expert_swiglu(const moe_shape* shape, const uint16_t* x, const in
                              const int32_t* perm_pairs, const uint16_t* w_gate_up, const uint16_t* w_down,
                              const uint16_t* ws_gate_up, const uint16_t* ws_down, uint16_t* y_perm, float* y_shared,
                              void* workspace, size_t ws_bytes, void* stream);
+
+/* moe_expert_swiglu on one contiguous share of the experts, as one GPU of
+ * an expert-parallel group runs it ([Blog] §2.2: expert parallelism for
+ * scalable deployment, §2.2.2: EP-group balance, §3.2: 8-way expert
+ * parallelism; [Digest] inference-cost table: EP8 serving): the routed
+ * groups are experts expert_begin .. expert_end-1 and nothing else (no
+ * shared expert; call moe_shared_swiglu for it).
+ * In:  x, expert_offsets [E+1] and perm_pairs as for moe_expert_swiglu (the
+ *      whole routing; the share's pairs are rows expert_offsets[expert_begin]
+ *      .. expert_offsets[expert_end]-1 of the permuted order);
+ *      w_gate_up [E_l, 2h, d] and w_down [E_l, d, h] bf16, the share's
+ *      E_l = expert_end - expert_begin experts only.
+ * Out: y_perm [T*k, d] bf16: the share's rows, exactly as moe_expert_swiglu
+ *      computes them (same kernels and reduction order); other rows are not
+ *      written.
+ * 0 <= expert_begin < expert_end <= E, else MOE_ERR_INVALID_ARGUMENT.  The
+ * workspace rule is the one of every call.                                  */
+moe_status moe_expert_swiglu_range(const moe_shape* shape, int32_t expert_begin, int32_t expert_end,
+                                   const uint16_t* x, const int32_t* expert_offsets, const int32_t* perm_pairs,
+                                   const uint16_t* w_gate_up, const uint16_t* w_down, uint16_t* y_perm,
+                                   void* workspace, size_t ws_bytes, void* stream);
 
 /* The two phases of moe_expert_swiglu, for callers that keep the hidden
  * activations themselves: hid [T*k, h] bf16 (permuted order) and, with the

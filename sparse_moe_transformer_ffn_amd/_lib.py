@@ -24,7 +24,7 @@ STATUS = {
 EXPORTS = (
     "moe_status_str", "moe_check_shape", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_swiglu",
     "moe_expert_gate_up", "moe_expert_down", "moe_shared_swiglu", "moe_combine", "moe_rmsnorm", "moe_route_diag",
-    "moe_combine_diag", "moe_dense_workspace_bytes", "moe_dense_swiglu",
+    "moe_combine_diag", "moe_dense_workspace_bytes", "moe_dense_swiglu", "moe_expert_swiglu_range",
 )
 
 
@@ -69,6 +69,8 @@ def lib():
                                                  ctypes.POINTER(ctypes.c_size_t)]
         L.moe_dense_swiglu.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P,
                                        ctypes.c_size_t, _P]
+        L.moe_expert_swiglu_range.argtypes = [_SP, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
+                                              ctypes.c_size_t, _P]
         L.moe_combine_diag.argtypes = [_SP, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                        _P]
         for name in EXPORTS[1:]:
@@ -206,3 +208,11 @@ def moe_dense_swiglu(num_tokens, d_model, d_hidden, x, w_gate_up, w_down, y, wor
     _check("moe_dense_swiglu", lib().moe_dense_swiglu(int(num_tokens), int(d_model), int(d_hidden), _ptr(x),
                                                       _ptr(w_gate_up), _ptr(w_down), _ptr(y), ws, nb,
                                                       _stream(stream)))
+
+
+def moe_expert_swiglu_range(shape, expert_begin, expert_end, x, expert_offsets, perm_pairs, w_gate_up, w_down,
+                            y_perm, workspace, stream=None):
+    ws, nb = _ws(workspace)
+    _check("moe_expert_swiglu_range", lib().moe_expert_swiglu_range(
+        ctypes.byref(shape), int(expert_begin), int(expert_end), _ptr(x), _ptr(expert_offsets), _ptr(perm_pairs),
+        _ptr(w_gate_up), _ptr(w_down), _ptr(y_perm), ws, nb, _stream(stream)))

@@ -203,6 +203,35 @@ moe_status moe_expert_swiglu(const moe_shape* shape, const uint16_t* x, const in
   return hip_status(err);
 }
 
+moe_status moe_expert_swiglu_range(const moe_shape* shape, int32_t expert_begin, int32_t expert_end,
+                                   const uint16_t* x, const int32_t* expert_offsets, const int32_t* perm_pairs,
+                                   const uint16_t* w_gate_up, const uint16_t* w_down, uint16_t* y_perm,
+                                   void* workspace, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (expert_begin < 0 || expert_end > shape->num_experts || expert_begin >= expert_end)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!x || !expert_offsets || !perm_pairs || !w_gate_up || !w_down || !y_perm) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(y_perm) ||
+      !aligned4(expert_offsets) || !aligned4(perm_pairs))
+    return MOE_ERR_MISALIGNED;
+  if ((st = check_workspace(shape, workspace, ws_bytes)) != MOE_OK) return st;
+  // The share's groups are experts begin..end-1: their offsets entries hold
+  // absolute rows of the permuted order, so the share's rows land where the
+  // whole call would put them; the weights are the share's own.
+  const int T = shape->num_tokens, d = shape->d_model, E = shape->num_experts, k = shape->top_k;
+  const int h = shape->d_expert, hs = shape->d_shared, El = expert_end - expert_begin;
+  const int32_t* off = expert_offsets + expert_begin;
+  int32_t* queue = static_cast<int32_t*>(workspace);
+  uint16_t* hid = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + moe::kQueueBytes);
+  hipError_t err = moe::launch_gate_up(T, d, El, k, h, hs, x, off, perm_pairs, w_gate_up, nullptr, hid, nullptr,
+                                       queue, (hipStream_t)stream, E);
+  if (err == hipSuccess)
+    err = moe::launch_down(T, d, El, k, h, hs, off, hid, nullptr, w_down, nullptr, y_perm, nullptr, queue,
+                           (hipStream_t)stream, E);
+  return hip_status(err);
+}
+
 moe_status moe_shared_swiglu(const moe_shape* shape, const uint16_t* x, const uint16_t* ws_gate_up,
                              const uint16_t* ws_down, float* y_shared, void* workspace, size_t ws_bytes,
                              void* stream) {

@@ -288,15 +288,16 @@ hipError_t down_bm(const Groups& gs, int d, int h, int hs, const uint16_t* hid, 
 
 hipError_t launch_gate_up(int T, int d, int E, int k, int h, int hs, const uint16_t* x, const int32_t* offsets,
                           const int32_t* perm, const uint16_t* w_gu, const uint16_t* ws_gu, uint16_t* hid,
-                          uint16_t* hid_shared, int32_t* queue, hipStream_t stream) {
+                          uint16_t* hid_shared, int32_t* queue, hipStream_t stream, int e_total) {
   if (T == 0) return hipSuccess;
+  const int et = e_total > 0 ? e_total : E;
   // The tiled gate/up item covers 128 hidden units of each group.
-  if (use_tiled(T, k, E, offsets, 2 * hs) && h % 128 == 0 && hs % 128 == 0)
+  if (use_tiled(T, k, et, offsets, 2 * hs) && h % 128 == 0 && hs % 128 == 0)
     return launch_gate_up_tiled(T, d, E, k, h, hs, x, offsets, perm, w_gu, ws_gu, hid, hid_shared, queue, stream);
   const Groups gs = make_groups(T, E, k, offsets, perm, ws_gu != nullptr);
   // Reduction split over the waves when every quarter is whole 32-wide steps.
   const bool split = d % 128 == 0;
-  if (pick_bm(T, k, offsets ? E : 1) == 16) {
+  if (pick_bm(T, k, offsets ? et : 1) == 16) {
     if (split) return gate_up_bm<16, 4>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, stream);
     return gate_up_bm<16, 1>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, stream);
   }
@@ -306,10 +307,11 @@ hipError_t launch_gate_up(int T, int d, int E, int k, int h, int hs, const uint1
 
 hipError_t launch_down(int T, int d, int E, int k, int h, int hs, const int32_t* offsets, const uint16_t* hid,
                        const uint16_t* hid_shared, const uint16_t* w_down, const uint16_t* ws_down, uint16_t* y_perm,
-                       float* y_shared, int32_t* queue, hipStream_t stream) {
+                       float* y_shared, int32_t* queue, hipStream_t stream, int e_total) {
   if (T == 0) return hipSuccess;
+  const int et = e_total > 0 ? e_total : E;
   // The tiled down item covers 256 output columns.
-  if (use_tiled(T, k, E, offsets, d) && d % 256 == 0)
+  if (use_tiled(T, k, et, offsets, d) && d % 256 == 0)
     return launch_down_tiled(T, d, E, k, h, hs, offsets, hid, hid_shared, w_down, ws_down, y_perm, y_shared, queue,
                              stream);
   const Groups gs = make_groups(T, E, k, offsets, nullptr, ws_down != nullptr);
@@ -317,7 +319,7 @@ hipError_t launch_down(int T, int d, int E, int k, int h, int hs, const int32_t*
   // of it are too few steps to keep loads in flight.  A long reduction of the
   // shared group alone (the dense FFN) is split over the waves.
   const bool split = !offsets && hs >= 4096 && hs % 128 == 0 && d % 16 == 0;
-  if (pick_bm(T, k, offsets ? E : 1) == 16) {
+  if (pick_bm(T, k, offsets ? et : 1) == 16) {
     if (split) return down_bm<16, 4>(gs, d, h, hs, hid, hid_shared, w_down, ws_down, y_perm, y_shared, stream);
     return down_bm<16, 1>(gs, d, h, hs, hid, hid_shared, w_down, ws_down, y_perm, y_shared, stream);
   }

@@ -42,12 +42,16 @@ size_t permute_workspace_bytes(int T, int E);
 // given (ws_gu / ws_down non-NULL).  `queue` is kQueueBytes of device scratch
 // for the work queue of the compute-regime kernels.
 constexpr size_t kQueueBytes = 256;
+// e_total: the experts the routing chose among, when the routed groups are a
+// contiguous share of them (offsets then points at the share's first entry
+// and E counts the share); 0 means E.  It sets the regime, which follows the
+// average rows per expert.
 hipError_t launch_gate_up(int T, int d, int E, int k, int h, int hs, const uint16_t* x, const int32_t* offsets,
                           const int32_t* perm, const uint16_t* w_gu, const uint16_t* ws_gu, uint16_t* hid,
-                          uint16_t* hid_shared, int32_t* queue, hipStream_t stream);
+                          uint16_t* hid_shared, int32_t* queue, hipStream_t stream, int e_total = 0);
 hipError_t launch_down(int T, int d, int E, int k, int h, int hs, const int32_t* offsets, const uint16_t* hid,
                        const uint16_t* hid_shared, const uint16_t* w_down, const uint16_t* ws_down, uint16_t* y_perm,
-                       float* y_shared, int32_t* queue, hipStream_t stream);
+                       float* y_shared, int32_t* queue, hipStream_t stream, int e_total = 0);
 // The compute-regime (LDS-tiled, MFMA 32x32x16) versions of the same two
 // phases; the launchers above pick them when groups are large.
 hipError_t launch_gate_up_tiled(int T, int d, int E, int k, int h, int hs, const uint16_t* x, const int32_t* offsets,

@@ -228,3 +228,21 @@ def test_dense_validation():
     assert L.moe_dense_swiglu(64, 256, 128, A, A, A, A + 4, A, nb, None) == MISALIGNED
     assert L.moe_dense_swiglu(64, 256, 128, A, A, A, A, A + 16, nb, None) == MISALIGNED
     assert L.moe_dense_swiglu(64, 256, 128, A, A, A, A, A, nb - 1, None) == WS_SMALL
+
+
+def test_expert_range_validation():
+    s = shape(1)
+    L = moe.lib()
+    nb = moe.moe_workspace_bytes(s)
+
+    def call(b=0, e=36, x=A, off=A, wgu=A, ws=A, nbytes=nb):
+        return L.moe_expert_swiglu_range(ctypes.byref(s), b, e, x, off, A, wgu, A, A, ws, nbytes, None)
+
+    for b, e in ((-1, 36), (0, 0), (36, 36), (40, 36), (0, 289), (288, 289)):
+        assert call(b, e) == INVALID, (b, e)
+    assert call(x=None) == INVALID
+    assert call(ws=None) == INVALID
+    assert call(x=MIS) == MISALIGNED
+    assert call(off=A + 2) == MISALIGNED
+    assert call(wgu=A + 8) == MISALIGNED
+    assert call(nbytes=nb - 256) == WS_SMALL

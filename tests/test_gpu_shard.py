@@ -1,0 +1,75 @@
+"""moe_expert_swiglu_range: the grouped expert kernels on one contiguous share
+of the experts, as one GPU of an 8-way expert-parallel group would run them
+(36 of 288 experts, with only those experts' weights).
+
+Each share's rows must be bit-identical to the whole call's (same kernels,
+same reduction order), rows outside the share untouched, and sampled rows
+within the output tolerance of the oracle's SwiGLU.  Inputs: the oracle's
+routing and permutation of the generator's tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moegen
+import oracle
+import sparse_moe_transformer_ffn_amd as moe
+from tests.gpu_harness import DeviceLayer, bf16_host, check_output, i32_dev, log, oracle_route_all
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0x7FBF  # a bf16 NaN pattern no kernel writes
+
+
+def shard_bounds(E, shards):
+    per = E // shards
+    return [(i * per, (i + 1) * per) for i in range(shards)]
+
+
+@pytest.mark.parametrize("idx,shards", [(0, 4), (1, 8), (2, 8)])
+def test_expert_shares_match_whole_call(device, idx, shards):
+    cfg = moegen.CONFIGS[idx]
+    log(f"[shard] config {idx}: {shards} shares of {cfg.E // shards} experts")
+    dl = DeviceLayer(cfg)
+    o_ids, _, _ = oracle_route_all(dl)
+    cnt, off, perm, _ = oracle.permute(o_ids, cfg.E)
+    s = moe.make_shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, cfg.hs)
+    ws = torch.empty(moe.moe_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    off_d, perm_d = i32_dev(off), i32_dev(perm)
+    y_full = torch.zeros((cfg.T * cfg.k, cfg.d), dtype=torch.bfloat16, device="cuda")
+    moe.moe_expert_swiglu(s, dl.x, off_d, perm_d, dl.w_gu, dl.w_d, y_full, ws)
+    torch.cuda.synchronize()
+    full = bf16_host(y_full)
+    for b, e in shard_bounds(cfg.E, shards):
+        y = torch.full((cfg.T * cfg.k, cfg.d), SENTINEL, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        moe.moe_expert_swiglu_range(s, b, e, dl.x, off_d, perm_d, dl.w_gu[b:e], dl.w_d[b:e], y, ws)
+        torch.cuda.synchronize()
+        got = bf16_host(y)
+        lo, hi = off[b], off[e]
+        np.testing.assert_array_equal(got[lo:hi], full[lo:hi])
+        assert np.all(got[:lo] == SENTINEL) and np.all(got[hi:] == SENTINEL)
+    # The first share against the oracle: first, middle and last row of each
+    # of up to eight of its touched experts.
+    b, e = shard_bounds(cfg.E, shards)[0]
+    touched = [g for g in range(b, e) if cnt[g] > 0][:8]
+    rows = sorted({r for g in touched for r in (off[g], (off[g] + off[g + 1] - 1) // 2, off[g + 1] - 1)})
+    ew = moegen.expert_weights_host(cfg, 0, touched)
+    ref = np.stack([oracle.expert(dl.x_h[perm[r] // cfg.k], *ew[int(np.searchsorted(off, r, side="right") - 1)])
+                    for r in rows])
+    check_output(moegen.bf16_to_f32(full[rows]), ref, f"share rows ({len(rows)})")
+
+
+def test_share_without_rows_writes_nothing(device):
+    # Experts 4..7 receive no token: their share's call leaves y_perm alone.
+    cfg = moegen.CONFIGS[0]
+    dl = DeviceLayer(cfg)
+    ids = moegen.random_ids(91, cfg.T, cfg.E - 4, cfg.k)
+    ids = np.where(ids >= 4, ids + 4, ids).astype(np.int32)
+    _, off, perm, _ = oracle.permute(ids, cfg.E)
+    assert off[8] == off[4]
+    s = moe.make_shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, cfg.hs)
+    ws = torch.empty(moe.moe_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    y = torch.full((cfg.T * cfg.k, cfg.d), 3.0, dtype=torch.bfloat16, device="cuda")
+    moe.moe_expert_swiglu_range(s, 4, 8, dl.x, i32_dev(off), i32_dev(perm), dl.w_gu[4:8], dl.w_d[4:8], y, ws)
+    torch.cuda.synchronize()
+    assert np.all(moegen.bf16_to_f32(bf16_host(y)) == 3.0)
