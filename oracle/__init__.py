@@ -34,7 +34,7 @@ def lib():
         L.oracle_layer.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
                                    _I, _P, _P, _P, _P, _P]
         L.oracle_rmsnorm.argtypes = [_I, _I, _P, _P, ctypes.c_float, _P]
-        L.oracle_combine.argtypes = [_I, _I, _I, _P, _P, _P, _P, ctypes.c_float, _P]
+        L.oracle_combine.argtypes = [_I, _I, _I, _P, _P, _P, _P, ctypes.c_float, _P, _P]
         L.oracle_route_diag.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P]
         L.oracle_activation_rms.argtypes = [_I, _I, _P, _P]
         for f in (L.oracle_route, L.oracle_permute, L.oracle_expert, L.oracle_layer, L.oracle_rmsnorm,
@@ -146,17 +146,19 @@ def layer(x, w_router, sel_bias, k, w_gu, w_d, ws_gu=None, ws_d=None, routed_sca
     return ids, wts, gap, y
 
 
-def combine(y_perm, pair_pos, weights, y_shared=None, routed_scale=1.0):
-    """y = y_shared + routed_scale * sum_j w[t,j] y_perm[pos[t*k+j]]; f32 [T,d]."""
+def combine(y_perm, pair_pos, weights, y_shared=None, routed_scale=1.0, residual=None):
+    """y = residual + (y_shared + routed_scale * sum_j w[t,j] y_perm[pos[t*k+j]]);
+    f32 [T,d].  residual: bf16 bits [T,d] or None."""
     y_perm = _c(y_perm, np.uint16)
     weights = _c(weights, np.float32)
     pair_pos = _c(pair_pos, np.int32)
     y_shared = _c(y_shared, np.float32)
+    residual = _c(residual, np.uint16)
     T, k = weights.shape
     d = y_perm.shape[1]
     y = np.zeros((T, d), np.float32)
     rc = lib().oracle_combine(T, d, k, _ptr(y_perm), _ptr(pair_pos), _ptr(weights), _ptr(y_shared),
-                              float(routed_scale), _ptr(y))
+                              float(routed_scale), _ptr(residual), _ptr(y))
     _check(rc, "oracle_combine")
     return y
 

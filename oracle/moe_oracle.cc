@@ -224,8 +224,12 @@ int oracle_layer(int T, int d, int E, int k, int h, int hs, const uint16_t* x, c
 // routed aggregation): y[t,i] = y_shared[t,i] + routed_scale *
 // sum_{j<k} weights[t,j] * y_perm[pair_pos[t*k+j], i], with y_perm bf16 rows,
 // y_shared f32 or NULL (zero), everything summed in double, y f32.
+// residual [T,d] bf16 or NULL: the pre-norm block's skip connection ([Blog]
+// §2.2, Figure 2 caption: zero-centred RMSNorm in front of each sub-layer,
+// whose output is added back to the stream), summed with the FFN output
+// before the single rounding.
 int oracle_combine(int T, int d, int k, const uint16_t* y_perm, const int32_t* pair_pos, const float* weights,
-                   const float* y_shared, float routed_scale, float* y) {
+                   const float* y_shared, float routed_scale, const uint16_t* residual, float* y) {
   if (T < 0 || d <= 0 || k < 1 || !y_perm || !pair_pos || !weights || !y) return -1;
   for (int t = 0; t < T; ++t) {
     for (int i = 0; i < d; ++i) {
@@ -235,7 +239,8 @@ int oracle_combine(int T, int d, int k, const uint16_t* y_perm, const int32_t* p
         routed += (double)weights[(size_t)t * k + j] * (double)bf16_value(y_perm[(size_t)row * d + i]);
       }
       const double base = y_shared ? (double)y_shared[(size_t)t * d + i] : 0.0;
-      y[(size_t)t * d + i] = (float)(base + (double)routed_scale * routed);
+      const double skip = residual ? (double)bf16_value(residual[(size_t)t * d + i]) : 0.0;
+      y[(size_t)t * d + i] = (float)(skip + (base + (double)routed_scale * routed));
     }
   }
   return 0;

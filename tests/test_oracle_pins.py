@@ -429,6 +429,28 @@ def test_combine_closed_forms():
     np.testing.assert_allclose(b, 2 * a, rtol=1e-6)
 
 
+def test_combine_residual_is_added_once():
+    # The skip connection: zero expert outputs give the residual back exactly;
+    # otherwise the residual adds to the output of the call without it (the
+    # two differ only by the final f32 rounding).
+    rng = np.random.default_rng(52)
+    T, d, k = 12, 64, 3
+    P = T * k
+    pos = rng.permutation(P).astype(np.int32)
+    res = rand_bf16(rng, (T, d), 2.0)
+    w = rng.random((T, k)).astype(np.float32)
+    zero = np.zeros((P, d), np.uint16)
+    np.testing.assert_array_equal(oracle.combine(zero, pos, w, residual=res), from_bf16(res))
+    y_perm = rand_bf16(rng, (P, d))
+    sh = rng.standard_normal((T, d)).astype(np.float32)
+    a = oracle.combine(y_perm, pos, w, sh, routed_scale=0.5)
+    b = oracle.combine(y_perm, pos, w, sh, routed_scale=0.5, residual=res)
+    np.testing.assert_allclose(b, a.astype(np.float64) + from_bf16(res), rtol=2e-7, atol=1e-6)
+    # The residual is not scaled with the routed part.
+    c = oracle.combine(y_perm, pos, w, None, routed_scale=0.0, residual=res)
+    np.testing.assert_array_equal(c, from_bf16(res))
+
+
 # ---------------------------------------------------------------- rmsnorm --
 
 def test_rmsnorm_matches_library_and_is_scale_invariant():
