@@ -159,17 +159,24 @@ class Workload:
         self.route_summary = torch.empty((2,), dtype=torch.float32, device=dev)
         self.expert_rms = torch.empty((E + 1,), dtype=torch.float32, device=dev)
         self.rms_ratio = torch.empty((2,), dtype=torch.float32, device=dev)
+        self.x_norm = torch.empty_like(self.x)
         torch.cuda.synchronize()
 
-    def step(self, main, ev=None, diag=False):
+    def step(self, main, ev=None, diag=False, prenorm=False):
         """One forward; ev = (step start, before gate_up, after gate_up,
         after down, step end) events; diag: the routing and combine calls
-        with their diagnostic side outputs."""
+        with their diagnostic side outputs; prenorm: the pre-norm block, with
+        x taken as the residual stream, normalised inside the router call
+        into x_norm, and added back inside the combine."""
         import sparse_moe_transformer_ffn_amd as moe
         b, sh, c = self.buf, self.buf.shape, self.cfg
+        x = self.x_norm if prenorm else self.x
         if ev:
             ev[0].record(main)
-        if diag:
+        if prenorm:
+            moe.moe_rmsnorm_route(sh, self.x, None, 1e-6, self.wr, self.b, self.c, self.x_norm, b.topk_ids,
+                                  b.topk_weights, b.expert_counts, b.topk_gap, b.workspace, main)
+        elif diag:
             moe.moe_route_diag(sh, self.x, self.wr, self.b, self.c, b.topk_ids, b.topk_weights, b.expert_counts,
                                b.topk_gap, DIAG_GROUPS, self.p_e, self.f_e, self.route_summary, b.workspace, main)
         else:
@@ -178,7 +185,7 @@ class Workload:
         moe.moe_permute(sh, b.topk_ids, b.expert_offsets, b.perm_pairs, b.pair_pos, b.workspace, main)
         if ev:
             ev[1].record(main)
-        moe.moe_expert_gate_up(sh, self.x, b.expert_offsets, b.perm_pairs, self.w_gu, self.hid, b.workspace, main,
+        moe.moe_expert_gate_up(sh, x, b.expert_offsets, b.perm_pairs, self.w_gu, self.hid, b.workspace, main,
                                ws_gate_up=self.ws_gu, hid_shared=self.hid_shared)
         if ev:
             ev[2].record(main)
@@ -186,7 +193,10 @@ class Workload:
                             hid_shared=self.hid_shared, ws_down=self.ws_d, y_shared=b.y_shared)
         if ev:
             ev[3].record(main)
-        if diag:
+        if prenorm:
+            moe.moe_combine_residual(sh, b.y_perm, b.pair_pos, b.topk_weights, b.y_shared, c.routed_scale, self.x,
+                                     b.y, main)
+        elif diag:
             moe.moe_combine_diag(sh, b.y_perm, b.pair_pos, b.topk_weights, b.y_shared, c.routed_scale, b.y,
                                  b.expert_offsets, self.expert_rms, self.rms_ratio, b.workspace, main)
         else:
@@ -239,6 +249,14 @@ def time_workload(cfg, steps, warmup, dev):
         wl.step(main, dev_ev[i], diag=True)
     torch.cuda.synchronize()
     diag_step = np.array([e[0].elapsed_time(e[4]) for e in dev_ev])
+    # The pre-norm block (RMSNorm fused into the router, residual into the
+    # combine), timed the same way.
+    wl.step(main, prenorm=True)
+    pre_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for i in range(steps):
+        wl.step(main, pre_ev[i], prenorm=True)
+    torch.cuda.synchronize()
+    pre_step = np.array([e[0].elapsed_time(e[4]) for e in pre_ev])
     diag = dict(ep_groups=DIAG_GROUPS, ms_per_step_median=float(np.median(diag_step)),
                 l_ep=float(wl.route_summary[0]), confidence=float(wl.route_summary[1]),
                 rms_min_to_median=float(wl.rms_ratio[0]), rms_max_to_median=float(wl.rms_ratio[1]))
@@ -253,6 +271,8 @@ def time_workload(cfg, steps, warmup, dev):
                n_touched=n_touched, max_load=int(counts.max()), idle_experts=int((counts == 0).sum()), alg=alg)
     diag["overhead_ms"] = diag["ms_per_step_median"] - res["ms_per_step_median"]
     res["diagnostics"] = diag
+    res["prenorm_block"] = {"ms_per_step_median": float(np.median(pre_step)),
+                            "overhead_ms": float(np.median(pre_step)) - res["ms_per_step_median"]}
     return wl, res
 
 
@@ -448,6 +468,7 @@ def main():
                     "gate_up_gbs": gate_up_gbs,
                     "down_gbs": alg["down_bytes"] / (r["down_ms"] * 1e-3) / 1e9},
         "diagnostics": r["diagnostics"],
+        "prenorm_block": r["prenorm_block"],
     }
     out["ep_share"] = time_share(wl, args.steps)
     if not args.no_cpu_baseline:
@@ -475,6 +496,7 @@ def main():
                         "down_tflops": palg["down_flops"] / (p["down_ms"] * 1e-3) / 1e12},
             "touched_experts": p["n_touched"], "max_load": p["max_load"], "idle_experts": p["idle_experts"],
             "diagnostics": p["diagnostics"],
+            "prenorm_block": p["prenorm_block"],
             "ep_share": time_share(pwl, args.prefill_steps),
         }
         del pwl

@@ -26,7 +26,11 @@
  *   moe_shared_swiglu  the always-on shared expert
  *   moe_combine        y = y_shared + routed_scale * sum_j w_j * y_perm[pos]
  *
- * with diagnostic variants of two of them (same outputs, plus side outputs):
+ * with fused variants of the first and last (the RMSNorm in front of the
+ * layer, the residual add behind it):
+ *   moe_rmsnorm_route    RMSNorm(h) -> x_out, then moe_route on it
+ *   moe_combine_residual moe_combine plus the skip connection
+ * and diagnostic variants of two of them (same outputs, plus side outputs):
  *   moe_route_diag     + load-balance and confidence statistics of the routing
  *   moe_combine_diag   + per-expert activation RMS and its spread
  *
@@ -117,6 +121,24 @@ moe_status moe_workspace_bytes(const moe_shape* shape, size_t* bytes);
 moe_status moe_route(const moe_shape* shape, const uint16_t* x, const uint16_t* w_router, const float* sel_bias,
                      const float* logit_bias, int32_t* topk_ids, float* topk_weights, int32_t* expert_counts,
                      float* topk_gap, void* workspace, size_t ws_bytes, void* stream);
+
+/* Pre-norm router: the zero-centred RMSNorm in front of the FFN sub-layer
+ * ([Blog] §2.2, Figure 2 caption; the [Digest] notes the pre-norm placement)
+ * fused with moe_route:
+ *   x_out[t,i] = bf16(h[t,i] / sqrt(mean_i(h[t,:]^2) + eps) * (1 + gamma[i]))
+ * then moe_route on x_out.  x_out is bit-identical to moe_rmsnorm's output
+ * and the routing outputs to moe_route's on it; for batches that take the
+ * router's LDS-staged kernel (>= 1024 tokens) the normalisation runs first
+ * and the router reads x_out back, otherwise the router normalises h as it
+ * loads it.
+ * In:  h [T,d] bf16 (the residual stream); gamma [d] f32 or NULL (unit
+ *      gain); eps >= 0 finite; w_router, sel_bias, logit_bias as moe_route.
+ * Out: x_out [T,d] bf16 (the experts' input; must not alias h), and the
+ *      outputs of moe_route.  The workspace rule is the one of every call.  */
+moe_status moe_rmsnorm_route(const moe_shape* shape, const uint16_t* h, const float* gamma, float eps,
+                             const uint16_t* w_router, const float* sel_bias, const float* logit_bias,
+                             uint16_t* x_out, int32_t* topk_ids, float* topk_weights, int32_t* expert_counts,
+                             float* topk_gap, void* workspace, size_t ws_bytes, void* stream);
 
 /* moe_route plus routing statistics ([Blog] §2.2.2: routing probability
  * p_{t,e}, dispatch fraction f_e, their per-group sums and the EP-level
@@ -221,6 +243,17 @@ moe_status moe_shared_swiglu(const moe_shape* shape, const uint16_t* x, const ui
 moe_status moe_combine(const moe_shape* shape, const uint16_t* y_perm, const int32_t* pair_pos,
                        const float* topk_weights, const float* y_shared, float routed_scale, uint16_t* y,
                        void* stream);
+
+/* moe_combine with the pre-norm block's skip connection ([Blog] §2.2,
+ * Figure 2 caption: the normalised sub-layer's output is added back to the
+ * stream):
+ *   y[t,:] = residual[t,:] + (y_shared[t,:] + routed_scale * sum_j w_j y_perm[..])
+ * in f32, rounded once to bf16.  residual [T,d] bf16 (required, 16-byte
+ * aligned; it may alias y: each element is read before it is written by the
+ * same thread).  Other arguments as moe_combine.                           */
+moe_status moe_combine_residual(const moe_shape* shape, const uint16_t* y_perm, const int32_t* pair_pos,
+                                const float* topk_weights, const float* y_shared, float routed_scale,
+                                const uint16_t* residual, uint16_t* y, void* stream);
 
 /* moe_combine plus the per-expert activation RMS ([Blog] §4.1.2: monitor
  * per-expert activation norms; §4.1.3, Figure 4: maximum against median

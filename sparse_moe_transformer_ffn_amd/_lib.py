@@ -25,6 +25,7 @@ EXPORTS = (
     "moe_status_str", "moe_check_shape", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_swiglu",
     "moe_expert_gate_up", "moe_expert_down", "moe_shared_swiglu", "moe_combine", "moe_rmsnorm", "moe_route_diag",
     "moe_combine_diag", "moe_dense_workspace_bytes", "moe_dense_swiglu", "moe_expert_swiglu_range",
+    "moe_rmsnorm_route", "moe_combine_residual",
 )
 
 
@@ -71,6 +72,9 @@ def lib():
                                        ctypes.c_size_t, _P]
         L.moe_expert_swiglu_range.argtypes = [_SP, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
                                               ctypes.c_size_t, _P]
+        L.moe_rmsnorm_route.argtypes = [_SP, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                         ctypes.c_size_t, _P]
+        L.moe_combine_residual.argtypes = [_SP, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P]
         L.moe_combine_diag.argtypes = [_SP, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                        _P]
         for name in EXPORTS[1:]:
@@ -216,3 +220,18 @@ def moe_expert_swiglu_range(shape, expert_begin, expert_end, x, expert_offsets, 
     _check("moe_expert_swiglu_range", lib().moe_expert_swiglu_range(
         ctypes.byref(shape), int(expert_begin), int(expert_end), _ptr(x), _ptr(expert_offsets), _ptr(perm_pairs),
         _ptr(w_gate_up), _ptr(w_down), _ptr(y_perm), ws, nb, _stream(stream)))
+
+
+def moe_rmsnorm_route(shape, h, gamma, eps, w_router, sel_bias, logit_bias, x_out, topk_ids, topk_weights,
+                      expert_counts, topk_gap, workspace, stream=None):
+    ws, nb = _ws(workspace)
+    _check("moe_rmsnorm_route", lib().moe_rmsnorm_route(
+        ctypes.byref(shape), _ptr(h), _ptr(gamma), float(eps), _ptr(w_router), _ptr(sel_bias), _ptr(logit_bias),
+        _ptr(x_out), _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_counts), _ptr(topk_gap), ws, nb,
+        _stream(stream)))
+
+
+def moe_combine_residual(shape, y_perm, pair_pos, topk_weights, y_shared, routed_scale, residual, y, stream=None):
+    _check("moe_combine_residual", lib().moe_combine_residual(
+        ctypes.byref(shape), _ptr(y_perm), _ptr(pair_pos), _ptr(topk_weights), _ptr(y_shared),
+        float(routed_scale), _ptr(residual), _ptr(y), _stream(stream)))

@@ -95,6 +95,26 @@ moe_status moe_route(const moe_shape* shape, const uint16_t* x, const uint16_t* 
                                       topk_gap, nullptr, workspace, (hipStream_t)stream));
 }
 
+moe_status moe_rmsnorm_route(const moe_shape* shape, const uint16_t* h, const float* gamma, float eps,
+                             const uint16_t* w_router, const float* sel_bias, const float* logit_bias,
+                             uint16_t* x_out, int32_t* topk_ids, float* topk_weights, int32_t* expert_counts,
+                             float* topk_gap, void* workspace, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!h || !w_router || !sel_bias || !x_out || !topk_ids || !topk_weights || !expert_counts)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (h == x_out || !(eps >= 0.0f) || !isfinite(eps)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(h) || !aligned16(x_out) || !aligned16(w_router) || !aligned4(sel_bias) || !aligned4(topk_ids) ||
+      !aligned4(topk_weights) || !aligned4(expert_counts) || (gamma && !aligned4(gamma)) ||
+      (logit_bias && !aligned4(logit_bias)) || (topk_gap && !aligned4(topk_gap)))
+    return MOE_ERR_MISALIGNED;
+  if ((st = check_workspace(shape, workspace, ws_bytes)) != MOE_OK) return st;
+  const moe::RouteNorm norm{gamma, eps, x_out};
+  return hip_status(moe::launch_route(shape->num_tokens, shape->d_model, shape->num_experts, shape->top_k, h,
+                                      w_router, sel_bias, logit_bias, topk_ids, topk_weights, expert_counts,
+                                      topk_gap, nullptr, workspace, (hipStream_t)stream, &norm));
+}
+
 moe_status moe_route_diag(const moe_shape* shape, const uint16_t* x, const uint16_t* w_router, const float* sel_bias,
                           const float* logit_bias, int32_t* topk_ids, float* topk_weights, int32_t* expert_counts,
                           float* topk_gap, int32_t ep_groups, float* p_e, float* f_e, float* summary,
@@ -266,7 +286,22 @@ moe_status moe_combine(const moe_shape* shape, const uint16_t* y_perm, const int
       (y_shared && !aligned16(y_shared)))
     return MOE_ERR_MISALIGNED;
   return hip_status(moe::launch_combine(shape->num_tokens, shape->d_model, shape->top_k, y_perm, pair_pos,
-                                        topk_weights, y_shared, routed_scale, y, nullptr, nullptr,
+                                        topk_weights, y_shared, nullptr, routed_scale, y, nullptr, nullptr,
+                                        (hipStream_t)stream));
+}
+
+moe_status moe_combine_residual(const moe_shape* shape, const uint16_t* y_perm, const int32_t* pair_pos,
+                                const float* topk_weights, const float* y_shared, float routed_scale,
+                                const uint16_t* residual, uint16_t* y, void* stream) {
+  const moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!y_perm || !pair_pos || !topk_weights || !residual || !y) return MOE_ERR_INVALID_ARGUMENT;
+  if (!isfinite(routed_scale)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(y_perm) || !aligned16(y) || !aligned16(residual) || !aligned4(pair_pos) ||
+      !aligned4(topk_weights) || (y_shared && !aligned16(y_shared)))
+    return MOE_ERR_MISALIGNED;
+  return hip_status(moe::launch_combine(shape->num_tokens, shape->d_model, shape->top_k, y_perm, pair_pos,
+                                        topk_weights, y_shared, residual, routed_scale, y, nullptr, nullptr,
                                         (hipStream_t)stream));
 }
 
@@ -285,7 +320,7 @@ moe_status moe_combine_diag(const moe_shape* shape, const uint16_t* y_perm, cons
   if ((st = check_workspace(shape, workspace, ws_bytes)) != MOE_OK) return st;
   const moe::CombineDiag diag{shape->num_experts, expert_offsets, expert_rms, rms_ratio};
   return hip_status(moe::launch_combine(shape->num_tokens, shape->d_model, shape->top_k, y_perm, pair_pos,
-                                        topk_weights, y_shared, routed_scale, y, &diag, workspace,
+                                        topk_weights, y_shared, nullptr, routed_scale, y, &diag, workspace,
                                         (hipStream_t)stream));
 }
 

@@ -8,30 +8,15 @@
 
 namespace moe {
 
-namespace {
-
-__device__ __forceinline__ void unpack8(u32x4 v, float* f) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    f[2 * q] = __uint_as_float(v[q] << 16);
-    f[2 * q + 1] = __uint_as_float(v[q] & 0xffff0000u);
-  }
-}
-
-__device__ __forceinline__ u32x4 pack8(const float* f) {
-  u32x4 v;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) v[q] = f32_to_bf16(f[2 * q]) | (f32_to_bf16(f[2 * q + 1]) << 16);
-  return v;
-}
-
-}  // namespace
-
 // One block per token; each thread owns 8 consecutive columns per step.  The
 // k contributions are summed in slot order (ascending expert id), in f32;
 // the k rows' loads of a step are all issued before the sums, so a step waits
 // on one memory latency rather than k.  KMAX >= k bounds the rows held in
 // registers (8 or kMaxTopK), which sets the occupancy.
+//
+// residual (NULL: none): the pre-norm block's skip connection, added to the
+// f32 result before its one rounding to bf16.  It may alias y (neither is
+// declared restrict): each thread reads its 16 bytes before writing them.
 //
 // DIAG: the rows are already in registers, so the block also forms each
 // row's sum of squares (f32: per thread in column order, then a butterfly
@@ -41,8 +26,9 @@ template <int KMAX, bool DIAG>
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y_perm,
                                                  const int32_t* __restrict__ pair_pos,
                                                  const float* __restrict__ topk_weights,
-                                                 const float* __restrict__ y_shared, float routed_scale, int d,
-                                                 int k, uint16_t* __restrict__ y, float* __restrict__ row_ss,
+                                                 const float* __restrict__ y_shared,
+                                                 const uint16_t* residual, float routed_scale, int d, int k,
+                                                 uint16_t* y, float* __restrict__ row_ss,
                                                  float* __restrict__ shared_ss) {
   __shared__ int pos[KMAX];
   __shared__ float wt[KMAX];
@@ -67,6 +53,7 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y_
       s0 = s[0];
       s1 = s[1];
     }
+    const u32x4 res = residual ? load16(residual + (size_t)t * d + c) : u32x4{0u, 0u, 0u, 0u};
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
@@ -93,6 +80,12 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y_
     } else {
 #pragma unroll
       for (int q = 0; q < 8; ++q) o[q] = routed_scale * acc[q];
+    }
+    if (residual) {
+      float rv[8];
+      unpack8(res, rv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) o[q] = rv[q] + o[q];
     }
     *reinterpret_cast<u32x4*>(y + (size_t)t * d + c) = pack8(o);
   }
@@ -219,27 +212,27 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const uint16_t* __restrict__ in
   for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
   if (tid % kWave == 0) part[tid / kWave] = ss;
   __syncthreads();
-  const float total = (part[0] + part[1]) + (part[2] + part[3]);
-  const float inv = 1.0f / sqrtf(total / (float)cols + eps);
+  const float inv = rms_inv((part[0] + part[1]) + (part[2] + part[3]), cols, eps);
   for (int c = tid * 8; c < cols; c += 256 * 8) {
     float v[8];
     unpack8(load16(src + c), v);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = v[q] * inv * (gamma ? 1.0f + gamma[c + q] : 1.0f);
+    for (int q = 0; q < 8; ++q) v[q] = rms_scale(v[q], inv, gamma, c + q);
     *reinterpret_cast<u32x4*>(out + (size_t)row * cols + c) = pack8(v);
   }
 }
 
 hipError_t launch_combine(int T, int d, int k, const uint16_t* y_perm, const int32_t* pair_pos,
-                          const float* topk_weights, const float* y_shared, float routed_scale, uint16_t* y,
-                          const CombineDiag* diag, void* workspace, hipStream_t stream) {
+                          const float* topk_weights, const float* y_shared, const uint16_t* residual,
+                          float routed_scale, uint16_t* y, const CombineDiag* diag, void* workspace,
+                          hipStream_t stream) {
   float* row_ss = diag ? static_cast<float*>(workspace) : nullptr;
   float* shared_ss = diag && y_shared ? row_ss + (size_t)T * k : nullptr;
   hipError_t err;
   if (T > 0) {
 #define MOE_COMBINE(KMAX, DIAG)                                                                                   \
   hipLaunchKernelGGL((k_combine<KMAX, DIAG>), dim3(T), dim3(256), 0, stream, y_perm, pair_pos, topk_weights, y_shared, \
-                     routed_scale, d, k, y, row_ss, shared_ss)
+                     residual, routed_scale, d, k, y, row_ss, shared_ss)
     if (k <= 8) {
       if (diag) MOE_COMBINE(8, true);
       else MOE_COMBINE(8, false);

@@ -45,4 +45,31 @@ __device__ __forceinline__ int xcd_contiguous(int bid, int nblocks) {
 
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
 
+// Eight bf16 values (one 16-byte load) <-> eight floats.
+__device__ __forceinline__ void unpack8(u32x4 v, float* f) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f[2 * q] = __uint_as_float(v[q] << 16);
+    f[2 * q + 1] = __uint_as_float(v[q] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ u32x4 pack8(const float* f) {
+  u32x4 v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = f32_to_bf16(f[2 * q]) | (f32_to_bf16(f[2 * q + 1]) << 16);
+  return v;
+}
+
+// Zero-centred RMSNorm pieces, shared by every kernel that normalises rows
+// so that they all produce the same bits: the inverse RMS from a row's sum
+// of squares, and one normalised element v / rms * (1 + gamma_i).
+__device__ __forceinline__ float rms_inv(float sum_sq, int cols, float eps) {
+  return 1.0f / sqrtf(sum_sq / (float)cols + eps);
+}
+
+__device__ __forceinline__ float rms_scale(float v, float inv, const float* gamma, int i) {
+  return v * inv * (gamma ? 1.0f + gamma[i] : 1.0f);
+}
+
 }  // namespace moe

@@ -27,10 +27,18 @@ struct RouteDiag {
   float* f_e;
   float* summary;
 };
+// RMSNorm in front of the router: x is the un-normalised stream h, and the
+// normalised rows bf16(h / rms(h) * (1 + gamma)) are written to x_out (the
+// experts' input) and routed.
+struct RouteNorm {
+  const float* gamma;
+  float eps;
+  uint16_t* x_out;
+};
 hipError_t launch_route(int T, int d, int E, int k, const uint16_t* x, const uint16_t* w_router,
                         const float* sel_bias, const float* logit_bias, int32_t* topk_ids, float* topk_weights,
                         int32_t* counts, float* topk_gap, const RouteDiag* diag, void* workspace,
-                        hipStream_t stream);
+                        hipStream_t stream, const RouteNorm* norm = nullptr);
 size_t route_workspace_bytes(int T, int d, int E);
 
 hipError_t launch_permute(int T, int E, int k, const int32_t* topk_ids, int32_t* expert_offsets,
@@ -73,8 +81,9 @@ struct CombineDiag {
   float* ratio;
 };
 hipError_t launch_combine(int T, int d, int k, const uint16_t* y_perm, const int32_t* pair_pos,
-                          const float* topk_weights, const float* y_shared, float routed_scale, uint16_t* y,
-                          const CombineDiag* diag, void* workspace, hipStream_t stream);
+                          const float* topk_weights, const float* y_shared, const uint16_t* residual,
+                          float routed_scale, uint16_t* y, const CombineDiag* diag, void* workspace,
+                          hipStream_t stream);
 size_t combine_diag_workspace_bytes(int T, int k);
 hipError_t launch_rmsnorm(int rows, int cols, const uint16_t* in, const float* gamma, float eps, uint16_t* out,
                           hipStream_t stream);

@@ -14,16 +14,57 @@ namespace moe {
 // x[t,:] . w_router[e,:].  One wave computes a 16-token x 16-expert tile; a
 // block of four waves covers 64 experts.  Grid: (ceil(E/64), ceil(T/16), ks).
 // Block (0,0,0) also clears expert_counts for the selection kernel.
+//
+// NORM: x is the un-normalised stream h.  The block first forms the sum of
+// squares of its 16 rows exactly as k_rmsnorm does (thread tid: columns
+// 8 tid + 2048 j in order, a butterfly over the wave, the four waves in
+// order), then normalises each 16-byte slice of x as it loads it, rounding
+// to bf16 as k_rmsnorm does; the blocks of the first expert column also store
+// their slices to x_out, so x_out matches moe_rmsnorm bit for bit.
+template <bool NORM>
 __global__ __launch_bounds__(256) void k_route_logits(const uint16_t* __restrict__ x,
                                                       const uint16_t* __restrict__ w_router, int T, int d, int E,
                                                       int kchunk, float* __restrict__ partial,
-                                                      int32_t* __restrict__ counts) {
+                                                      int32_t* __restrict__ counts, const float* __restrict__ gamma,
+                                                      float eps, uint16_t* __restrict__ x_out) {
   const int tid = threadIdx.x;
   if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
     for (int e = tid; e < E; e += 256) counts[e] = 0;
   const int wave = tid / kWave, lane = tid % kWave;
   const int r16 = lane & 15, kq = lane >> 4;
   const int t0 = blockIdx.y * 16;
+  float inv = 1.f;
+  if constexpr (NORM) {
+    __shared__ float part[16][4];
+    __shared__ float inv_s[16];
+    float ss[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ss[r] = 0.f;
+    for (int c = tid * 8; c < d; c += 256 * 8) {
+      u32x4 v[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        v[r] = t0 + r < T ? load16(x + (size_t)(t0 + r) * d + c) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float f[8];
+        unpack8(v[r], f);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) ss[r] = fmaf(f[q], f[q], ss[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v = ss[r];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+      if (lane == 0) part[r][wave] = v;
+    }
+    __syncthreads();
+    if (tid < 16) inv_s[tid] = rms_inv((part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]), d, eps);
+    __syncthreads();
+    inv = inv_s[r16];
+  }
   const int e0 = blockIdx.x * 64 + wave * 16;
   if (e0 >= E) return;
   const int k_begin = blockIdx.z * kchunk;
@@ -34,10 +75,20 @@ __global__ __launch_bounds__(256) void k_route_logits(const uint16_t* __restrict
   const uint16_t* pb = w_router + (size_t)(vb ? eb : 0) * d + kq * 8;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const bool store_x = NORM && va && blockIdx.x == 0 && wave == 0;
 #pragma unroll 4
   for (int kk = k_begin; kk < k_end; kk += 32) {
-    const u32x4 a = va ? load16(pa + kk) : zero;
+    u32x4 a = va ? load16(pa + kk) : zero;
     const u32x4 b = vb ? load16(pb + kk) : zero;
+    if constexpr (NORM) {
+      const int c = kk + kq * 8;
+      float f[8];
+      unpack8(a, f);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) f[q] = rms_scale(f[q], inv, gamma, c + q);
+      a = va ? pack8(f) : zero;
+      if (store_x) *reinterpret_cast<u32x4*>(x_out + (size_t)ta * d + c) = a;
+    }
     acc = mfma_16x16x32(a, b, acc);
   }
   const int e = e0 + r16;
@@ -510,7 +561,7 @@ size_t logits_bytes(int T, int d, int E) {
 hipError_t launch_route(int T, int d, int E, int k, const uint16_t* x, const uint16_t* w_router,
                         const float* sel_bias, const float* logit_bias, int32_t* topk_ids, float* topk_weights,
                         int32_t* counts, float* topk_gap, const RouteDiag* diag, void* workspace,
-                        hipStream_t stream) {
+                        hipStream_t stream, const RouteNorm* norm) {
   if (T == 0) {
     hipLaunchKernelGGL(k_zero_i32, dim3((E + 255) / 256), dim3(256), 0, stream, counts, E);
     if (diag)
@@ -520,14 +571,24 @@ hipError_t launch_route(int T, int d, int E, int k, const uint16_t* x, const uin
   }
   const RouteSplit rs = route_split(T, d, E);
   float* partial = static_cast<float*>(workspace);
-  if (rs.tiled)
+  hipError_t err;
+  if (rs.tiled) {
+    // The staged kernel loads x straight into LDS, so the normalised rows
+    // are formed first and routed from x_out.
+    if (norm) {
+      if ((err = launch_rmsnorm(T, d, x, norm->gamma, norm->eps, norm->x_out, stream)) != hipSuccess) return err;
+      x = norm->x_out;
+    }
     hipLaunchKernelGGL(k_route_logits_tiled, dim3((T + kRtM - 1) / kRtM, rs.ksplit), dim3(256), 0, stream, x,
                        w_router, T, d, E, rs.kchunk, partial, counts);
-  else
-    hipLaunchKernelGGL(k_route_logits, dim3((E + 63) / 64, (T + 15) / 16, rs.ksplit), dim3(256), 0, stream, x,
-                       w_router, T, d, E, rs.kchunk, partial, counts);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  } else if (norm) {
+    hipLaunchKernelGGL(k_route_logits<true>, dim3((E + 63) / 64, (T + 15) / 16, rs.ksplit), dim3(256), 0, stream,
+                       x, w_router, T, d, E, rs.kchunk, partial, counts, norm->gamma, norm->eps, norm->x_out);
+  } else {
+    hipLaunchKernelGGL(k_route_logits<false>, dim3((E + 63) / 64, (T + 15) / 16, rs.ksplit), dim3(256), 0, stream,
+                       x, w_router, T, d, E, rs.kchunk, partial, counts, nullptr, 0.f, nullptr);
+  }
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   const int tpw = select_tpw(T);
   const int nw = (T + tpw - 1) / tpw;
   char* diag_base = static_cast<char*>(workspace) + logits_bytes(T, d, E);

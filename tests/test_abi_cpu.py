@@ -246,3 +246,34 @@ def test_expert_range_validation():
     assert call(off=A + 2) == MISALIGNED
     assert call(wgu=A + 8) == MISALIGNED
     assert call(nbytes=nb - 256) == WS_SMALL
+
+
+def test_fused_norm_and_residual_validation():
+    s = shape(1)
+    L = moe.lib()
+    nb = moe.moe_workspace_bytes(s)
+    eps = ctypes.c_float(1e-6)
+
+    def route(h=A, x_out=A + 4096, e=eps, gamma=None, ws=A, nbytes=nb):
+        # moe_rmsnorm_route(shape, h, gamma, eps, w, b, c, x_out, ids, wts, cnt, gap, ws, nb, stream)
+        return L.moe_rmsnorm_route(ctypes.byref(s), h, gamma, e, A, A, None, x_out, A, A, A, None, ws, nbytes, None)
+
+    assert route(h=None) == INVALID
+    assert route(x_out=None) == INVALID
+    assert route(x_out=A) == INVALID                      # aliases h
+    assert route(e=ctypes.c_float(-1.0)) == INVALID
+    assert route(e=ctypes.c_float(float("inf"))) == INVALID
+    assert route(h=MIS) == MISALIGNED
+    assert route(x_out=A + 4098) == MISALIGNED
+    assert route(gamma=A + 2) == MISALIGNED
+    assert route(ws=None) == INVALID
+    assert route(nbytes=nb - 256) == WS_SMALL
+    one = ctypes.c_float(1.0)
+
+    def comb(res=A, scale=one, y=A + 4096):
+        return L.moe_combine_residual(ctypes.byref(s), A, A, A, None, scale, res, y, None)
+
+    assert comb(res=None) == INVALID
+    assert comb(scale=ctypes.c_float(float("nan"))) == INVALID
+    assert comb(res=A + 8) == MISALIGNED
+    assert comb(y=A + 8) == MISALIGNED
