@@ -37,8 +37,9 @@ def lib():
         L.oracle_combine.argtypes = [_I, _I, _I, _P, _P, _P, _P, ctypes.c_float, _P, _P]
         L.oracle_route_diag.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P]
         L.oracle_activation_rms.argtypes = [_I, _I, _P, _P]
+        L.oracle_expert_clamped.argtypes = [_I, _I, _P, _P, _P, ctypes.c_double, _P]
         for f in (L.oracle_route, L.oracle_permute, L.oracle_expert, L.oracle_layer, L.oracle_rmsnorm,
-                  L.oracle_combine, L.oracle_route_diag, L.oracle_activation_rms):
+                  L.oracle_combine, L.oracle_route_diag, L.oracle_activation_rms, L.oracle_expert_clamped):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -100,6 +101,19 @@ def expert(x_row, w_gu, w_d):
     h = w_gu.shape[0] // 2
     out = np.zeros(d, np.float32)
     _check(lib().oracle_expert(d, h, _ptr(x_row), _ptr(w_gu), _ptr(w_d), _ptr(out)), "oracle_expert")
+    return out
+
+
+def expert_clamped(x_row, w_gu, w_d, clamp):
+    """oracle expert with every hidden activation clipped to [-clamp, clamp]."""
+    x_row = _c(x_row, np.uint16)
+    w_gu = _c(w_gu, np.uint16)
+    w_d = _c(w_d, np.uint16)
+    d = x_row.shape[0]
+    h = w_gu.shape[0] // 2
+    out = np.zeros(d, np.float32)
+    _check(lib().oracle_expert_clamped(d, h, _ptr(x_row), _ptr(w_gu), _ptr(w_d), float(clamp), _ptr(out)),
+           "oracle_expert_clamped")
     return out
 
 

@@ -109,12 +109,19 @@ void route_token(int d, int E, int k, const uint16_t* x_row, const uint16_t* w_r
 
 // One SwiGLU expert on one token: out = W_d (SiLU(W_g x) * (W_u x)).
 // w_gu is [2h, d] (rows 0..h-1 gate, h..2h-1 up), w_d is [d, h].
-void swiglu_token(int d, int h, const uint16_t* x_row, const uint16_t* w_gu, const uint16_t* w_d, float* out) {
+// clamp > 0: each hidden activation is clipped to [-clamp, clamp] (activation
+// clipping, [Blog] §4.1.3 and Figure 4; placed on the SwiGLU product, where
+// the [Digest] locates the sparse huge activations of aligned gate and up
+// branches).
+void swiglu_token(int d, int h, const uint16_t* x_row, const uint16_t* w_gu, const uint16_t* w_d, float* out,
+                  double clamp = 0.0) {
   std::vector<float> act(h);
   for (int j = 0; j < h; ++j) {
     const float g = dot_bf16(w_gu + (size_t)j * d, x_row, d);
     const float u = dot_bf16(w_gu + (size_t)(h + j) * d, x_row, d);
-    act[j] = (float)((double)g * sigmoid((double)g) * (double)u);
+    double a = (double)g * sigmoid((double)g) * (double)u;
+    if (clamp > 0.0) a = std::min(std::max(a, -clamp), clamp);
+    act[j] = (float)a;
   }
   for (int i = 0; i < d; ++i) {
     double acc = 0.0;
@@ -174,6 +181,15 @@ int oracle_permute(int T, int E, int k, const int32_t* topk_ids, int32_t* counts
 int oracle_expert(int d, int h, const uint16_t* x_row, const uint16_t* w_gu, const uint16_t* w_d, float* out) {
   if (d <= 0 || h <= 0 || !x_row || !w_gu || !w_d || !out) return -1;
   swiglu_token(d, h, x_row, w_gu, w_d, out);
+  return 0;
+}
+
+// oracle_expert with the hidden activations clipped to [-clamp, clamp]
+// (clamp > 0).
+int oracle_expert_clamped(int d, int h, const uint16_t* x_row, const uint16_t* w_gu, const uint16_t* w_d,
+                          double clamp, float* out) {
+  if (d <= 0 || h <= 0 || !x_row || !w_gu || !w_d || !out || !(clamp > 0.0)) return -1;
+  swiglu_token(d, h, x_row, w_gu, w_d, out, clamp);
   return 0;
 }
 

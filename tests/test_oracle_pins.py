@@ -287,6 +287,36 @@ def test_expert_permutation_matrix_closed_form():
     np.testing.assert_allclose(out, expect, rtol=1e-6, atol=1e-30)
 
 
+def test_expert_clamped_closed_form():
+    # The permutation-matrix expert again: out_i is one hidden activation, so
+    # clipping shows up element by element as numpy's clip of the closed form.
+    # A clamp above every activation changes nothing.
+    rng = np.random.default_rng(23)
+    d, h = 64, 32
+    pi = rng.permutation(d)[:h]
+    rho = rng.permutation(d)[:h]
+    tau = rng.integers(0, h, d)
+    c = np.linspace(-3, 3, h).astype(np.float32)
+    gu = np.zeros((2 * h, d), np.float32)
+    gu[np.arange(h), pi] = c
+    gu[h + np.arange(h), rho] = 2.5
+    wd = np.zeros((d, h), np.float32)
+    wd[np.arange(d), tau] = 1.0
+    x = rand_bf16(rng, d, 2.0)
+    xf = from_bf16(x).astype(np.float64)
+    cf = from_bf16(to_bf16(c)).astype(np.float64)
+    act = F.silu(torch.from_numpy(cf[tau] * xf[pi[tau]])).numpy() * 2.5 * xf[rho[tau]]
+    for clamp in (0.05, 0.5, 2.0):
+        out = oracle.expert_clamped(x, to_bf16(gu), to_bf16(wd), clamp)
+        np.testing.assert_allclose(out, np.clip(act, -clamp, clamp), rtol=1e-6, atol=1e-30)
+        assert np.any(np.abs(act) > clamp)
+    big = float(np.abs(act).max()) * 2
+    np.testing.assert_array_equal(oracle.expert_clamped(x, to_bf16(gu), to_bf16(wd), big),
+                                  oracle.expert(x, to_bf16(gu), to_bf16(wd)))
+    with pytest.raises(ValueError):
+        oracle.expert_clamped(x, to_bf16(gu), to_bf16(wd), 0.0)
+
+
 def test_expert_matches_library_swiglu():
     rng = np.random.default_rng(22)
     d, h = 128, 64
