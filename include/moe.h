@@ -21,8 +21,9 @@
  *   moe_permute        stable (expert, token) permutation of the k*T pairs
  *   moe_expert_swiglu  grouped gate/up GEMM + SwiGLU, then grouped down GEMM
  *                      (also callable as its two phases, moe_expert_gate_up
- *                      and moe_expert_down, and on a contiguous share of the
- *                      experts, moe_expert_swiglu_range)
+ *                      and moe_expert_down, on a contiguous share of the
+ *                      experts, moe_expert_swiglu_range, and with clipped
+ *                      hidden activations, moe_expert_swiglu_clamped)
  *   moe_shared_swiglu  the always-on shared expert
  *   moe_combine        y = y_shared + routed_scale * sum_j w_j * y_perm[pos]
  *
@@ -190,6 +191,21 @@ moe_status moe_expert_swiglu(const moe_shape* shape, const uint16_t* x, const in
                              const int32_t* perm_pairs, const uint16_t* w_gate_up, const uint16_t* w_down,
                              const uint16_t* ws_gate_up, const uint16_t* ws_down, uint16_t* y_perm, float* y_shared,
                              void* workspace, size_t ws_bytes, void* stream);
+
+/* moe_expert_swiglu with activation clipping ([Blog] §4.1.3 and Figure 4:
+ * clipping the activations, unlike the weights, keeps the largest expert
+ * output norm bounded in the deepest MoE layers; the pages give no
+ * threshold): every hidden activation, routed and shared, is clipped to
+ * [-act_clamp, act_clamp] before its bf16 rounding,
+ *   hid = min(max(SiLU(W_g x) * (W_u x), -act_clamp), act_clamp)
+ * (the [Digest] places the sparse huge activations in the product of the
+ * aligned gate and up branches).  act_clamp > 0 and finite, else
+ * MOE_ERR_INVALID_ARGUMENT.  Other arguments as moe_expert_swiglu.        */
+moe_status moe_expert_swiglu_clamped(const moe_shape* shape, const uint16_t* x, const int32_t* expert_offsets,
+                                     const int32_t* perm_pairs, const uint16_t* w_gate_up, const uint16_t* w_down,
+                                     const uint16_t* ws_gate_up, const uint16_t* ws_down, uint16_t* y_perm,
+                                     float* y_shared, float act_clamp, void* workspace, size_t ws_bytes,
+                                     void* stream);
 
 /* moe_expert_swiglu on one contiguous share of the experts, as one GPU of
  * an expert-parallel group runs it ([Blog] §2.2: expert parallelism for

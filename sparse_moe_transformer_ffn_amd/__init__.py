@@ -13,14 +13,15 @@ from typing import Optional
 
 from ._lib import (EXPORTS, LIB_PATH, MoeError, lib, make_shape, moe_check_shape, moe_combine, moe_combine_diag,
                    moe_combine_residual, moe_dense_swiglu, moe_dense_workspace_bytes, moe_expert_down,
-                   moe_expert_gate_up, moe_expert_swiglu, moe_expert_swiglu_range, moe_permute, moe_rmsnorm,
+                   moe_expert_gate_up, moe_expert_swiglu, moe_expert_swiglu_clamped, moe_expert_swiglu_range,
+                   moe_permute, moe_rmsnorm,
                    moe_rmsnorm_route, moe_route, moe_route_diag, moe_shape, moe_shared_swiglu, moe_status_str,
                    moe_workspace_bytes)
 
 __all__ = [
     "EXPORTS", "LIB_PATH", "MoeError", "lib", "make_shape", "moe_check_shape", "moe_combine", "moe_combine_diag",
     "moe_combine_residual", "moe_dense_swiglu", "moe_dense_workspace_bytes", "moe_expert_down", "moe_expert_gate_up",
-    "moe_expert_swiglu", "moe_expert_swiglu_range", "moe_permute", "moe_rmsnorm", "moe_rmsnorm_route", "moe_route",
+    "moe_expert_swiglu", "moe_expert_swiglu_clamped", "moe_expert_swiglu_range", "moe_permute", "moe_rmsnorm", "moe_rmsnorm_route", "moe_route",
     "moe_route_diag", "moe_shape", "moe_shared_swiglu", "moe_status_str", "moe_workspace_bytes", "LayerBuffers",
 ]
 

@@ -25,7 +25,7 @@ EXPORTS = (
     "moe_status_str", "moe_check_shape", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_swiglu",
     "moe_expert_gate_up", "moe_expert_down", "moe_shared_swiglu", "moe_combine", "moe_rmsnorm", "moe_route_diag",
     "moe_combine_diag", "moe_dense_workspace_bytes", "moe_dense_swiglu", "moe_expert_swiglu_range",
-    "moe_rmsnorm_route", "moe_combine_residual",
+    "moe_rmsnorm_route", "moe_combine_residual", "moe_expert_swiglu_clamped",
 )
 
 
@@ -75,6 +75,8 @@ def lib():
         L.moe_rmsnorm_route.argtypes = [_SP, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                          ctypes.c_size_t, _P]
         L.moe_combine_residual.argtypes = [_SP, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P]
+        L.moe_expert_swiglu_clamped.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P,
+                                                ctypes.c_size_t, _P]
         L.moe_combine_diag.argtypes = [_SP, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                        _P]
         for name in EXPORTS[1:]:
@@ -235,3 +237,11 @@ def moe_combine_residual(shape, y_perm, pair_pos, topk_weights, y_shared, routed
     _check("moe_combine_residual", lib().moe_combine_residual(
         ctypes.byref(shape), _ptr(y_perm), _ptr(pair_pos), _ptr(topk_weights), _ptr(y_shared),
         float(routed_scale), _ptr(residual), _ptr(y), _stream(stream)))
+
+
+def moe_expert_swiglu_clamped(shape, x, expert_offsets, perm_pairs, w_gate_up, w_down, y_perm, act_clamp, workspace,
+                              stream=None, ws_gate_up=None, ws_down=None, y_shared=None):
+    ws, nb = _ws(workspace)
+    _check("moe_expert_swiglu_clamped", lib().moe_expert_swiglu_clamped(
+        ctypes.byref(shape), _ptr(x), _ptr(expert_offsets), _ptr(perm_pairs), _ptr(w_gate_up), _ptr(w_down),
+        _ptr(ws_gate_up), _ptr(ws_down), _ptr(y_perm), _ptr(y_shared), float(act_clamp), ws, nb, _stream(stream)))

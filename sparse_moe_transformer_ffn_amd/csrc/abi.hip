@@ -223,6 +223,36 @@ moe_status moe_expert_swiglu(const moe_shape* shape, const uint16_t* x, const in
   return hip_status(err);
 }
 
+moe_status moe_expert_swiglu_clamped(const moe_shape* shape, const uint16_t* x, const int32_t* expert_offsets,
+                                     const int32_t* perm_pairs, const uint16_t* w_gate_up, const uint16_t* w_down,
+                                     const uint16_t* ws_gate_up, const uint16_t* ws_down, uint16_t* y_perm,
+                                     float* y_shared, float act_clamp, void* workspace, size_t ws_bytes,
+                                     void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!(act_clamp > 0.0f) || !isfinite(act_clamp)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!x || !expert_offsets || !perm_pairs || !w_gate_up || !w_down || !y_perm) return MOE_ERR_INVALID_ARGUMENT;
+  bool shared = false;
+  if ((st = shared_set(shape, {ws_gate_up, ws_down, y_shared}, &shared)) != MOE_OK) return st;
+  if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(y_perm) ||
+      !aligned4(expert_offsets) || !aligned4(perm_pairs) ||
+      (shared && (!aligned16(ws_gate_up) || !aligned16(ws_down) || !aligned16(y_shared))))
+    return MOE_ERR_MISALIGNED;
+  if ((st = check_workspace(shape, workspace, ws_bytes)) != MOE_OK) return st;
+  const int T = shape->num_tokens, d = shape->d_model, E = shape->num_experts, k = shape->top_k;
+  const int h = shape->d_expert, hs = shape->d_shared;
+  int32_t* queue = static_cast<int32_t*>(workspace);
+  uint16_t* hid = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + moe::kQueueBytes);
+  uint16_t* hid_shared = shared ? hid + moe::expert_hid_bytes(T, k, h) / 2 : nullptr;
+  hipError_t err = moe::launch_gate_up(T, d, E, k, h, hs, x, expert_offsets, perm_pairs, w_gate_up,
+                                       shared ? ws_gate_up : nullptr, hid, hid_shared, queue, (hipStream_t)stream, 0,
+                                       act_clamp);
+  if (err == hipSuccess)
+    err = moe::launch_down(T, d, E, k, h, hs, expert_offsets, hid, hid_shared, w_down, shared ? ws_down : nullptr,
+                           y_perm, shared ? y_shared : nullptr, queue, (hipStream_t)stream);
+  return hip_status(err);
+}
+
 moe_status moe_expert_swiglu_range(const moe_shape* shape, int32_t expert_begin, int32_t expert_end,
                                    const uint16_t* x, const int32_t* expert_offsets, const int32_t* perm_pairs,
                                    const uint16_t* w_gate_up, const uint16_t* w_down, uint16_t* y_perm,

@@ -45,6 +45,13 @@ __device__ __forceinline__ int xcd_contiguous(int bid, int nblocks) {
 
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
 
+// SwiGLU hidden activation SiLU(g) * u, clipped to [-clamp, clamp] when
+// clamp > 0 (activation clipping; off when clamp <= 0).
+__device__ __forceinline__ float swiglu(float g, float u, float clamp) {
+  const float v = silu(g) * u;
+  return clamp > 0.f ? fminf(fmaxf(v, -clamp), clamp) : v;
+}
+
 // Eight bf16 values (one 16-byte load) <-> eight floats.
 __device__ __forceinline__ void unpack8(u32x4 v, float* f) {
 #pragma unroll

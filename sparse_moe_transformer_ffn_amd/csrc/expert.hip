@@ -36,11 +36,11 @@ constexpr int kUnroll = 8;  // K steps (of 32) per batch of loads
 //         added in wave order (a fixed order: results do not depend on the
 //         schedule).  Items are four times smaller, so the last items of the
 //         launch, which run alone, take a quarter of the time.
-template <int BM, int KW>
+template <int BM, int KW, bool CLAMP = false>
 __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x, Groups gs, int d, int h, int hs,
                                                  const uint16_t* __restrict__ w_gu,
                                                  const uint16_t* __restrict__ ws_gu, uint16_t* __restrict__ hid,
-                                                 uint16_t* __restrict__ hid_shared) {
+                                                 uint16_t* __restrict__ hid_shared, float clamp) {
   __shared__ int ip[kMaxGroups + 1];
   __shared__ int wsum[4];
   constexpr int MB = BM / 16;
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
         const int r = it.m0 + mb * 16 + kq * 4 + i;
         if (r < it.nrows) {
           const float g = ag[mb][i], u = au[mb][i];
-          out[(size_t)(it.row0 + r) * H + j] = (uint16_t)f32_to_bf16(silu(g) * u);
+          out[(size_t)(it.row0 + r) * H + j] = (uint16_t)f32_to_bf16(swiglu(g, u, CLAMP ? clamp : 0.f));
         }
       }
     }
@@ -267,10 +267,10 @@ int pick_bm(int T, int k, int E) {
 
 template <int BM, int KW>
 hipError_t gate_up_bm(const uint16_t* x, const Groups& gs, int d, int h, int hs, const uint16_t* w_gu,
-                      const uint16_t* ws_gu, uint16_t* hid, uint16_t* hid_shared, hipStream_t stream) {
-  const auto kern = k_gate_up<BM, KW>;
+                      const uint16_t* ws_gu, uint16_t* hid, uint16_t* hid_shared, float clamp, hipStream_t stream) {
+  const auto kern = clamp > 0.f ? k_gate_up<BM, KW, true> : k_gate_up<BM, KW, false>;
   hipLaunchKernelGGL(kern, dim3(persistent_grid(kern)), dim3(256), 0, stream, x, gs, d, h, hs, w_gu, ws_gu, hid,
-                     hid_shared);
+                     hid_shared, clamp);
   return hipGetLastError();
 }
 
@@ -288,21 +288,22 @@ hipError_t down_bm(const Groups& gs, int d, int h, int hs, const uint16_t* hid, 
 
 hipError_t launch_gate_up(int T, int d, int E, int k, int h, int hs, const uint16_t* x, const int32_t* offsets,
                           const int32_t* perm, const uint16_t* w_gu, const uint16_t* ws_gu, uint16_t* hid,
-                          uint16_t* hid_shared, int32_t* queue, hipStream_t stream, int e_total) {
+                          uint16_t* hid_shared, int32_t* queue, hipStream_t stream, int e_total, float act_clamp) {
   if (T == 0) return hipSuccess;
   const int et = e_total > 0 ? e_total : E;
   // The tiled gate/up item covers 128 hidden units of each group.
   if (use_tiled(T, k, et, offsets, 2 * hs) && h % 128 == 0 && hs % 128 == 0)
-    return launch_gate_up_tiled(T, d, E, k, h, hs, x, offsets, perm, w_gu, ws_gu, hid, hid_shared, queue, stream);
+    return launch_gate_up_tiled(T, d, E, k, h, hs, x, offsets, perm, w_gu, ws_gu, hid, hid_shared, queue, stream,
+                                act_clamp);
   const Groups gs = make_groups(T, E, k, offsets, perm, ws_gu != nullptr);
   // Reduction split over the waves when every quarter is whole 32-wide steps.
   const bool split = d % 128 == 0;
   if (pick_bm(T, k, offsets ? et : 1) == 16) {
-    if (split) return gate_up_bm<16, 4>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, stream);
-    return gate_up_bm<16, 1>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, stream);
+    if (split) return gate_up_bm<16, 4>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, act_clamp, stream);
+    return gate_up_bm<16, 1>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, act_clamp, stream);
   }
-  if (split) return gate_up_bm<32, 4>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, stream);
-  return gate_up_bm<32, 1>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, stream);
+  if (split) return gate_up_bm<32, 4>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, act_clamp, stream);
+  return gate_up_bm<32, 1>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, act_clamp, stream);
 }
 
 hipError_t launch_down(int T, int d, int E, int k, int h, int hs, const int32_t* offsets, const uint16_t* hid,

@@ -300,17 +300,18 @@ __device__ __forceinline__ void issue_first(const Plan& pl, uint16_t* stage0) {
 }
 
 // PHASE kGateUp: A = x rows (gathered), B rows = gate/up rows, K = d,
-//                out = SiLU(G) * U -> hid / hid_shared (bf16, row stride H).
+//                out = SiLU(G) * U -> hid / hid_shared (bf16, row stride H),
+//                clipped to [-clamp, clamp] when CLAMP.
 // PHASE kDown:   A = hid rows, B rows = W_d rows, K = H,
 //                out -> y_perm (bf16) / y_shared (f32), row stride d.
-template <int PHASE>
+template <int PHASE, bool CLAMP = false>
 __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __restrict__ a_src,
                                                               const uint16_t* __restrict__ a_src_shared, Groups gs,
                                                               int d, int h, int hs, const uint16_t* __restrict__ w,
                                                               const uint16_t* __restrict__ ws,
                                                               uint16_t* __restrict__ out,
                                                               void* __restrict__ out_shared,
-                                                              int* __restrict__ queue) {
+                                                              int* __restrict__ queue, float clamp) {
   __shared__ int ip[kMaxGroups + 1];
   __shared__ int next_item;
   __shared__ int wsum[kWaves];
@@ -399,7 +400,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
 #pragma unroll
             for (int ns = 0; ns < 2; ++ns) {
               const float g = acc[ms][ns][i], u = acc[ms][ns + 2][i];
-              o[grow * H + it.nt * (kTileN / 2) + wn * 64 + ns * 32 + l32] = (uint16_t)f32_to_bf16(silu(g) * u);
+              o[grow * H + it.nt * (kTileN / 2) + wn * 64 + ns * 32 + l32] =
+                  (uint16_t)f32_to_bf16(swiglu(g, u, CLAMP ? clamp : 0.f));
             }
           } else {
 #pragma unroll
@@ -429,13 +431,13 @@ __global__ void k_clear_queue(int* queue) {
 
 hipError_t launch_gate_up_tiled(int T, int d, int E, int k, int h, int hs, const uint16_t* x, const int32_t* offsets,
                                 const int32_t* perm, const uint16_t* w_gu, const uint16_t* ws_gu, uint16_t* hid,
-                                uint16_t* hid_shared, int32_t* queue, hipStream_t stream) {
+                                uint16_t* hid_shared, int32_t* queue, hipStream_t stream, float act_clamp) {
   if (T == 0) return hipSuccess;
   const Groups gs = make_groups(T, E, k, offsets, perm, ws_gu != nullptr);
   hipLaunchKernelGGL(k_clear_queue, dim3(1), dim3(64), 0, stream, queue);
-  const auto kern = k_expert_tiled<kGateUp>;
+  const auto kern = act_clamp > 0.f ? k_expert_tiled<kGateUp, true> : k_expert_tiled<kGateUp, false>;
   hipLaunchKernelGGL(kern, dim3(persistent_grid(kern, kThreads)), dim3(kThreads), 0, stream, x, x, gs, d, h, hs,
-                     w_gu, ws_gu, hid, static_cast<void*>(hid_shared), queue);
+                     w_gu, ws_gu, hid, static_cast<void*>(hid_shared), queue, act_clamp);
   return hipGetLastError();
 }
 
@@ -447,7 +449,7 @@ hipError_t launch_down_tiled(int T, int d, int E, int k, int h, int hs, const in
   hipLaunchKernelGGL(k_clear_queue, dim3(1), dim3(64), 0, stream, queue);
   const auto kern = k_expert_tiled<kDown>;
   hipLaunchKernelGGL(kern, dim3(persistent_grid(kern, kThreads)), dim3(kThreads), 0, stream, hid, hid_shared, gs, d,
-                     h, hs, w_down, ws_down, y_perm, static_cast<void*>(y_shared), queue);
+                     h, hs, w_down, ws_down, y_perm, static_cast<void*>(y_shared), queue, 0.f);
   return hipGetLastError();
 }
 

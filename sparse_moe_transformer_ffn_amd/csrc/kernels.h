@@ -53,10 +53,12 @@ constexpr size_t kQueueBytes = 256;
 // e_total: the experts the routing chose among, when the routed groups are a
 // contiguous share of them (offsets then points at the share's first entry
 // and E counts the share); 0 means E.  It sets the regime, which follows the
-// average rows per expert.
+// average rows per expert.  act_clamp > 0 clips every hidden activation to
+// [-act_clamp, act_clamp] before its bf16 rounding.
 hipError_t launch_gate_up(int T, int d, int E, int k, int h, int hs, const uint16_t* x, const int32_t* offsets,
                           const int32_t* perm, const uint16_t* w_gu, const uint16_t* ws_gu, uint16_t* hid,
-                          uint16_t* hid_shared, int32_t* queue, hipStream_t stream, int e_total = 0);
+                          uint16_t* hid_shared, int32_t* queue, hipStream_t stream, int e_total = 0,
+                          float act_clamp = 0.f);
 hipError_t launch_down(int T, int d, int E, int k, int h, int hs, const int32_t* offsets, const uint16_t* hid,
                        const uint16_t* hid_shared, const uint16_t* w_down, const uint16_t* ws_down, uint16_t* y_perm,
                        float* y_shared, int32_t* queue, hipStream_t stream, int e_total = 0);
@@ -64,7 +66,7 @@ hipError_t launch_down(int T, int d, int E, int k, int h, int hs, const int32_t*
 // phases; the launchers above pick them when groups are large.
 hipError_t launch_gate_up_tiled(int T, int d, int E, int k, int h, int hs, const uint16_t* x, const int32_t* offsets,
                                 const int32_t* perm, const uint16_t* w_gu, const uint16_t* ws_gu, uint16_t* hid,
-                                uint16_t* hid_shared, int32_t* queue, hipStream_t stream);
+                                uint16_t* hid_shared, int32_t* queue, hipStream_t stream, float act_clamp = 0.f);
 hipError_t launch_down_tiled(int T, int d, int E, int k, int h, int hs, const int32_t* offsets, const uint16_t* hid,
                              const uint16_t* hid_shared, const uint16_t* w_down, const uint16_t* ws_down,
                              uint16_t* y_perm, float* y_shared, int32_t* queue, hipStream_t stream);

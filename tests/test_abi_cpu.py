@@ -277,3 +277,21 @@ def test_fused_norm_and_residual_validation():
     assert comb(scale=ctypes.c_float(float("nan"))) == INVALID
     assert comb(res=A + 8) == MISALIGNED
     assert comb(y=A + 8) == MISALIGNED
+
+
+def test_expert_clamped_validation():
+    s = shape(1)
+    L = moe.lib()
+    nb = moe.moe_workspace_bytes(s)
+
+    def call(clamp=1.0, x=A, ysh=None, nbytes=nb):
+        # (shape, x, off, perm, w_gu, w_d, ws_gu, ws_d, y_perm, y_shared, act_clamp, ws, nb, stream)
+        return L.moe_expert_swiglu_clamped(ctypes.byref(s), x, A, A, A, A, None, None, A, ysh,
+                                           ctypes.c_float(clamp), A, nbytes, None)
+
+    for bad in (0.0, -2.0, float("inf"), float("nan")):
+        assert call(clamp=bad) == INVALID, bad
+    assert call(x=None) == INVALID
+    assert call(ysh=A) == INVALID          # shared pointers come as a set
+    assert call(x=MIS) == MISALIGNED
+    assert call(nbytes=nb - 256) == WS_SMALL
