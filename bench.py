@@ -38,7 +38,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 EXPERT_SOURCES = ("expert.hip", "expert_tiled.hip", "grouped.h", "common.h")
 # Kernel-name patterns of each phase: the streaming kernels (decode) and the
 # LDS-tiled kernels (prefill).
-PHASE_KERNELS = {"gate_up": ("k_gate_up<", "k_expert_tiled<0>"), "down": ("k_down<", "k_expert_tiled<1>")}
+PHASE_KERNELS = {"gate_up": ("k_gate_up<", "k_expert_tiled<0"), "down": ("k_down<", "k_expert_tiled<1")}
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30            # the --copy-probe copy: bytes read, and bytes written, per copy
 
@@ -93,7 +93,7 @@ def write_traffic(pmc_dir):
 
       rocprofv3 --pmc FETCH_SIZE -f csv -d <pmc_dir>/copy_fetch -o copy_fetch -- python3 bench.py --copy-probe
       rocprofv3 --pmc FETCH_SIZE -f csv -d <pmc_dir>/dec_fetch -o dec_fetch -- \
-          python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-prefill
+          python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-prefill --no-extras
       rocprofv3 --pmc FETCH_SIZE -f csv -d <pmc_dir>/pre_fetch -o pre_fetch -- \
           python3 bench.py --steps 2 --warmup 1 --only-prefill
       (and the same three with WRITE_SIZE into *_write)
@@ -221,7 +221,7 @@ def algorithmic(cfg, n_touched):
                 gate_up_flops=gate_up_flops, down_bytes=down_bytes, down_flops=down_flops)
 
 
-def time_workload(cfg, steps, warmup, dev):
+def time_workload(cfg, steps, warmup, dev, extras=True):
     import numpy as np
     import torch
     wl = Workload(cfg, dev)
@@ -241,6 +241,17 @@ def time_workload(cfg, steps, warmup, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = t0.elapsed_time(t1) / steps
+    gate_up_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    down_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    per_step = np.array([e[0].elapsed_time(e[4]) for e in evs])
+    counts = wl.buf.expert_counts.cpu().numpy()
+    n_touched = int((counts > 0).sum())
+    alg = algorithmic(cfg, n_touched)
+    res = dict(ms_per_step=ms, wall_ms_per_step=wall * 1e3 / steps, gate_up_ms=gate_up_ms, down_ms=down_ms,
+               ms_per_step_median=float(np.median(per_step)), ms_per_step_min=float(per_step.min()),
+               n_touched=n_touched, max_load=int(counts.max()), idle_experts=int((counts == 0).sum()), alg=alg)
+    if not extras:
+        return wl, res
     # The same steps with the diagnostic side outputs, timed separately (not
     # part of the headline figure).
     wl.step(main, diag=True)
@@ -260,15 +271,6 @@ def time_workload(cfg, steps, warmup, dev):
     diag = dict(ep_groups=DIAG_GROUPS, ms_per_step_median=float(np.median(diag_step)),
                 l_ep=float(wl.route_summary[0]), confidence=float(wl.route_summary[1]),
                 rms_min_to_median=float(wl.rms_ratio[0]), rms_max_to_median=float(wl.rms_ratio[1]))
-    gate_up_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    down_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-    per_step = np.array([e[0].elapsed_time(e[4]) for e in evs])
-    counts = wl.buf.expert_counts.cpu().numpy()
-    n_touched = int((counts > 0).sum())
-    alg = algorithmic(cfg, n_touched)
-    res = dict(ms_per_step=ms, wall_ms_per_step=wall * 1e3 / steps, gate_up_ms=gate_up_ms, down_ms=down_ms,
-               ms_per_step_median=float(np.median(per_step)), ms_per_step_min=float(per_step.min()),
-               n_touched=n_touched, max_load=int(counts.max()), idle_experts=int((counts == 0).sum()), alg=alg)
     diag["overhead_ms"] = diag["ms_per_step_median"] - res["ms_per_step_median"]
     res["diagnostics"] = diag
     res["prenorm_block"] = {"ms_per_step_median": float(np.median(pre_step)),
@@ -416,6 +418,9 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense SwiGLU FFN lines")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time the layer step only: no diagnostics, pre-norm block, expert share or dense FFN "
+                         "(profiling runs)")
     ap.add_argument("--cpu-sample", type=int, default=64)
     ap.add_argument("--write-traffic", metavar="PMC_DIR",
                     help="no GPU work: write profiles/traffic_*.json from rocprofv3 counter runs in PMC_DIR")
@@ -443,12 +448,13 @@ def main():
         return
     if args.only_prefill:
         pcfg = moegen.CONFIGS[2]
-        _, p = time_workload(pcfg, args.steps, args.warmup, dev)
+        _, p = time_workload(pcfg, args.steps, args.warmup, dev, extras=False)
         print(json.dumps({"workload": pcfg.workload, "ms_per_step": p["ms_per_step"],
                           "gate_up_ms": p["gate_up_ms"], "down_ms": p["down_ms"]}), flush=True)
         return
     cfg = moegen.CONFIGS[1]
-    wl, r = time_workload(cfg, args.steps, args.warmup, dev)
+    extras = not args.no_extras
+    wl, r = time_workload(cfg, args.steps, args.warmup, dev, extras)
     alg = r["alg"]
     tok_s = cfg.T / (r["ms_per_step"] * 1e-3)
     gate_up_gbs = alg["gate_up_bytes"] / (r["gate_up_ms"] * 1e-3) / 1e9
@@ -467,15 +473,16 @@ def main():
         "kernels": {"gate_up_ms": r["gate_up_ms"], "down_ms": r["down_ms"],
                     "gate_up_gbs": gate_up_gbs,
                     "down_gbs": alg["down_bytes"] / (r["down_ms"] * 1e-3) / 1e9},
-        "diagnostics": r["diagnostics"],
-        "prenorm_block": r["prenorm_block"],
     }
-    out["ep_share"] = time_share(wl, args.steps)
+    if extras:
+        out["diagnostics"] = r["diagnostics"]
+        out["prenorm_block"] = r["prenorm_block"]
+        out["ep_share"] = time_share(wl, args.steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
     del wl
     torch.cuda.empty_cache()
-    if not args.no_dense:
+    if extras and not args.no_dense:
         out["dense_ffn"] = {"d_model": cfg.d, "hidden": DENSE_HIDDEN,
                             "decode": time_dense(cfg.T, args.steps, dev),
                             "prefill": None if args.no_prefill else time_dense(moegen.CONFIGS[2].T, 10, dev)}
@@ -483,7 +490,7 @@ def main():
 
     if not args.no_prefill:
         pcfg = moegen.CONFIGS[2]
-        pwl, p = time_workload(pcfg, args.prefill_steps, args.warmup, dev)
+        pwl, p = time_workload(pcfg, args.prefill_steps, args.warmup, dev, extras)
         palg = p["alg"]
         gate_up_tf = palg["gate_up_flops"] / (p["gate_up_ms"] * 1e-3) / 1e12
         step_tf = palg["step_flops"] / (p["ms_per_step"] * 1e-3) / 1e12
@@ -495,10 +502,10 @@ def main():
             "kernels": {"gate_up_ms": p["gate_up_ms"], "down_ms": p["down_ms"],
                         "down_tflops": palg["down_flops"] / (p["down_ms"] * 1e-3) / 1e12},
             "touched_experts": p["n_touched"], "max_load": p["max_load"], "idle_experts": p["idle_experts"],
-            "diagnostics": p["diagnostics"],
-            "prenorm_block": p["prenorm_block"],
-            "ep_share": time_share(pwl, args.prefill_steps),
         }
+        if extras:
+            out["prefill"].update(diagnostics=p["diagnostics"], prenorm_block=p["prenorm_block"],
+                                  ep_share=time_share(pwl, args.prefill_steps))
         del pwl
     print(json.dumps(out), flush=True)
 
