@@ -92,6 +92,14 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & (kSegs - 1); }
 
+// Orders one wave's LDS accesses across its lanes (writes before the reads
+// that follow, reads before the writes that follow).
+__device__ __forceinline__ void wave_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 enum Phase { kGateUp = 0, kDown = 1 };
 
 // Row of N-subtile ns (0..3) of wave column wn inside the 256-row B tile.
@@ -148,11 +156,12 @@ __device__ __forceinline__ u32x4 read_frag(const uint16_t* stage, const ReadMap&
 
 // One K step: the eight MFMAs of `cur` (if MUL), after MFMA i the LDS read i
 // of the next step's fragments (step `s` of `stage` into `nxt`, i < 6, if
-// READ) and, with LOADS, direct load i of chunk `cload` into `other`.  The
-// order is pinned (sched_barrier).
+// READ) and, with LOADS and `issue` (uniform), direct load i of chunk `cload`
+// into `other`.  The order is pinned (sched_barrier).
 template <int PHASE, int NA, bool MUL, bool READ, bool LOADS>
 __device__ __forceinline__ void mma_step(const Frags& cur, Frags& nxt, const uint16_t* stage, const ReadMap& m,
-                                         int s, const Pipe& p, uint16_t* other, int cload, f32x16 (&acc)[2][4]) {
+                                         int s, const Pipe& p, uint16_t* other, int cload, bool issue,
+                                         f32x16 (&acc)[2][4]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     if (MUL) {
@@ -163,7 +172,7 @@ __device__ __forceinline__ void mma_step(const Frags& cur, Frags& nxt, const uin
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (LOADS && load_used<NA>(i)) {
+    if (LOADS && issue && load_used<NA>(i)) {
       __builtin_amdgcn_global_load_lds(p.src[i] + cload * kChunk, other + p.lds_off[i], 16, 0, kPolicy);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -176,18 +185,20 @@ __device__ __forceinline__ void mma_step(const Frags& cur, Frags& nxt, const uin
 // having been consumed by that chunk's MFMAs).  Steps 0-2 read steps 1-3 of
 // `cur`; step 3 only multiplies.  Then each thread waits for its loads of
 // chunk c+1 and the block barrier makes them visible; its first fragments
-// are read last.  Past the last chunk the loads repeat it (an L2 hit into a
-// stage nobody reads) and the final reads fetch unused data, so every chunk
-// issues and waits the same way.  Waves without rows in the item (MUL =
-// false) only load and wait.
+// are read last.  In the down phase the last chunk issues no loads, so both
+// stages are free once the item's K loop ends (its epilogue uses one); in
+// gate/up it repeats its own loads (an L2 hit into a stage nobody reads), so
+// every chunk issues and waits the same way.  The final reads fetch unused
+// data.  Waves without rows in the item (MUL = false) only load and wait.
 template <int PHASE, int NA, bool MUL>
 __device__ __forceinline__ void pipe_chunk(const Pipe& p, const uint16_t* cur, uint16_t* other, int c, int nch,
                                            const ReadMap& m, Frags (&fr)[2], f32x16 (&acc)[2][4]) {
   const int cl = min(c + 1, nch - 1);
-  mma_step<PHASE, NA, MUL, true, true>(fr[0], fr[1], cur, m, 1, p, other, cl, acc);
-  mma_step<PHASE, NA, MUL, true, false>(fr[1], fr[0], cur, m, 2, p, other, cl, acc);
-  mma_step<PHASE, NA, MUL, true, false>(fr[0], fr[1], cur, m, 3, p, other, cl, acc);
-  mma_step<PHASE, NA, MUL, false, false>(fr[1], fr[0], cur, m, 0, p, other, cl, acc);
+  const bool issue = PHASE == kGateUp || c + 1 < nch;
+  mma_step<PHASE, NA, MUL, true, true>(fr[0], fr[1], cur, m, 1, p, other, cl, issue, acc);
+  mma_step<PHASE, NA, MUL, true, false>(fr[1], fr[0], cur, m, 2, p, other, cl, issue, acc);
+  mma_step<PHASE, NA, MUL, true, false>(fr[0], fr[1], cur, m, 3, p, other, cl, issue, acc);
+  mma_step<PHASE, NA, MUL, false, false>(fr[1], fr[0], cur, m, 0, p, other, cl, issue, acc);
   __builtin_amdgcn_s_waitcnt(kWaitAll);
   __builtin_amdgcn_s_barrier();
   if (MUL) {
@@ -384,32 +395,72 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
     }
 
     // Epilogue.  Element i of acc[ms][ns] is row 8*(i/4) + 4*lhi + (i%4) of
-    // M-subtile ms, column l32 of N-subtile ns.
+    // M-subtile ms, column l32 of N-subtile ns.  The routed down output
+    // (bf16, 128 columns per wave) goes through stage1 (free: the down K
+    // loop's last chunk issued no loads, and the next item's first chunk went
+    // to stage0): each wave writes its tile there and reads it back as 16-byte
+    // row segments, so the global stores are whole 16-byte pieces (eight times
+    // fewer than one per element).  Only the wave's own 8 KiB region is
+    // touched, so a wave-level fence orders the writes before the reads and
+    // the reads before the next writes.  The other outputs are stored per
+    // element.
     if (mul) {
       const Item& it = cur.it;
       const int H = cur.H;
+      if (PHASE == kGateUp) {
+        // Unit ns*32 + l32 pairs gate acc[ms][ns] with up acc[ms][ns+2]; the
+        // hidden rows are short (64 units of this wave), stored per element.
+        uint16_t* o = it.shared ? static_cast<uint16_t*>(out_shared) : out;
 #pragma unroll
-      for (int ms = 0; ms < 2; ++ms) {
+        for (int ms = 0; ms < 2; ++ms) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = wave_row0 + ms * 32 + 8 * (i / 4) + 4 * lhi + (i % 4);
-          if (r >= it.nrows) continue;
-          const size_t grow = (size_t)(it.row0 + r);
-          if (PHASE == kGateUp) {
-            uint16_t* o = it.shared ? static_cast<uint16_t*>(out_shared) : out;
+          for (int i = 0; i < 16; ++i) {
+            const int r = wave_row0 + ms * 32 + 8 * (i / 4) + 4 * lhi + (i % 4);
+            if (r >= it.nrows) continue;
+            const size_t grow = (size_t)(it.row0 + r);
 #pragma unroll
             for (int ns = 0; ns < 2; ++ns) {
               const float g = acc[ms][ns][i], u = acc[ms][ns + 2][i];
               o[grow * H + it.nt * (kTileN / 2) + wn * 64 + ns * 32 + l32] =
                   (uint16_t)f32_to_bf16(swiglu(g, u, CLAMP ? clamp : 0.f));
             }
-          } else {
+          }
+        }
+      } else if (!it.shared) {
+        // 64 rows x 128 columns of this wave, in two halves of 32 rows.
+        uint16_t* sb = stage1 + wave * (32 * 128);  // 4096 bf16
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
 #pragma unroll
             for (int ns = 0; ns < 4; ++ns) {
-              const size_t o = grow * d + it.nt * kTileN + wn * 128 + ns * 32 + l32;
-              if (it.shared) static_cast<float*>(out_shared)[o] = acc[ms][ns][i];
-              else out[o] = (uint16_t)f32_to_bf16(acc[ms][ns][i]);
+              const int rr = 8 * (i / 4) + 4 * lhi + (i % 4);
+              sb[rr * 128 + ns * 32 + l32] = (uint16_t)f32_to_bf16(acc[ms][ns][i]);
             }
+          wave_fence();
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {  // 32 rows x 16 segments
+            const int idx = lane + kWave * j, rr = idx / 16, sg = idx % 16;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(sb + rr * 128 + sg * 8);
+            const int r = wave_row0 + ms * 32 + rr;
+            if (r < it.nrows)
+              *reinterpret_cast<u32x4*>(out + (size_t)(it.row0 + r) * d + it.nt * kTileN + wn * 128 + sg * 8) = v;
+          }
+          wave_fence();
+        }
+      } else {
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int r = wave_row0 + ms * 32 + 8 * (i / 4) + 4 * lhi + (i % 4);
+            if (r >= it.nrows) continue;
+            const size_t grow = (size_t)(it.row0 + r);
+#pragma unroll
+            for (int ns = 0; ns < 4; ++ns)
+              static_cast<float*>(out_shared)[grow * d + it.nt * kTileN + wn * 128 + ns * 32 + l32] =
+                  acc[ms][ns][i];
           }
         }
       }
