@@ -156,26 +156,31 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
 //         the reduction, the partial sums added in LDS in wave order: for a
 //         long reduction (the dense FFN's 11,264) with few rows, four times
 //         as many items keep enough waves streaming.
-template <int BM, int KW>
+// KS > 1 (the shared group alone): the reduction is also split over KS
+//         items, each writing its partial sums to partial[ks][row][d] (f32);
+//         k_sum_partials adds them in ks order into y_shared.
+template <int BM, int KW, int KS = 1>
 __global__ __launch_bounds__(256) void k_down(Groups gs, int d, int h, int hs, const uint16_t* __restrict__ hid,
                                               const uint16_t* __restrict__ hid_shared,
                                               const uint16_t* __restrict__ w_down,
                                               const uint16_t* __restrict__ ws_down, uint16_t* __restrict__ y_perm,
-                                              float* __restrict__ y_shared) {
+                                              float* __restrict__ y_shared, float* __restrict__ partial) {
   __shared__ int ip[kMaxGroups + 1];
   __shared__ int wsum[4];
   constexpr int MB = BM / 16;
   constexpr int COLS = 64 / KW;  // output columns per item
   __shared__ float red[KW > 1 ? KW - 1 : 1][MB * 4][kWave];
-  const int items = item_prefix<BM>(ip, wsum, gs, d / COLS, d / COLS);
+  const int ncol = d / COLS;
+  const int items = item_prefix<BM>(ip, wsum, gs, ncol, ncol * KS);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int r16 = lane & 15, kq = lane >> 4;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   for (int w = xcd_contiguous(blockIdx.x, gridDim.x); w < items; w += gridDim.x) {
-    const Item it = decode_item<0>(ip, gs, BM, d / COLS, d / COLS, w);
+    const Item it = decode_item<0>(ip, gs, BM, ncol, ncol * KS, w);
     const int H = it.shared ? hs : h;
-    const int klen = H / KW, kbeg = KW > 1 ? wave * klen : 0;
-    const int n = it.nt * COLS + (KW > 1 ? 0 : wave * 16) + r16;
+    const int ks = KS > 1 ? it.nt / ncol : 0, cg = KS > 1 ? it.nt % ncol : it.nt;
+    const int klen = H / (KW * KS), kbeg = (ks * KW + (KW > 1 ? wave : 0)) * klen;
+    const int n = cg * COLS + (KW > 1 ? 0 : wave * 16) + r16;
     const uint16_t* pb =
         (it.shared ? ws_down : w_down + (size_t)it.group * d * h) + (size_t)n * H + kbeg + kq * 8;
     const uint16_t* src = it.shared ? hid_shared : hid;
@@ -238,11 +243,31 @@ __global__ __launch_bounds__(256) void k_down(Groups gs, int d, int h, int hs, c
         const int r = it.m0 + mb * 16 + kq * 4 + i;
         if (r < it.nrows) {
           const size_t o = (size_t)(it.row0 + r) * d + n;
-          if (it.shared) y_shared[o] = acc[mb][i];
+          if (KS > 1) partial[(size_t)ks * gs.T * d + o] = acc[mb][i];
+          else if (it.shared) y_shared[o] = acc[mb][i];
           else y_perm[o] = (uint16_t)f32_to_bf16(acc[mb][i]);
         }
       }
     }
+  }
+}
+
+// y[i] = sum over k = 0..KS-1 of partial[k][i], in k order (n elements, n a
+// multiple of 4).
+template <int KS>
+__global__ __launch_bounds__(256) void k_sum_partials(const float* __restrict__ partial, size_t n,
+                                                      float* __restrict__ y) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n / 4; i += (size_t)gridDim.x * 256) {
+    float4 s = reinterpret_cast<const float4*>(partial)[i];
+#pragma unroll
+    for (int k = 1; k < KS; ++k) {
+      const float4 v = reinterpret_cast<const float4*>(partial + (size_t)k * n)[i];
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+    reinterpret_cast<float4*>(y)[i] = s;
   }
 }
 
@@ -280,7 +305,23 @@ hipError_t down_bm(const Groups& gs, int d, int h, int hs, const uint16_t* hid, 
                    hipStream_t stream) {
   const auto kern = k_down<BM, KW>;
   hipLaunchKernelGGL(kern, dim3(persistent_grid(kern)), dim3(256), 0, stream, gs, d, h, hs, hid, hid_shared, w_down,
-                     ws_down, y_perm, y_shared);
+                     ws_down, y_perm, y_shared, nullptr);
+  return hipGetLastError();
+}
+
+// The shared group alone with its reduction also split over items.
+template <int BM>
+hipError_t down_bm_split(const Groups& gs, int d, int hs, const uint16_t* hid_shared, const uint16_t* ws_down,
+                         float* y_shared, float* partial, hipStream_t stream) {
+  const auto kern = k_down<BM, 4, kDownSplits>;
+  hipLaunchKernelGGL(kern, dim3(persistent_grid(kern)), dim3(256), 0, stream, gs, d, 0, hs, nullptr, hid_shared,
+                     nullptr, ws_down, nullptr, nullptr, partial);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const size_t n = (size_t)gs.T * d;
+  const size_t blocks = (n / 4 + 255) / 256;
+  hipLaunchKernelGGL(k_sum_partials<kDownSplits>, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0,
+                     stream, partial, n, y_shared);
   return hipGetLastError();
 }
 
@@ -308,7 +349,7 @@ hipError_t launch_gate_up(int T, int d, int E, int k, int h, int hs, const uint1
 
 hipError_t launch_down(int T, int d, int E, int k, int h, int hs, const int32_t* offsets, const uint16_t* hid,
                        const uint16_t* hid_shared, const uint16_t* w_down, const uint16_t* ws_down, uint16_t* y_perm,
-                       float* y_shared, int32_t* queue, hipStream_t stream, int e_total) {
+                       float* y_shared, int32_t* queue, hipStream_t stream, int e_total, float* partial) {
   if (T == 0) return hipSuccess;
   const int et = e_total > 0 ? e_total : E;
   // The tiled down item covers 256 output columns.
@@ -320,12 +361,22 @@ hipError_t launch_down(int T, int d, int E, int k, int h, int hs, const int32_t*
   // of it are too few steps to keep loads in flight.  A long reduction of the
   // shared group alone (the dense FFN) is split over the waves.
   const bool split = !offsets && hs >= 4096 && hs % 128 == 0 && d % 16 == 0;
+  // With few rows that still leaves too few items: split the reduction over
+  // items too, into the caller's partial-sum buffer.
+  if (split && partial && T <= kDownSplitMaxTokens && hs % (128 * kDownSplits) == 0) {
+    if (pick_bm(T, k, 1) == 16) return down_bm_split<16>(gs, d, hs, hid_shared, ws_down, y_shared, partial, stream);
+    return down_bm_split<32>(gs, d, hs, hid_shared, ws_down, y_shared, partial, stream);
+  }
   if (pick_bm(T, k, offsets ? et : 1) == 16) {
     if (split) return down_bm<16, 4>(gs, d, h, hs, hid, hid_shared, w_down, ws_down, y_perm, y_shared, stream);
     return down_bm<16, 1>(gs, d, h, hs, hid, hid_shared, w_down, ws_down, y_perm, y_shared, stream);
   }
   if (split) return down_bm<32, 4>(gs, d, h, hs, hid, hid_shared, w_down, ws_down, y_perm, y_shared, stream);
   return down_bm<32, 1>(gs, d, h, hs, hid, hid_shared, w_down, ws_down, y_perm, y_shared, stream);
+}
+
+size_t down_partial_bytes(int T, int d) {
+  return T <= kDownSplitMaxTokens ? ((size_t)kDownSplits * T * d * sizeof(float) + 255) / 256 * 256 : 0;
 }
 
 size_t expert_hid_bytes(int T, int k, int h) { return ((size_t)T * k * h * sizeof(uint16_t) + 255) / 256 * 256; }

@@ -59,9 +59,16 @@ hipError_t launch_gate_up(int T, int d, int E, int k, int h, int hs, const uint1
                           const int32_t* perm, const uint16_t* w_gu, const uint16_t* ws_gu, uint16_t* hid,
                           uint16_t* hid_shared, int32_t* queue, hipStream_t stream, int e_total = 0,
                           float act_clamp = 0.f);
+// partial: optional f32 scratch of down_partial_bytes(T, d) for a launch of
+// the shared group alone with a long reduction and few rows, which then
+// splits the reduction over kDownSplits items and adds their sums.
+constexpr int kDownSplits = 4;
+constexpr int kDownSplitMaxTokens = 256;
 hipError_t launch_down(int T, int d, int E, int k, int h, int hs, const int32_t* offsets, const uint16_t* hid,
                        const uint16_t* hid_shared, const uint16_t* w_down, const uint16_t* ws_down, uint16_t* y_perm,
-                       float* y_shared, int32_t* queue, hipStream_t stream, int e_total = 0);
+                       float* y_shared, int32_t* queue, hipStream_t stream, int e_total = 0,
+                       float* partial = nullptr);
+size_t down_partial_bytes(int T, int d);
 // The compute-regime (LDS-tiled, MFMA 32x32x16) versions of the same two
 // phases; the launchers above pick them when groups are large.
 hipError_t launch_gate_up_tiled(int T, int d, int E, int k, int h, int hs, const uint16_t* x, const int32_t* offsets,
