@@ -268,6 +268,21 @@ def time_workload(cfg, steps, warmup, dev, extras=True):
         wl.step(main, pre_ev[i], prenorm=True)
     torch.cuda.synchronize()
     pre_step = np.array([e[0].elapsed_time(e[4]) for e in pre_ev])
+    # The step captured once into a HIP graph and replayed (launch costs off
+    # the host; the same kernels).
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        wl.step(torch.cuda.current_stream())
+    graph.replay()
+    g_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, z in g_ev:
+        a.record(main)
+        graph.replay()
+        z.record(main)
+    torch.cuda.synchronize()
+    graph_step = np.array([a.elapsed_time(z) for a, z in g_ev])
+    del graph
     diag = dict(ep_groups=DIAG_GROUPS, ms_per_step_median=float(np.median(diag_step)),
                 l_ep=float(wl.route_summary[0]), confidence=float(wl.route_summary[1]),
                 rms_min_to_median=float(wl.rms_ratio[0]), rms_max_to_median=float(wl.rms_ratio[1]))
@@ -275,6 +290,8 @@ def time_workload(cfg, steps, warmup, dev, extras=True):
     res["diagnostics"] = diag
     res["prenorm_block"] = {"ms_per_step_median": float(np.median(pre_step)),
                             "overhead_ms": float(np.median(pre_step)) - res["ms_per_step_median"]}
+    res["graph_replay"] = {"ms_per_step_median": float(np.median(graph_step)),
+                           "ms_per_step_min": float(graph_step.min())}
     return wl, res
 
 
@@ -477,6 +494,7 @@ def main():
     if extras:
         out["diagnostics"] = r["diagnostics"]
         out["prenorm_block"] = r["prenorm_block"]
+        out["graph_replay"] = r["graph_replay"]
         out["ep_share"] = time_share(wl, args.steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
@@ -505,6 +523,7 @@ def main():
         }
         if extras:
             out["prefill"].update(diagnostics=p["diagnostics"], prenorm_block=p["prenorm_block"],
+                                  graph_replay=p["graph_replay"],
                                   ep_share=time_share(pwl, args.prefill_steps))
         del pwl
     print(json.dumps(out), flush=True)
