@@ -522,6 +522,18 @@ def main():
             "touched_experts": p["n_touched"], "max_load": p["max_load"], "idle_experts": p["idle_experts"],
         }
         if extras:
+            # Supplementary, not one of the workloads: the same batch with a
+            # selection bias of U[-0.005, 0.005], which spreads the loads
+            # nearly evenly over the experts.
+            bcfg = moegen.custom(2, bias=0.005)
+            bwl, bp = time_workload(bcfg, args.prefill_steps, args.warmup, dev, extras=False)
+            del bwl
+            btf = bp["alg"]["step_flops"] / (bp["ms_per_step"] * 1e-3) / 1e12
+            out["prefill"]["balanced_bias_0.005"] = {
+                "ms_per_step_median": bp["ms_per_step_median"], "tok_s": bcfg.T / (bp["ms_per_step"] * 1e-3),
+                "step_tflops": btf, "step_mfma_frac": btf / BF16_PEAK_TFLOPS,
+                "gate_up_tflops": bp["alg"]["gate_up_flops"] / (bp["gate_up_ms"] * 1e-3) / 1e12,
+                "touched_experts": bp["n_touched"], "max_load": bp["max_load"], "idle_experts": bp["idle_experts"]}
             out["prefill"].update(diagnostics=p["diagnostics"], prenorm_block=p["prenorm_block"],
                                   graph_replay=p["graph_replay"],
                                   ep_share=time_share(pwl, args.prefill_steps))
