@@ -34,15 +34,6 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-// Workgroups are dispatched round-robin over the XCDs (block b runs on XCD
-// b % 8).  Renumber them so that each XCD receives one contiguous range of
-// logical tile ids: tiles that share operands then share an L2.
-__device__ __forceinline__ int xcd_contiguous(int bid, int nblocks) {
-  const int per = nblocks / kNumXcd, rem = nblocks % kNumXcd;
-  const int xcd = bid % kNumXcd, idx = bid / kNumXcd;
-  return xcd * per + (xcd < rem ? xcd : rem) + idx;
-}
-
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
 
 // SwiGLU hidden activation SiLU(g) * u, clipped to [-clamp, clamp] when

@@ -25,6 +25,14 @@ namespace {
 
 constexpr int kUnroll = 8;  // K steps (of 32) per batch of loads
 
+// Blocks launched per resident block slot.  Item w goes to block w % grid and
+// block b runs on XCD b % 8, so every round of items is spread over all eight
+// XCDs (an XCD-contiguous order left the last, partial round on the first few
+// XCDs); with four blocks per slot the dispatcher hands the remaining blocks
+// to whichever CU of an XCD frees first, which evens out the tail.  Items of
+// these kernels share no weights, so nothing is lost in L2.
+constexpr int kOversubscribe = 4;
+
 }  // namespace
 
 // Phase 1: hid[row, j] = SiLU(x_row . W_g[j]) * (x_row . W_u[j]).  Routed
@@ -51,7 +59,7 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
   const int r16 = lane & 15, kq = lane >> 4;
   const int klen = d / KW, kbeg = KW > 1 ? wave * klen : 0;
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  for (int w = xcd_contiguous(blockIdx.x, gridDim.x); w < items; w += gridDim.x) {
+  for (int w = (int)blockIdx.x; w < items; w += gridDim.x) {
     const Item it = decode_item<0>(ip, gs, BM, h / UNITS, hs / UNITS, w);
     const int H = it.shared ? hs : h;
     const int j = it.nt * UNITS + (KW > 1 ? 0 : wave * 16) + r16;
@@ -175,7 +183,7 @@ __global__ __launch_bounds__(256) void k_down(Groups gs, int d, int h, int hs, c
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int r16 = lane & 15, kq = lane >> 4;
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  for (int w = xcd_contiguous(blockIdx.x, gridDim.x); w < items; w += gridDim.x) {
+  for (int w = (int)blockIdx.x; w < items; w += gridDim.x) {
     const Item it = decode_item<0>(ip, gs, BM, ncol, ncol * KS, w);
     const int H = it.shared ? hs : h;
     const int ks = KS > 1 ? it.nt / ncol : 0, cg = KS > 1 ? it.nt % ncol : it.nt;
@@ -294,7 +302,7 @@ template <int BM, int KW>
 hipError_t gate_up_bm(const uint16_t* x, const Groups& gs, int d, int h, int hs, const uint16_t* w_gu,
                       const uint16_t* ws_gu, uint16_t* hid, uint16_t* hid_shared, float clamp, hipStream_t stream) {
   const auto kern = clamp > 0.f ? k_gate_up<BM, KW, true> : k_gate_up<BM, KW, false>;
-  hipLaunchKernelGGL(kern, dim3(persistent_grid(kern)), dim3(256), 0, stream, x, gs, d, h, hs, w_gu, ws_gu, hid,
+  hipLaunchKernelGGL(kern, dim3(persistent_grid(kern) * kOversubscribe), dim3(256), 0, stream, x, gs, d, h, hs, w_gu, ws_gu, hid,
                      hid_shared, clamp);
   return hipGetLastError();
 }
@@ -304,7 +312,7 @@ hipError_t down_bm(const Groups& gs, int d, int h, int hs, const uint16_t* hid, 
                    const uint16_t* w_down, const uint16_t* ws_down, uint16_t* y_perm, float* y_shared,
                    hipStream_t stream) {
   const auto kern = k_down<BM, KW>;
-  hipLaunchKernelGGL(kern, dim3(persistent_grid(kern)), dim3(256), 0, stream, gs, d, h, hs, hid, hid_shared, w_down,
+  hipLaunchKernelGGL(kern, dim3(persistent_grid(kern) * kOversubscribe), dim3(256), 0, stream, gs, d, h, hs, hid, hid_shared, w_down,
                      ws_down, y_perm, y_shared, nullptr);
   return hipGetLastError();
 }
@@ -314,7 +322,7 @@ template <int BM>
 hipError_t down_bm_split(const Groups& gs, int d, int hs, const uint16_t* hid_shared, const uint16_t* ws_down,
                          float* y_shared, float* partial, hipStream_t stream) {
   const auto kern = k_down<BM, 4, kDownSplits>;
-  hipLaunchKernelGGL(kern, dim3(persistent_grid(kern)), dim3(256), 0, stream, gs, d, 0, hs, nullptr, hid_shared,
+  hipLaunchKernelGGL(kern, dim3(persistent_grid(kern) * kOversubscribe), dim3(256), 0, stream, gs, d, 0, hs, nullptr, hid_shared,
                      nullptr, ws_down, nullptr, nullptr, partial);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

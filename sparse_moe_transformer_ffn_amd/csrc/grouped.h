@@ -3,13 +3,11 @@
 // A "group" is one routed expert's rows of the permuted order (rows
 // expert_offsets[g] .. expert_offsets[g+1], token = perm_pairs[row] / k) or,
 // as group E, the shared expert's rows (every token in order).  Each group is
-// cut into M-tiles; an item is (group, N-tile, M-tile), ordered so that items
-// running side by side on one XCD share an operand through that XCD's L2
-// (see decode_item).  Blocks are
-// persistent: each builds the per-group item prefix in LDS once from
-// expert_offsets (no host round trip for the data-dependent group sizes) and
-// strides over the items; block b's first item is chosen so that every XCD
-// owns a contiguous range of items at each step.
+// cut into M-tiles; an item is (group, N-tile, M-tile), ordered so that
+// neighbouring items share an operand (see decode_item).  Each block builds
+// the per-group item prefix in LDS once from expert_offsets (no host round
+// trip for the data-dependent group sizes) and then strides over the items;
+// how items map to blocks and XCDs is up to each kernel.
 #pragma once
 #include <mutex>
 
@@ -130,8 +128,9 @@ __device__ __forceinline__ Item decode_item(const int* ip, const Groups& gs, int
 }
 
 // Persistent grid: as many blocks as can be resident at once on the current
-// device (occupancy x compute units), so that no block starts late and every
-// block strides over its share of the items.  Cached per kernel (by address:
+// device (occupancy x compute units); a kernel launches this many, or a
+// multiple of it when it wants the dispatcher to balance the tail.  Cached
+// per kernel (by address:
 // instances of one kernel template share a type but not their occupancy) and
 // device.
 struct GridCacheEntry {
