@@ -281,19 +281,26 @@ __global__ __launch_bounds__(256) void k_sum_partials(const float* __restrict__ 
 
 namespace {
 
-// Average rows per routed group decides the regime: >= 64 rows is
-// compute-bound work for the tiled kernels.  A launch of the shared group
-// alone (no routed groups) goes tiled only when the tiled items of the phase,
-// ceil(T / 256) x (its 256-wide weight tiles), at least fill the chip;
-// otherwise the streaming kernels' finer items spread it over every CU.
-bool use_tiled(int T, int k, int E, const int32_t* offsets, int weight_rows) {
-  if (!offsets) return (long)((T + 255) / 256) * (weight_rows / 256) >= 256;
-  return (long)T * k >= 64L * E;
+// Which regime a phase runs in (crossovers measured on the 288-expert layer,
+// d = 4,096, and on the dense FFN of hidden 11,264):
+// - routed launches: the LDS-tiled kernels from 4 rows per routed group on
+//   average.  At 3.6 rows per group the two regimes tie; above it more
+//   groups span several 16-row M-tiles, each of which reads the expert's
+//   weights again in the streaming kernels, while the tiled ones read them
+//   once per 256 rows (5.3 rows per group: 8% faster tiled; 57 rows per
+//   group: three times faster).
+// - the shared group alone (the dense FFN): gate/up tiled from 64 tokens;
+//   down tiled only beyond 256 tokens, since one 256-row M-tile gives the
+//   tiled down only d / 256 items, while the streaming down splits its long
+//   reduction over items.
+bool use_tiled(int T, int k, int E, const int32_t* offsets, bool down) {
+  if (offsets) return (long)T * k >= 4L * E;
+  return down ? T > 256 : T >= 64;
 }
 
 int pick_bm(int T, int k, int E) {
-  // Average rows per routed group decides the M-tile: 16 for decode-sized
-  // batches.
+  // Average rows per group decides the M-tile: 16 up to 16 rows (every routed
+  // launch that streams), else 32 (the shared group alone from 17 tokens).
   const long rows = (long)T * k;
   return rows <= 16L * E ? 16 : 32;
 }
@@ -341,7 +348,7 @@ hipError_t launch_gate_up(int T, int d, int E, int k, int h, int hs, const uint1
   if (T == 0) return hipSuccess;
   const int et = e_total > 0 ? e_total : E;
   // The tiled gate/up item covers 128 hidden units of each group.
-  if (use_tiled(T, k, et, offsets, 2 * hs) && h % 128 == 0 && hs % 128 == 0)
+  if (use_tiled(T, k, et, offsets, false) && h % 128 == 0 && hs % 128 == 0)
     return launch_gate_up_tiled(T, d, E, k, h, hs, x, offsets, perm, w_gu, ws_gu, hid, hid_shared, queue, stream,
                                 act_clamp);
   const Groups gs = make_groups(T, E, k, offsets, perm, ws_gu != nullptr);
@@ -361,7 +368,7 @@ hipError_t launch_down(int T, int d, int E, int k, int h, int hs, const int32_t*
   if (T == 0) return hipSuccess;
   const int et = e_total > 0 ? e_total : E;
   // The tiled down item covers 256 output columns.
-  if (use_tiled(T, k, et, offsets, d) && d % 256 == 0)
+  if (use_tiled(T, k, et, offsets, true) && d % 256 == 0)
     return launch_down_tiled(T, d, E, k, h, hs, offsets, hid, hid_shared, w_down, ws_down, y_perm, y_shared, queue,
                              stream);
   const Groups gs = make_groups(T, E, k, offsets, nullptr, ws_down != nullptr);

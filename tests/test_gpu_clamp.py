@@ -32,8 +32,9 @@ def run(dl, off, perm, clamp):
 
 
 @pytest.mark.parametrize("cfg,clamp", [
-    (moegen.CONFIGS[0], 0.02),                                                   # streaming kernels
-    (moegen.CONFIGS[1], 0.5),                                                    # decode size
+    (moegen.custom(0, T=24, seed=951), 0.02),                                    # streaming kernels
+    (moegen.CONFIGS[0], 0.02),                                                   # tiled, 8 rows per expert
+    (moegen.CONFIGS[1], 0.5),                                                    # decode size (streaming)
     (moegen.custom(0, T=2048, d=256, E=16, k=2, h=128, hs=128, seed=950), 0.02),  # tiled kernels
 ])
 def test_clamped_experts_parity(device, cfg, clamp):

@@ -3,8 +3,9 @@ the MTP heads, hidden 11,264) with the CPU oracle's SwiGLU, on generator
 inputs.  The weights are the generator's shared-expert tensors of a workload
 whose shared hidden size is the dense one; the oracle gets the host copy.
 
-Both launch regimes are covered: fewer than 64 tokens take the streaming
-kernels, 64 and more the LDS-tiled ones.  Bar: the layer's output tolerance
+Both launch regimes are covered: gate/up runs on the streaming kernels below
+64 tokens and on the LDS-tiled ones from 64; down streams up to 256 tokens
+and is tiled beyond.  Bar: the layer's output tolerance
 (relative L2 <= 5e-3, max |err| <= 3e-2 RMS), every token at the small sizes
 and sampled tokens at T = 8192.
 """
@@ -46,7 +47,8 @@ def oracle_rows(cfg, x_h, rows):
 
 @pytest.mark.parametrize("T,d,H", [
     (1, 256, 128), (37, 256, 384), (63, 512, 256),     # streaming kernels
-    (64, 256, 384), (300, 512, 640), (1000, 256, 128),  # tiled kernels, ragged last M-tile
+    (64, 256, 384), (256, 512, 256),                    # tiled gate/up, streaming down
+    (300, 512, 640), (1000, 256, 128),                  # tiled kernels, ragged last M-tile
     (64, 4096, DENSE_HIDDEN),                           # decode batch at the model's size
 ])
 def test_dense_parity(device, T, d, H):

@@ -128,7 +128,10 @@ def test_layer_diagnostic_side_outputs(device, idx):
     np.testing.assert_allclose(ratio, [rms[used].min() / med, rms[used].max() / med], rtol=1e-6)
 
 
-@pytest.mark.parametrize("T,k,hs,scale", [(1, 8, 1280, 1.0), (3, 1, 1280, 1.0), (97, 8, 0, 0.5), (130, 8, 1280, 2.0)])
+@pytest.mark.parametrize("T,k,hs,scale", [
+    (1, 8, 1280, 1.0), (3, 1, 1280, 1.0), (97, 8, 0, 0.5), (130, 8, 1280, 2.0),  # streaming kernels
+    (144, 8, 1280, 1.0), (256, 8, 1280, 1.0),  # tiled from 4 rows per expert on average
+])
 def test_layer_edge_shapes(device, T, k, hs, scale):
     cfg = moegen.custom(1, T=T, k=k, hs=hs, routed_scale=scale, seed=500 + T)
     log(f"[layer-edge] T={T} k={k} hs={hs} routed_scale={scale}")
