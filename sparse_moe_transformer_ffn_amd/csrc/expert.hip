@@ -158,8 +158,10 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
 
 // Phase 2: out[row, n] = hid[row, :] . W_d[n, :]; routed rows -> y_perm
 // (bf16), shared rows -> y_shared (f32).
-// KW = 1: an item is BM rows x 64 output columns, wave w owns columns
-//         16w..16w+15 over the whole reduction (the routed experts' 1,280).
+// KW = 1: an item is BM rows x 64·CPW output columns, wave w owns CPW groups
+//         of 16 columns over the whole reduction (the routed experts' 1,280);
+//         with CPW = 2 each wave keeps 16 weight rows' loads in flight per
+//         batch, as the gate/up waves do (292 vs 300 µs at decode).
 // KW = 4: an item is BM rows x 16 columns and wave w owns the w-th quarter of
 //         the reduction, the partial sums added in LDS in wave order: for a
 //         long reduction (the dense FFN's 11,264) with few rows, four times
@@ -167,16 +169,17 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
 // KS > 1 (the shared group alone): the reduction is also split over KS
 //         items, each writing its partial sums to partial[ks][row][d] (f32);
 //         k_sum_partials adds them in ks order into y_shared.
-template <int BM, int KW, int KS = 1>
+template <int BM, int KW, int KS = 1, int CPW = 1>
 __global__ __launch_bounds__(256) void k_down(Groups gs, int d, int h, int hs, const uint16_t* __restrict__ hid,
                                               const uint16_t* __restrict__ hid_shared,
                                               const uint16_t* __restrict__ w_down,
                                               const uint16_t* __restrict__ ws_down, uint16_t* __restrict__ y_perm,
                                               float* __restrict__ y_shared, float* __restrict__ partial) {
+  static_assert(KW == 1 || CPW == 1, "column groups per wave need the whole reduction per wave");
   __shared__ int ip[kMaxGroups + 1];
   __shared__ int wsum[4];
   constexpr int MB = BM / 16;
-  constexpr int COLS = 64 / KW;  // output columns per item
+  constexpr int COLS = 64 * CPW / KW;  // output columns per item
   __shared__ float red[KW > 1 ? KW - 1 : 1][MB * 4][kWave];
   const int ncol = d / COLS;
   const int items = item_prefix<BM>(ip, wsum, gs, ncol, ncol * KS);
@@ -188,7 +191,8 @@ __global__ __launch_bounds__(256) void k_down(Groups gs, int d, int h, int hs, c
     const int H = it.shared ? hs : h;
     const int ks = KS > 1 ? it.nt / ncol : 0, cg = KS > 1 ? it.nt % ncol : it.nt;
     const int klen = H / (KW * KS), kbeg = (ks * KW + (KW > 1 ? wave : 0)) * klen;
-    const int n = cg * COLS + (KW > 1 ? 0 : wave * 16) + r16;
+    // Column of this lane in its first 16-column group; group c adds 16c.
+    const int n = cg * COLS + (KW > 1 ? 0 : wave * 16 * CPW) + r16;
     const uint16_t* pb =
         (it.shared ? ws_down : w_down + (size_t)it.group * d * h) + (size_t)n * H + kbeg + kq * 8;
     const uint16_t* src = it.shared ? hid_shared : hid;
@@ -200,14 +204,18 @@ __global__ __launch_bounds__(256) void k_down(Groups gs, int d, int h, int hs, c
       va[mb] = r < it.nrows;
       pa[mb] = src + (size_t)(it.row0 + (va[mb] ? r : 0)) * H + kbeg + kq * 8;
     }
-    f32x4 acc[MB];
+    f32x4 acc[CPW][MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[c][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
     int kk = 0;
     for (; kk + 32 * kUnroll <= klen; kk += 32 * kUnroll) {
-      u32x4 b[kUnroll], a[MB][kUnroll];
+      u32x4 b[CPW][kUnroll], a[MB][kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) b[u] = load16(pb + kk + 32 * u);
+      for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) b[c][u] = load16(pb + (size_t)c * 16 * H + kk + 32 * u);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -215,14 +223,19 @@ __global__ __launch_bounds__(256) void k_down(Groups gs, int d, int h, int hs, c
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_16x16x32(a[mb][u], b[u], acc[mb]);
+        for (int c = 0; c < CPW; ++c)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) acc[c][mb] = mfma_16x16x32(a[mb][u], b[c][u], acc[c][mb]);
     }
     for (; kk < klen; kk += 32) {
-      const u32x4 b = load16(pb + kk);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const u32x4 a = va[mb] ? load16(pa[mb] + kk) : zero;
-        acc[mb] = mfma_16x16x32(a, b, acc[mb]);
+      for (int c = 0; c < CPW; ++c) {
+        const u32x4 b = load16(pb + (size_t)c * 16 * H + kk);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const u32x4 a = va[mb] ? load16(pa[mb] + kk) : zero;
+          acc[c][mb] = mfma_16x16x32(a, b, acc[c][mb]);
+        }
       }
     }
     if (KW > 1) {
@@ -230,7 +243,7 @@ __global__ __launch_bounds__(256) void k_down(Groups gs, int d, int h, int hs, c
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) red[wave - 1][mb * 4 + i][lane] = acc[mb][i];
+          for (int i = 0; i < 4; ++i) red[wave - 1][mb * 4 + i][lane] = acc[0][mb][i];
       }
       __syncthreads();
       if (wave == 0) {
@@ -239,24 +252,26 @@ __global__ __launch_bounds__(256) void k_down(Groups gs, int d, int h, int hs, c
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mb][i] += red[q][mb * 4 + i][lane];
+            for (int i = 0; i < 4; ++i) acc[0][mb][i] += red[q][mb * 4 + i][lane];
       }
       __syncthreads();  // red[] free for the next item
       if (wave > 0) continue;
     }
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+    for (int c = 0; c < CPW; ++c)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = it.m0 + mb * 16 + kq * 4 + i;
-        if (r < it.nrows) {
-          const size_t o = (size_t)(it.row0 + r) * d + n;
-          if (KS > 1) partial[(size_t)ks * gs.T * d + o] = acc[mb][i];
-          else if (it.shared) y_shared[o] = acc[mb][i];
-          else y_perm[o] = (uint16_t)f32_to_bf16(acc[mb][i]);
+      for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = it.m0 + mb * 16 + kq * 4 + i;
+          if (r < it.nrows) {
+            const size_t o = (size_t)(it.row0 + r) * d + n + c * 16;
+            if (KS > 1) partial[(size_t)ks * gs.T * d + o] = acc[c][mb][i];
+            else if (it.shared) y_shared[o] = acc[c][mb][i];
+            else y_perm[o] = (uint16_t)f32_to_bf16(acc[c][mb][i]);
+          }
         }
       }
-    }
   }
 }
 
@@ -318,7 +333,8 @@ template <int BM, int KW>
 hipError_t down_bm(const Groups& gs, int d, int h, int hs, const uint16_t* hid, const uint16_t* hid_shared,
                    const uint16_t* w_down, const uint16_t* ws_down, uint16_t* y_perm, float* y_shared,
                    hipStream_t stream) {
-  const auto kern = k_down<BM, KW>;
+  // Two 16-column groups per wave where the item width (128 columns) divides d.
+  const auto kern = (KW == 1 && d % 128 == 0) ? k_down<BM, KW, 1, KW == 1 ? 2 : 1> : k_down<BM, KW>;
   hipLaunchKernelGGL(kern, dim3(persistent_grid(kern) * kOversubscribe), dim3(256), 0, stream, gs, d, h, hs, hid, hid_shared, w_down,
                      ws_down, y_perm, y_shared, nullptr);
   return hipGetLastError();
