@@ -10,7 +10,9 @@ distributions of the model's layer; no trained weights exist here).
 
 Default workload: the decode batch (T=64 tokens, d_model 4096, 288 experts,
 top-8, expert and shared hidden 1280).  The prefill batch (T=8192) is timed
-after it and reported in the "prefill" object.  Prints one JSON line.
+after it and reported in the "prefill" object; the skewed-load batch
+(T=4096) and the 12-layer stack (T=256) follow as supplementary "skew" and
+"stack" objects.  Prints one JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill]
                        [--no-cpu-baseline] [--cpu-sample N]
@@ -124,16 +126,16 @@ def write_traffic(pmc_dir):
 class Workload:
     """Device tensors of one recipe, filled by the generator."""
 
-    def __init__(self, cfg, dev):
+    def __init__(self, cfg, dev, layer=0):
         import numpy as np
         import torch
         import moegen
         import sparse_moe_transformer_ffn_amd as moe
         self.cfg = cfg
-        self.x_h = moegen.x(cfg)
-        self.wr_h = moegen.router(cfg)
-        self.b_h = moegen.sel_bias(cfg)
-        self.c_h = moegen.logit_bias(cfg)
+        self.x_h = moegen.x(cfg, layer)
+        self.wr_h = moegen.router(cfg, layer)
+        self.b_h = moegen.sel_bias(cfg, layer)
+        self.c_h = moegen.logit_bias(cfg, layer)
 
         def bf16(a):
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -147,8 +149,8 @@ class Workload:
         self.ws_gu = torch.empty((2 * hs, d), dtype=torch.bfloat16, device=dev)
         self.ws_d = torch.empty((d, hs), dtype=torch.bfloat16, device=dev)
         s = torch.cuda.current_stream().cuda_stream
-        moegen.fill_experts_device(cfg, 0, self.w_gu.data_ptr(), self.w_d.data_ptr(), s)
-        moegen.fill_shared_device(cfg, 0, self.ws_gu.data_ptr(), self.ws_d.data_ptr(), s)
+        moegen.fill_experts_device(cfg, layer, self.w_gu.data_ptr(), self.w_d.data_ptr(), s)
+        moegen.fill_shared_device(cfg, layer, self.ws_gu.data_ptr(), self.ws_d.data_ptr(), s)
         self.buf = moe.LayerBuffers.allocate(cfg.T, d, E, cfg.k, h, hs, device=dev)
         self.hid = torch.empty((cfg.T * cfg.k, h), dtype=torch.bfloat16, device=dev)
         self.hid_shared = torch.empty((cfg.T, hs), dtype=torch.bfloat16, device=dev)
@@ -295,6 +297,62 @@ def time_workload(cfg, steps, warmup, dev, extras=True):
     return wl, res
 
 
+def time_skew(steps, warmup, dev):
+    """The skewed-load workload (T = 4096, Zipf(1.1) logit offset: the
+    busiest expert gets about ten times the mean load) timed like the others;
+    a supplementary figure, not the bench line."""
+    import moegen
+    cfg = moegen.CONFIGS[3]
+    wl, r = time_workload(cfg, steps, warmup, dev, extras=False)
+    del wl
+    alg = r["alg"]
+    sec = r["ms_per_step"] * 1e-3
+    return {"workload": cfg.workload, "tok_s": cfg.T / sec, "ms_per_step": r["ms_per_step"],
+            "ms_per_step_median": r["ms_per_step_median"], "steps": steps,
+            "step_hbm_gbs": alg["step_bytes"] / sec / 1e9, "step_hbm_frac": alg["step_bytes"] / sec / 1e9 / HBM_PEAK_GBS,
+            "step_tflops": alg["step_flops"] / sec / 1e12,
+            "step_mfma_frac": alg["step_flops"] / sec / 1e12 / BF16_PEAK_TFLOPS,
+            "kernels": {"gate_up_ms": r["gate_up_ms"], "down_ms": r["down_ms"]},
+            "touched_experts": r["n_touched"], "max_load": r["max_load"], "idle_experts": r["idle_experts"]}
+
+
+def time_stack(steps, warmup, dev):
+    """The 12-layer stack (T = 256, distinct weights per layer, 109 GB
+    resident): layer l + 1 takes the unit-gain RMSNorm of layer l's output.
+    One pass = 12 layer steps and 11 normalisations; supplementary figure."""
+    import numpy as np
+    import torch
+    import moegen
+    import sparse_moe_transformer_ffn_amd as moe
+    cfg = moegen.CONFIGS[4]
+    layers = [Workload(cfg, dev, layer=l) for l in range(cfg.layers)]
+    main = torch.cuda.current_stream()
+
+    def chain():
+        for l, wl in enumerate(layers):
+            wl.step(main)
+            if l + 1 < cfg.layers:
+                moe.moe_rmsnorm(cfg.T, cfg.d, wl.buf.y, None, 1e-6, layers[l + 1].x, main)
+
+    for _ in range(warmup):
+        chain()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, z in ev:
+        a.record(main)
+        chain()
+        z.record(main)
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(z) for a, z in ev])
+    touched = [int((wl.buf.expert_counts.cpu().numpy() > 0).sum()) for wl in layers]
+    nbytes = sum(algorithmic(cfg, n)["step_bytes"] for n in touched)
+    ms = float(np.median(per))
+    del layers
+    return {"workload": cfg.workload, "layers": cfg.layers, "tok_s": cfg.T / (ms * 1e-3), "ms_per_pass_median": ms,
+            "ms_per_pass_min": float(per.min()), "passes": steps, "hbm_gbs": nbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "touched_experts_per_layer": touched}
+
+
 DENSE_HIDDEN = 11264   # dense FFN hidden size of the first blocks and the MTP heads
 
 
@@ -438,6 +496,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="time the layer step only: no diagnostics, pre-norm block, expert share or dense FFN "
                          "(profiling runs)")
+    ap.add_argument("--no-supplementary", action="store_true",
+                    help="skip the skewed-load workload and the 12-layer stack")
     ap.add_argument("--cpu-sample", type=int, default=64)
     ap.add_argument("--write-traffic", metavar="PMC_DIR",
                     help="no GPU work: write profiles/traffic_*.json from rocprofv3 counter runs in PMC_DIR")
@@ -538,6 +598,12 @@ def main():
                                   graph_replay=p["graph_replay"],
                                   ep_share=time_share(pwl, args.prefill_steps))
         del pwl
+    if extras and not args.no_supplementary:
+        torch.cuda.empty_cache()
+        out["skew"] = time_skew(args.prefill_steps, args.warmup, dev)
+        torch.cuda.empty_cache()
+        out["stack"] = time_stack(args.prefill_steps, args.warmup, dev)
+        torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
 
 

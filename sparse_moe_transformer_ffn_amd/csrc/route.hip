@@ -76,10 +76,8 @@ __global__ __launch_bounds__(256) void k_route_logits(const uint16_t* __restrict
   const u32x4 zero = {0u, 0u, 0u, 0u};
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const bool store_x = NORM && va && blockIdx.x == 0 && wave == 0;
-#pragma unroll 4
-  for (int kk = k_begin; kk < k_end; kk += 32) {
-    u32x4 a = va ? load16(pa + kk) : zero;
-    const u32x4 b = vb ? load16(pb + kk) : zero;
+  // One 32-wide K step on loaded slices (normalising x first under NORM).
+  auto step = [&](u32x4 a, u32x4 b, int kk) {
     if constexpr (NORM) {
       const int c = kk + kq * 8;
       float f[8];
@@ -90,7 +88,20 @@ __global__ __launch_bounds__(256) void k_route_logits(const uint16_t* __restrict
       if (store_x) *reinterpret_cast<u32x4*>(x_out + (size_t)ta * d + c) = a;
     }
     acc = mfma_16x16x32(a, b, acc);
+  };
+  // Four steps' loads issued before their MFMAs, then the remaining steps.
+  int kk = k_begin;
+  for (; kk + 4 * 32 <= k_end; kk += 4 * 32) {
+    u32x4 a[4], b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a[u] = va ? load16(pa + kk + 32 * u) : zero;
+      b[u] = vb ? load16(pb + kk + 32 * u) : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) step(a[u], b[u], kk + 32 * u);
   }
+  for (; kk < k_end; kk += 32) step(va ? load16(pa + kk) : zero, vb ? load16(pb + kk) : zero, kk);
   const int e = e0 + r16;
   if (e < E) {
 #pragma unroll
