@@ -231,18 +231,26 @@ def time_workload(cfg, steps, warmup, dev, extras=True):
     for _ in range(warmup):
         wl.step(main)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    # The timed steps: nothing recorded between them.  Each event record on
+    # the stream leaves the GPU idle for about 5 us before the next kernel,
+    # so the per-kernel times come from a second, instrumented pass.
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(main)
-    for i in range(steps):
-        wl.step(main, evs[i])
+    for _ in range(steps):
+        wl.step(main)
     t1.record(main)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = t0.elapsed_time(t1) / steps
+    # The same number of steps with events at the step ends and around the
+    # two expert launches (five records per step).
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for i in range(steps):
+        wl.step(main, evs[i])
+    torch.cuda.synchronize()
     gate_up_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     down_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
     per_step = np.array([e[0].elapsed_time(e[4]) for e in evs])
@@ -251,6 +259,7 @@ def time_workload(cfg, steps, warmup, dev, extras=True):
     alg = algorithmic(cfg, n_touched)
     res = dict(ms_per_step=ms, wall_ms_per_step=wall * 1e3 / steps, gate_up_ms=gate_up_ms, down_ms=down_ms,
                ms_per_step_median=float(np.median(per_step)), ms_per_step_min=float(per_step.min()),
+               ms_per_step_instrumented=float(per_step.mean()),
                n_touched=n_touched, max_load=int(counts.max()), idle_experts=int((counts == 0).sum()), alg=alg)
     if not extras:
         return wl, res
@@ -308,7 +317,7 @@ def time_skew(steps, warmup, dev):
     alg = r["alg"]
     sec = r["ms_per_step"] * 1e-3
     return {"workload": cfg.workload, "tok_s": cfg.T / sec, "ms_per_step": r["ms_per_step"],
-            "ms_per_step_median": r["ms_per_step_median"], "steps": steps,
+            "instrumented": instrumented(r), "steps": steps,
             "step_hbm_gbs": alg["step_bytes"] / sec / 1e9, "step_hbm_frac": alg["step_bytes"] / sec / 1e9 / HBM_PEAK_GBS,
             "step_tflops": alg["step_flops"] / sec / 1e12,
             "step_mfma_frac": alg["step_flops"] / sec / 1e12 / BF16_PEAK_TFLOPS,
@@ -353,6 +362,20 @@ def time_stack(steps, warmup, dev):
             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "touched_experts_per_layer": touched}
 
 
+def mean_ms(call, n, stream):
+    """Mean time of n back-to-back calls on `stream`, events only around the
+    whole loop."""
+    import torch
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(n):
+        call()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / n
+
+
 DENSE_HIDDEN = 11264   # dense FFN hidden size of the first blocks and the MTP heads
 
 
@@ -374,17 +397,10 @@ def time_dense(T, steps, dev):
     main = torch.cuda.current_stream()
     for _ in range(2):
         moe.moe_dense_swiglu(T, d, H, x, w_gu, w_d, y, ws, main)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
-    for a, b in ev:
-        a.record(main)
-        moe.moe_dense_swiglu(T, d, H, x, w_gu, w_d, y, ws, main)
-        b.record(main)
-    torch.cuda.synchronize()
-    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    ms = mean_ms(lambda: moe.moe_dense_swiglu(T, d, H, x, w_gu, w_d, y, ws, main), steps, main)
     nbytes = 3 * d * H * 2 + T * d * 2 + T * d * 4
     flops = 2 * T * 3 * d * H
-    return {"tokens": T, "ms_median": ms, "tok_s": T / (ms * 1e-3),
+    return {"tokens": T, "ms": ms, "tok_s": T / (ms * 1e-3),
             "hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "tflops": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
 
@@ -409,20 +425,13 @@ def time_share(wl, steps):
 
     for _ in range(2):
         share()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
-    for a, z in ev:
-        a.record(main)
-        share()
-        z.record(main)
-    torch.cuda.synchronize()
-    ms = float(np.median([a.elapsed_time(z) for a, z in ev]))
+    ms = mean_ms(share, steps, main)
     counts = b.expert_counts.cpu().numpy()[:e1]
     rows = int(counts.sum())
     touched = int((counts > 0).sum())
     nbytes = touched * 3 * c.d * c.h * 2 + rows * c.d * 2 * 2
     flops = 2 * rows * 3 * c.d * c.h
-    return {"experts": [0, e1], "rows": rows, "touched_experts": touched, "ms_median": ms,
+    return {"experts": [0, e1], "rows": rows, "touched_experts": touched, "ms": ms,
             "hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "tflops": flops / (ms * 1e-3) / 1e12}
 
 
@@ -471,6 +480,12 @@ def host_cpu_model():
     except OSError:
         pass
     return "unknown"
+
+
+def instrumented(r):
+    """Step times of the instrumented pass (five event records per step)."""
+    return {"ms_per_step": r["ms_per_step_instrumented"], "ms_per_step_median": r["ms_per_step_median"],
+            "ms_per_step_min": r["ms_per_step_min"], "event_records_per_step": 5}
 
 
 def roofline(kind, achieved, traffic):
@@ -537,8 +552,8 @@ def main():
     gate_up_gbs = alg["gate_up_bytes"] / (r["gate_up_ms"] * 1e-3) / 1e9
     out = {
         "metric": METRIC, "value": tok_s, "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": r["ms_per_step"], "ms_per_step_median": r["ms_per_step_median"],
-        "ms_per_step_min": r["ms_per_step_min"], "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": r["ms_per_step"], "instrumented": instrumented(r),
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.workload, "tokens": cfg.T, "d_model": cfg.d, "experts": cfg.E, "top_k": cfg.k,
                    "expert_hidden": cfg.h, "shared_hidden": cfg.hs, "seed": cfg.seed},
@@ -574,7 +589,7 @@ def main():
         step_tf = palg["step_flops"] / (p["ms_per_step"] * 1e-3) / 1e12
         out["prefill"] = {
             "workload": pcfg.workload, "tok_s": pcfg.T / (p["ms_per_step"] * 1e-3), "ms_per_step": p["ms_per_step"],
-            "ms_per_step_median": p["ms_per_step_median"], "ms_per_step_min": p["ms_per_step_min"],
+            "instrumented": instrumented(p),
             "steps": args.prefill_steps, "step_tflops": step_tf, "step_mfma_frac": step_tf / BF16_PEAK_TFLOPS,
             "roofline": roofline("mfma", gate_up_tf, load_traffic("prefill", "gate_up")),
             "kernels": {"gate_up_ms": p["gate_up_ms"], "down_ms": p["down_ms"],
@@ -590,7 +605,7 @@ def main():
             del bwl
             btf = bp["alg"]["step_flops"] / (bp["ms_per_step"] * 1e-3) / 1e12
             out["prefill"]["balanced_bias_0.005"] = {
-                "ms_per_step_median": bp["ms_per_step_median"], "tok_s": bcfg.T / (bp["ms_per_step"] * 1e-3),
+                "ms_per_step": bp["ms_per_step"], "tok_s": bcfg.T / (bp["ms_per_step"] * 1e-3),
                 "step_tflops": btf, "step_mfma_frac": btf / BF16_PEAK_TFLOPS,
                 "gate_up_tflops": bp["alg"]["gate_up_flops"] / (bp["gate_up_ms"] * 1e-3) / 1e12,
                 "touched_experts": bp["n_touched"], "max_load": bp["max_load"], "idle_experts": bp["idle_experts"]}
