@@ -28,7 +28,8 @@
 //
 // Work order (grouped.h): M-tiles fastest in bands of up to 4; blocks take
 // items from a per-XCD queue, so the items in flight on an XCD are a window of
-// consecutive items sharing their groups' token rows and weights through L2.
+// consecutive items sharing their groups' token rows and weights through L2;
+// a block whose queue is empty takes from the other XCDs' queues.
 //
 // Operand staging.  Both operands go from HBM/L2 straight into LDS with the
 // gfx950 direct-to-LDS load (global_load_lds_dwordx4: lane l of a wave writes
@@ -344,18 +345,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
     m.b[st] = kStageA + (b_row0<PHASE>(wn, 0) + l32) * kChunk + slot;
   }
 
-  // Dynamic work queue per XCD: XCD x owns items [lo, hi) and its blocks take
-  // them in order, one atomic per item.  Every block exits once its XCD's
-  // range is exhausted.  The next item is taken, planned and its first chunk
-  // issued right after the current item's K loop, so that chunk's latency
-  // overlaps the current item's epilogue.
+  // Dynamic work queue per XCD: queue q owns items [items·q/8, items·(q+1)/8)
+  // and hands them out in order, one atomic per item.  A block takes from its
+  // own XCD's queue (neighbouring items share operands through that XCD's
+  // L2); once that is exhausted it takes from the other queues in turn, so no
+  // XCD idles while another still has items (prefill gate/up 1.97 -> 1.83 ms).
+  // Only thread 0 walks the queues; `tried` only grows, so a block makes at
+  // most kNumXcd failed attempts before it exits.  The next item is taken,
+  // planned and its first chunk issued right after the current item's K
+  // loop, so that chunk's latency overlaps the current item's epilogue.
   const int xcd = blockIdx.x % kNumXcd;
-  const int lo = (int)((long long)items * xcd / kNumXcd);
-  const int hi = (int)((long long)items * (xcd + 1) / kNumXcd);
-  if (tid == 0) next_item = lo + atomicAdd(&queue[xcd], 1);
+  int tried = 0;
+  auto take = [&]() {
+    while (tried < kNumXcd) {
+      const int q = (xcd + tried) % kNumXcd;
+      const int t = (int)((long long)items * q / kNumXcd) + atomicAdd(&queue[q], 1);
+      if (t < (int)((long long)items * (q + 1) / kNumXcd)) return t;
+      ++tried;
+    }
+    return -1;
+  };
+  if (tid == 0) next_item = take();
   __syncthreads();
   int wi = next_item;
-  if (wi >= hi) return;  // uniform across the block
+  if (wi < 0) return;  // uniform across the block
   Plan cur = make_plan<PHASE>(ip, gs, nt_routed, nt_shared, wi, d, h, hs, a_src, a_src_shared, w, ws, wave, lane);
   issue_first(cur, stage0);
   for (;;) {
@@ -384,10 +397,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
     // landed: the release fence of this barrier drains both), so stage0 may
     // take the next item's first chunk; next_item was last read before the
     // K loop.
-    if (tid == 0) next_item = lo + atomicAdd(&queue[xcd], 1);
+    if (tid == 0) next_item = take();
     __syncthreads();
     wi = next_item;
-    const bool more = wi < hi;  // uniform across the block
+    const bool more = wi >= 0;  // uniform across the block
     Plan nxt;
     if (more) {
       nxt = make_plan<PHASE>(ip, gs, nt_routed, nt_shared, wi, d, h, hs, a_src, a_src_shared, w, ws, wave, lane);
