@@ -300,7 +300,9 @@ moe_status moe_combine_diag(const moe_shape* shape, const uint16_t* y_perm, cons
  *      two GEMMs; accumulation is f32.
  * Limits: 0 <= T <= 1048576; d, H in [64, 65536], multiples of 64
  * (MOE_ERR_UNSUPPORTED_SHAPE).  The workspace (256-byte aligned) holds the
- * hidden activations: moe_dense_workspace_bytes gives its size.            */
+ * hidden activations and, up to 256 tokens, the f32 partial sums of the
+ * reductions split over several work items (added in a fixed order, so the
+ * result is reproducible): moe_dense_workspace_bytes gives its size.       */
 moe_status moe_dense_workspace_bytes(int32_t num_tokens, int32_t d_model, int32_t d_hidden, size_t* bytes);
 moe_status moe_dense_swiglu(int32_t num_tokens, int32_t d_model, int32_t d_hidden, const uint16_t* x,
                             const uint16_t* w_gate_up, const uint16_t* w_down, float* y, void* workspace,

@@ -360,7 +360,7 @@ moe_status moe_dense_workspace_bytes(int32_t num_tokens, int32_t d_model, int32_
       d_hidden < 64 || d_hidden > kMaxDim || d_hidden % 64)
     return MOE_ERR_UNSUPPORTED_SHAPE;
   *bytes = round256(moe::kQueueBytes + moe::shared_hid_bytes(num_tokens, d_hidden) +
-                    moe::down_partial_bytes(num_tokens, d_model));
+                    moe::split_partial_bytes(num_tokens, d_model, d_hidden));
   return MOE_OK;
 }
 
@@ -380,12 +380,13 @@ moe_status moe_dense_swiglu(int32_t num_tokens, int32_t d_model, int32_t d_hidde
   const int T = num_tokens, d = d_model, H = d_hidden;
   int32_t* queue = static_cast<int32_t*>(workspace);
   uint16_t* hid = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + moe::kQueueBytes);
-  float* partial = moe::down_partial_bytes(T, d)
+  // Workspace: [work queue | hid | split partial sums].
+  float* partial = moe::split_partial_bytes(T, d, H)
                        ? reinterpret_cast<float*>(static_cast<char*>(workspace) + moe::kQueueBytes +
                                                   moe::shared_hid_bytes(T, H))
                        : nullptr;
   hipError_t err = moe::launch_gate_up(T, d, 1, 1, 128, H, x, nullptr, nullptr, nullptr, w_gate_up, nullptr, hid,
-                                       queue, (hipStream_t)stream);
+                                       queue, (hipStream_t)stream, 0, 0.f, partial);
   if (err == hipSuccess)
     err = moe::launch_down(T, d, 1, 1, 128, H, nullptr, nullptr, hid, nullptr, w_down, nullptr, y, queue,
                            (hipStream_t)stream, 0, partial);

@@ -304,13 +304,18 @@ namespace {
 //   weights again in the streaming kernels, while the tiled ones read them
 //   once per 256 rows (5.3 rows per group: 8% faster tiled; 57 rows per
 //   group: three times faster).
-// - the shared group alone (the dense FFN): gate/up tiled from 64 tokens;
-//   down tiled only beyond 256 tokens, since one 256-row M-tile gives the
-//   tiled down only d / 256 items, while the streaming down splits its long
-//   reduction over items.
-bool use_tiled(int T, int k, int E, const int32_t* offsets, bool down) {
+// - the shared group alone (the dense FFN): the tiled kernels from 64
+//   tokens.  Up to 256 tokens (one M-tile) they need the caller's split
+//   scratch, which spreads each weight tile's reduction over several items
+//   (gate/up 88 tiles x 4 splits, down 16 x 22 at hidden 11,264); without
+//   it down stays on the streaming kernels, whose own split covers its long
+//   reduction.  Dense FFN per call, streaming -> tiled with splits: 0.162 ->
+//   0.122 ms at 64 tokens, 0.355 -> 0.182 ms at 256; at 16 tokens the
+//   streaming kernels win (0.071 vs 0.110 ms).
+bool use_tiled(int T, int k, int E, const int32_t* offsets, bool down, bool split_scratch) {
   if (offsets) return (long)T * k >= 4L * E;
-  return down ? T > 256 : T >= 64;
+  if (T < 64) return false;
+  return down ? T > 256 || split_scratch : true;
 }
 
 int pick_bm(int T, int k, int E) {
@@ -360,13 +365,14 @@ hipError_t down_bm_split(const Groups& gs, int d, int hs, const uint16_t* hid_sh
 
 hipError_t launch_gate_up(int T, int d, int E, int k, int h, int hs, const uint16_t* x, const int32_t* offsets,
                           const int32_t* perm, const uint16_t* w_gu, const uint16_t* ws_gu, uint16_t* hid,
-                          uint16_t* hid_shared, int32_t* queue, hipStream_t stream, int e_total, float act_clamp) {
+                          uint16_t* hid_shared, int32_t* queue, hipStream_t stream, int e_total, float act_clamp,
+                          float* partial) {
   if (T == 0) return hipSuccess;
   const int et = e_total > 0 ? e_total : E;
   // The tiled gate/up item covers 128 hidden units of each group.
-  if (use_tiled(T, k, et, offsets, false) && h % 128 == 0 && hs % 128 == 0)
+  if (use_tiled(T, k, et, offsets, false, partial != nullptr) && h % 128 == 0 && hs % 128 == 0)
     return launch_gate_up_tiled(T, d, E, k, h, hs, x, offsets, perm, w_gu, ws_gu, hid, hid_shared, queue, stream,
-                                act_clamp);
+                                act_clamp, partial);
   const Groups gs = make_groups(T, E, k, offsets, perm, ws_gu != nullptr);
   // Reduction split over the waves when every quarter is whole 32-wide steps.
   const bool split = d % 128 == 0;
@@ -384,9 +390,9 @@ hipError_t launch_down(int T, int d, int E, int k, int h, int hs, const int32_t*
   if (T == 0) return hipSuccess;
   const int et = e_total > 0 ? e_total : E;
   // The tiled down item covers 256 output columns.
-  if (use_tiled(T, k, et, offsets, true) && d % 256 == 0)
+  if (use_tiled(T, k, et, offsets, true, partial != nullptr) && d % 256 == 0)
     return launch_down_tiled(T, d, E, k, h, hs, offsets, hid, hid_shared, w_down, ws_down, y_perm, y_shared, queue,
-                             stream);
+                             stream, partial);
   const Groups gs = make_groups(T, E, k, offsets, nullptr, ws_down != nullptr);
   // The routed experts' reduction (1,280) is short enough already: quarters
   // of it are too few steps to keep loads in flight.  A long reduction of the
@@ -406,8 +412,11 @@ hipError_t launch_down(int T, int d, int E, int k, int h, int hs, const int32_t*
   return down_bm<32, 1>(gs, d, h, hs, hid, hid_shared, w_down, ws_down, y_perm, y_shared, stream);
 }
 
-size_t down_partial_bytes(int T, int d) {
-  return T <= kDownSplitMaxTokens ? ((size_t)kDownSplits * T * d * sizeof(float) + 255) / 256 * 256 : 0;
+size_t split_partial_bytes(int T, int d, int hs) {
+  const size_t streaming =
+      T <= kDownSplitMaxTokens ? ((size_t)kDownSplits * T * d * sizeof(float) + 255) / 256 * 256 : 0;
+  const size_t tiled = tiled_split_bytes(T, d, hs);
+  return streaming > tiled ? streaming : tiled;
 }
 
 size_t expert_hid_bytes(int T, int k, int h) { return ((size_t)T * k * h * sizeof(uint16_t) + 255) / 256 * 256; }

@@ -234,20 +234,33 @@ __device__ __forceinline__ void run_item(const Pipe& p, uint16_t* stage0, uint16
 struct Plan {
   Item it;
   int H, nch, na;  // hidden size of its group, K chunks, A slices (1..4)
+  int ksi;         // reduction split of the item (0 unless SPLIT)
   Pipe p;
 };
 
-template <int PHASE>
+// SPLIT (the shared group alone, one M-tile): item N-tile index n stands for
+// weight tile n % ntiles over reduction split n / ntiles of ks, each split
+// nch / ks consecutive chunks.
+template <int PHASE, bool SPLIT>
 __device__ __forceinline__ Plan make_plan(const int* ip, const Groups& gs, int nt_routed, int nt_shared, int wi,
                                           int d, int h, int hs, const uint16_t* a_src,
                                           const uint16_t* a_src_shared, const uint16_t* w, const uint16_t* ws,
-                                          int wave, int lane) {
+                                          int wave, int lane, int ks) {
   Plan pl;
-  const Item it = decode_item<kBand>(ip, gs, kTileM, nt_routed, nt_shared, wi);
-  pl.it = it;
+  Item it = decode_item<kBand>(ip, gs, kTileM, nt_routed, nt_shared, wi);
   pl.H = it.shared ? hs : h;
   const int K = PHASE == kGateUp ? d : pl.H;
   pl.nch = K / kChunk;
+  pl.ksi = 0;
+  int k0 = 0;  // first reduction element of the item
+  if (SPLIT) {
+    const int ntiles = nt_shared / ks;
+    pl.ksi = it.nt / ntiles;
+    it.nt -= pl.ksi * ntiles;
+    pl.nch /= ks;
+    k0 = pl.ksi * pl.nch * kChunk;
+  }
+  pl.it = it;
   pl.na = min(kLoadsA, (it.nrows - it.m0 + 63) / 64);
   const uint16_t* wmat;
   int b_lo, b_hi;  // weight-matrix row of tile row r: b_lo + r (r < 128), b_hi + r (r >= 128)
@@ -292,10 +305,10 @@ __device__ __forceinline__ Plan make_plan(const int* ip, const Groups& gs, int n
     const int seg = (lane % kSegs) ^ swz(row);
     pl.p.lds_off[q] = (is_a ? 0 : kStageA) + region * kRegionRows * kChunk;
     if (is_a) {
-      pl.p.src[q] = abase + arow[q] * astride + seg * 8;
+      pl.p.src[q] = abase + arow[q] * astride + k0 + seg * 8;
     } else {
       const int grow = row < kTileN / 2 ? b_lo + row : b_hi + row;
-      pl.p.src[q] = wmat + (size_t)grow * K + seg * 8;
+      pl.p.src[q] = wmat + (size_t)grow * K + k0 + seg * 8;
     }
   }
   return pl;
@@ -316,21 +329,26 @@ __device__ __forceinline__ void issue_first(const Plan& pl, uint16_t* stage0) {
 //                clipped to [-clamp, clamp] when CLAMP.
 // PHASE kDown:   A = hid rows, B rows = W_d rows, K = H,
 //                out -> y_perm (bf16) / y_shared (f32), row stride d.
-template <int PHASE, bool CLAMP = false>
+// SPLIT: the shared group alone in one M-tile, its reduction split over ks
+// items per weight tile; each writes its f32 sums to partial[split][row][col]
+// (col < 2 hs for gate/up: gate unit j at j, up unit j at hs + j; col < d
+// for down), added up by k_swiglu_splits / k_sum_splits.
+template <int PHASE, bool CLAMP = false, bool SPLIT = false>
 __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __restrict__ a_src,
                                                               const uint16_t* __restrict__ a_src_shared, Groups gs,
                                                               int d, int h, int hs, const uint16_t* __restrict__ w,
                                                               const uint16_t* __restrict__ ws,
                                                               uint16_t* __restrict__ out,
                                                               void* __restrict__ out_shared,
-                                                              int* __restrict__ queue, float clamp) {
+                                                              int* __restrict__ queue, float clamp, int ks,
+                                                              float* __restrict__ partial) {
   __shared__ int ip[kMaxGroups + 1];
   __shared__ int next_item;
   __shared__ int wsum[kWaves];
   __shared__ __attribute__((aligned(16))) uint16_t stage0[kStage];
   __shared__ __attribute__((aligned(16))) uint16_t stage1[kStage];
   const int nt_routed = PHASE == kGateUp ? h / (kTileN / 2) : d / kTileN;
-  const int nt_shared = PHASE == kGateUp ? hs / (kTileN / 2) : d / kTileN;
+  const int nt_shared = (PHASE == kGateUp ? hs / (kTileN / 2) : d / kTileN) * (SPLIT ? ks : 1);
   const int items = item_prefix<kTileM, kThreads>(ip, wsum, gs, nt_routed, nt_shared);
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform per wave
@@ -369,7 +387,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
   __syncthreads();
   int wi = next_item;
   if (wi < 0) return;  // uniform across the block
-  Plan cur = make_plan<PHASE>(ip, gs, nt_routed, nt_shared, wi, d, h, hs, a_src, a_src_shared, w, ws, wave, lane);
+  Plan cur = make_plan<PHASE, SPLIT>(ip, gs, nt_routed, nt_shared, wi, d, h, hs, a_src, a_src_shared, w, ws, wave, lane, ks);
   issue_first(cur, stage0);
   for (;;) {
     const int wave_row0 = cur.it.m0 + wm * 64;
@@ -403,7 +421,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
     const bool more = wi >= 0;  // uniform across the block
     Plan nxt;
     if (more) {
-      nxt = make_plan<PHASE>(ip, gs, nt_routed, nt_shared, wi, d, h, hs, a_src, a_src_shared, w, ws, wave, lane);
+      nxt = make_plan<PHASE, SPLIT>(ip, gs, nt_routed, nt_shared, wi, d, h, hs, a_src, a_src_shared, w, ws, wave, lane, ks);
       issue_first(nxt, stage0);
     }
 
@@ -420,7 +438,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
     if (mul) {
       const Item& it = cur.it;
       const int H = cur.H;
-      if (PHASE == kGateUp) {
+      if (SPLIT) {
+        // Raw f32 sums of this split, per element.
+        const int NW = PHASE == kGateUp ? 2 * H : d;
+        float* pp = partial + (size_t)cur.ksi * gs.T * NW;
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int r = wave_row0 + ms * 32 + 8 * (i / 4) + 4 * lhi + (i % 4);
+            if (r >= it.nrows) continue;
+            const size_t grow = (size_t)(it.row0 + r);
+#pragma unroll
+            for (int ns = 0; ns < 4; ++ns) {
+              const int col = PHASE == kGateUp
+                                  ? (ns < 2 ? 0 : H) + it.nt * (kTileN / 2) + wn * 64 + (ns % 2) * 32 + l32
+                                  : it.nt * kTileN + wn * 128 + ns * 32 + l32;
+              pp[grow * NW + col] = acc[ms][ns][i];
+            }
+          }
+        }
+      } else if (PHASE == kGateUp) {
         // Unit ns*32 + l32 pairs gate acc[ms][ns] with up acc[ms][ns+2]; the
         // hidden rows are short (64 units of this wave), stored per element.
         uint16_t* o = it.shared ? static_cast<uint16_t*>(out_shared) : out;
@@ -491,29 +529,121 @@ __global__ void k_clear_queue(int* queue) {
   if (threadIdx.x < kNumXcd) queue[threadIdx.x] = 0;
 }
 
+// Gate/up splits: hid[t][j] = SwiGLU(sum_s P[s][t][j], sum_s P[s][t][H + j]),
+// the splits added in s order; four units per thread (H % 4 == 0).
+__global__ __launch_bounds__(256) void k_swiglu_splits(const float* __restrict__ P, int ks, int T, int H,
+                                                       float clamp, uint16_t* __restrict__ hid) {
+  const size_t plane = (size_t)T * 2 * H, n4 = (size_t)T * H / 4;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+    const size_t t = i / (H / 4), j = (i % (H / 4)) * 4;
+    const float* g0 = P + t * 2 * H + j;
+    float4 g = *reinterpret_cast<const float4*>(g0), u = *reinterpret_cast<const float4*>(g0 + H);
+    for (int s = 1; s < ks; ++s) {
+      const float4 gs = *reinterpret_cast<const float4*>(g0 + s * plane);
+      const float4 us = *reinterpret_cast<const float4*>(g0 + s * plane + H);
+      g.x += gs.x, g.y += gs.y, g.z += gs.z, g.w += gs.w;
+      u.x += us.x, u.y += us.y, u.z += us.z, u.w += us.w;
+    }
+    const uint32_t lo = f32_to_bf16(swiglu(g.x, u.x, clamp)) | (f32_to_bf16(swiglu(g.y, u.y, clamp)) << 16);
+    const uint32_t hi = f32_to_bf16(swiglu(g.z, u.z, clamp)) | (f32_to_bf16(swiglu(g.w, u.w, clamp)) << 16);
+    *reinterpret_cast<uint2*>(hid + t * H + j) = make_uint2(lo, hi);
+  }
+}
+
+// Down splits: y[i] = sum_s P[s][i] in s order (n % 4 == 0).
+__global__ __launch_bounds__(256) void k_sum_splits(const float* __restrict__ P, int ks, size_t n,
+                                                    float* __restrict__ y) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n / 4; i += (size_t)gridDim.x * 256) {
+    float4 v = reinterpret_cast<const float4*>(P)[i];
+    for (int s = 1; s < ks; ++s) {
+      const float4 w = reinterpret_cast<const float4*>(P + s * n)[i];
+      v.x += w.x, v.y += w.y, v.z += w.z, v.w += w.w;
+    }
+    reinterpret_cast<float4*>(y)[i] = v;
+  }
+}
+
+unsigned finish_grid(size_t n4) {
+  const size_t blocks = (n4 + 255) / 256;
+  return (unsigned)(blocks < 4096 ? blocks : 4096);
+}
+
+// Reduction splits of a launch of the shared group alone: with one M-tile
+// of rows the launch has only `ntiles` items (88 for gate/up at hidden
+// 11,264, 16 for down at d = 4,096), too few for 256 CUs.  Take the smallest
+// split of the nch chunks that gives at least kSplitItems items while every
+// split keeps at least kSplitMinChunks chunks (else the largest that does).
+constexpr int kSplitItems = 320;
+constexpr int kSplitMinChunks = 8;
+
+int tiled_splits(int T, int ntiles, int nch) {
+  if (T > kTileM || ntiles >= kSplitItems) return 1;
+  int best = 1;
+  for (int ks = 2; nch / ks >= kSplitMinChunks; ++ks) {
+    if (nch % ks) continue;
+    best = ks;
+    if (ntiles * ks >= kSplitItems) break;
+  }
+  return best;
+}
+
+int gate_up_splits(int T, int d, int hs) { return tiled_splits(T, hs / (kTileN / 2), d / kChunk); }
+int down_splits(int T, int d, int hs) { return tiled_splits(T, d / kTileN, hs / kChunk); }
+
 }  // namespace
+
+size_t tiled_split_bytes(int T, int d, int hs) {
+  if (T > kTileM || hs % (kTileN / 2) || d % kTileN) return 0;
+  const int kg = gate_up_splits(T, d, hs), kd = down_splits(T, d, hs);
+  const size_t g = kg > 1 ? (size_t)kg * T * 2 * hs * sizeof(float) : 0;
+  const size_t n = kd > 1 ? (size_t)kd * T * d * sizeof(float) : 0;
+  return ((g > n ? g : n) + 255) / 256 * 256;
+}
 
 hipError_t launch_gate_up_tiled(int T, int d, int E, int k, int h, int hs, const uint16_t* x, const int32_t* offsets,
                                 const int32_t* perm, const uint16_t* w_gu, const uint16_t* ws_gu, uint16_t* hid,
-                                uint16_t* hid_shared, int32_t* queue, hipStream_t stream, float act_clamp) {
+                                uint16_t* hid_shared, int32_t* queue, hipStream_t stream, float act_clamp,
+                                float* partial) {
   if (T == 0) return hipSuccess;
   const Groups gs = make_groups(T, E, k, offsets, perm, ws_gu != nullptr);
+  const int ks = partial && !offsets && ws_gu ? gate_up_splits(T, d, hs) : 1;
   hipLaunchKernelGGL(k_clear_queue, dim3(1), dim3(64), 0, stream, queue);
+  if (ks > 1) {
+    const auto kern = k_expert_tiled<kGateUp, false, true>;
+    hipLaunchKernelGGL(kern, dim3(persistent_grid(kern, kThreads)), dim3(kThreads), 0, stream, x, x, gs, d, h, hs,
+                       w_gu, ws_gu, hid, static_cast<void*>(hid_shared), queue, 0.f, ks, partial);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(k_swiglu_splits, dim3(finish_grid((size_t)T * hs / 4)), dim3(256), 0, stream, partial, ks, T,
+                       hs, act_clamp, hid_shared);
+    return hipGetLastError();
+  }
   const auto kern = act_clamp > 0.f ? k_expert_tiled<kGateUp, true> : k_expert_tiled<kGateUp, false>;
   hipLaunchKernelGGL(kern, dim3(persistent_grid(kern, kThreads)), dim3(kThreads), 0, stream, x, x, gs, d, h, hs,
-                     w_gu, ws_gu, hid, static_cast<void*>(hid_shared), queue, act_clamp);
+                     w_gu, ws_gu, hid, static_cast<void*>(hid_shared), queue, act_clamp, 1, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_down_tiled(int T, int d, int E, int k, int h, int hs, const int32_t* offsets, const uint16_t* hid,
                              const uint16_t* hid_shared, const uint16_t* w_down, const uint16_t* ws_down,
-                             uint16_t* y_perm, float* y_shared, int32_t* queue, hipStream_t stream) {
+                             uint16_t* y_perm, float* y_shared, int32_t* queue, hipStream_t stream, float* partial) {
   if (T == 0) return hipSuccess;
   const Groups gs = make_groups(T, E, k, offsets, nullptr, ws_down != nullptr);
+  const int ks = partial && !offsets && ws_down ? down_splits(T, d, hs) : 1;
   hipLaunchKernelGGL(k_clear_queue, dim3(1), dim3(64), 0, stream, queue);
+  if (ks > 1) {
+    const auto kern = k_expert_tiled<kDown, false, true>;
+    hipLaunchKernelGGL(kern, dim3(persistent_grid(kern, kThreads)), dim3(kThreads), 0, stream, hid, hid_shared, gs,
+                       d, h, hs, w_down, ws_down, y_perm, static_cast<void*>(y_shared), queue, 0.f, ks, partial);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const size_t n = (size_t)T * d;
+    hipLaunchKernelGGL(k_sum_splits, dim3(finish_grid(n / 4)), dim3(256), 0, stream, partial, ks, n, y_shared);
+    return hipGetLastError();
+  }
   const auto kern = k_expert_tiled<kDown>;
   hipLaunchKernelGGL(kern, dim3(persistent_grid(kern, kThreads)), dim3(kThreads), 0, stream, hid, hid_shared, gs, d,
-                     h, hs, w_down, ws_down, y_perm, static_cast<void*>(y_shared), queue, 0.f);
+                     h, hs, w_down, ws_down, y_perm, static_cast<void*>(y_shared), queue, 0.f, 1, nullptr);
   return hipGetLastError();
 }
 

@@ -55,28 +55,35 @@ constexpr size_t kQueueBytes = 256;
 // and E counts the share); 0 means E.  It sets the regime, which follows the
 // average rows per expert.  act_clamp > 0 clips every hidden activation to
 // [-act_clamp, act_clamp] before its bf16 rounding.
+// partial: optional f32 scratch of split_partial_bytes(T, d, hs) for a
+// launch of the shared group alone with few rows, which may then split the
+// reduction over items and add their sums afterwards (in a fixed order).
 hipError_t launch_gate_up(int T, int d, int E, int k, int h, int hs, const uint16_t* x, const int32_t* offsets,
                           const int32_t* perm, const uint16_t* w_gu, const uint16_t* ws_gu, uint16_t* hid,
                           uint16_t* hid_shared, int32_t* queue, hipStream_t stream, int e_total = 0,
-                          float act_clamp = 0.f);
-// partial: optional f32 scratch of down_partial_bytes(T, d) for a launch of
-// the shared group alone with a long reduction and few rows, which then
-// splits the reduction over kDownSplits items and adds their sums.
+                          float act_clamp = 0.f, float* partial = nullptr);
+// The streaming down kernel's split for the shared group alone: kDownSplits
+// items per output tile, up to kDownSplitMaxTokens tokens.
 constexpr int kDownSplits = 4;
 constexpr int kDownSplitMaxTokens = 256;
 hipError_t launch_down(int T, int d, int E, int k, int h, int hs, const int32_t* offsets, const uint16_t* hid,
                        const uint16_t* hid_shared, const uint16_t* w_down, const uint16_t* ws_down, uint16_t* y_perm,
                        float* y_shared, int32_t* queue, hipStream_t stream, int e_total = 0,
                        float* partial = nullptr);
-size_t down_partial_bytes(int T, int d);
+size_t split_partial_bytes(int T, int d, int hs);
 // The compute-regime (LDS-tiled, MFMA 32x32x16) versions of the same two
-// phases; the launchers above pick them when groups are large.
+// phases; the launchers above pick them when groups are large.  With
+// `partial` (the shared group alone, one M-tile of rows) they split the
+// reduction over items as tiled_split_bytes allows for.
 hipError_t launch_gate_up_tiled(int T, int d, int E, int k, int h, int hs, const uint16_t* x, const int32_t* offsets,
                                 const int32_t* perm, const uint16_t* w_gu, const uint16_t* ws_gu, uint16_t* hid,
-                                uint16_t* hid_shared, int32_t* queue, hipStream_t stream, float act_clamp = 0.f);
+                                uint16_t* hid_shared, int32_t* queue, hipStream_t stream, float act_clamp = 0.f,
+                                float* partial = nullptr);
 hipError_t launch_down_tiled(int T, int d, int E, int k, int h, int hs, const int32_t* offsets, const uint16_t* hid,
                              const uint16_t* hid_shared, const uint16_t* w_down, const uint16_t* ws_down,
-                             uint16_t* y_perm, float* y_shared, int32_t* queue, hipStream_t stream);
+                             uint16_t* y_perm, float* y_shared, int32_t* queue, hipStream_t stream,
+                             float* partial = nullptr);
+size_t tiled_split_bytes(int T, int d, int hs);
 size_t expert_hid_bytes(int T, int k, int h);
 size_t shared_hid_bytes(int T, int hs);
 

@@ -215,6 +215,9 @@ def test_dense_validation():
     n = ctypes.c_size_t(0)
     assert L.moe_dense_workspace_bytes(64, 4096, 11264, ctypes.byref(n)) == OK and n.value % 256 == 0
     assert n.value >= 64 * 11264 * 2
+    # Up to 256 tokens the reductions are split over items: room for at least
+    # two f32 partial planes of the gate/up outputs next to the activations.
+    assert n.value >= 64 * 11264 * 2 + 2 * 64 * 2 * 11264 * 4
     assert L.moe_dense_workspace_bytes(64, 4096, 11264, None) == INVALID
     for T, d, H in ((-1, 256, 128), (8, 100, 128), (8, 256, 100), (8, 256, 32), (8, 131072, 128),
                     ((1 << 20) + 1, 256, 128)):

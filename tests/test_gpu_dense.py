@@ -3,9 +3,10 @@ the MTP heads, hidden 11,264) with the CPU oracle's SwiGLU, on generator
 inputs.  The weights are the generator's shared-expert tensors of a workload
 whose shared hidden size is the dense one; the oracle gets the host copy.
 
-Both launch regimes are covered: gate/up runs on the streaming kernels below
-64 tokens and on the LDS-tiled ones from 64; down streams up to 256 tokens
-and is tiled beyond.  Bar: the layer's output tolerance
+Both launch regimes are covered: below 64 tokens the streaming kernels; from
+64 the LDS-tiled ones, which up to 256 tokens (one M-tile) split each weight
+tile's reduction over several items when the reduction is long enough
+(partial sums added afterwards in split order).  Bar: the layer's output tolerance
 (relative L2 <= 5e-3, max |err| <= 3e-2 RMS), every token at the small sizes
 and sampled tokens at T = 8192.
 """
@@ -47,9 +48,10 @@ def oracle_rows(cfg, x_h, rows):
 
 @pytest.mark.parametrize("T,d,H", [
     (1, 256, 128), (37, 256, 384), (63, 512, 256),     # streaming kernels
-    (64, 256, 384), (256, 512, 256),                    # tiled gate/up, streaming down
+    (64, 256, 384), (256, 512, 256),                    # tiled, reductions too short to split
+    (100, 1024, 1024), (200, 2048, 2560),               # tiled with split reductions (2 and 2; 4 and 5)
     (300, 512, 640), (1000, 256, 128),                  # tiled kernels, ragged last M-tile
-    (64, 4096, DENSE_HIDDEN),                           # decode batch at the model's size
+    (64, 4096, DENSE_HIDDEN), (256, 4096, DENSE_HIDDEN),  # the model's size: splits 4 (gate/up) and 22 (down)
 ])
 def test_dense_parity(device, T, d, H):
     cfg = moegen.custom(1, T=T, d=d, hs=H, seed=700 + T + H)
