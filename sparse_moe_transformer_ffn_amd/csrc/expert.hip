@@ -6,15 +6,18 @@
 // [Blog] "Step 3.5 Flash: Open Frontier-Level Intelligence with 11B Active
 // Parameters" §3.2.4 (fused MoE gather/scatter with grouped GEMM).
 //
-// These are the streaming-regime kernels (few rows per expert: decode-sized
-// batches), where the weights are read once and the MFMA work is small: every
-// wave loads its operands straight from HBM/L2 into registers, keeping eight
-// K-steps of weight rows in flight.  The item decomposition is in grouped.h.
+// These are the streaming-regime kernels (under 4 rows per expert on
+// average: decode-sized batches; the dense FFN below 64 tokens), where the
+// weights are read once and the MFMA work is small: every wave loads its
+// operands straight from HBM/L2 into registers, keeping eight K-steps of
+// weight rows in flight.  The item decomposition is in grouped.h.
 //
-// Phase 1 (gate/up): item = BM rows x 64 hidden units; each of the 4 waves
-// owns 16 hidden units j and computes both G = X W_g[j]^T and U = X W_u[j]^T
-// so that SwiGLU (SiLU(G) * U) is applied in registers before the bf16 store.
-// Phase 2 (down): item = BM rows x 64 output columns, reduction over h.
+// Phase 1 (gate/up): item = BM rows x 64 hidden units (or 16 with the
+// reduction split over the four waves); each wave computes both
+// G = X W_g[j]^T and U = X W_u[j]^T for its units j so that SwiGLU
+// (SiLU(G) * U) is applied in registers before the bf16 store.
+// Phase 2 (down): item = BM rows x 128 output columns (two groups of 16 per
+// wave), reduction over h.
 #include "common.h"
 #include "grouped.h"
 #include "kernels.h"
