@@ -7,10 +7,10 @@
 // Parameters" §3.2.4 (fused MoE gather/scatter with grouped GEMM).
 //
 // These are the streaming-regime kernels (under 4 rows per expert on
-// average: decode-sized batches; the dense FFN below 64 tokens), where the
-// weights are read once and the MFMA work is small: every wave loads its
-// operands straight from HBM/L2 into registers, keeping eight K-steps of
-// weight rows in flight.  The item decomposition is in grouped.h.
+// average, 8 for down: decode-sized batches; the dense FFN below 64 tokens),
+// where the weights are read once and the MFMA work is small: every wave
+// loads its operands straight from HBM/L2 into registers, keeping up to eight
+// K-steps of weight rows in flight.  The item decomposition is in grouped.h.
 //
 // Phase 1 (gate/up): item = BM rows x 64 hidden units (or 16 with the
 // reduction split over the four waves); each wave computes both
@@ -172,7 +172,9 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
 // KS > 1 (the shared group alone): the reduction is also split over KS
 //         items, each writing its partial sums to partial[ks][row][d] (f32);
 //         k_sum_partials adds them in ks order into y_shared.
-template <int BM, int KW, int KS = 1, int CPW = 1>
+// UNR: K steps per batch of loads (fewer keep a 32-row item at four waves
+//         per SIMD).
+template <int BM, int KW, int KS = 1, int CPW = 1, int UNR = kUnroll>
 __global__ __launch_bounds__(256) void k_down(Groups gs, int d, int h, int hs, const uint16_t* __restrict__ hid,
                                               const uint16_t* __restrict__ hid_shared,
                                               const uint16_t* __restrict__ w_down,
@@ -213,18 +215,18 @@ __global__ __launch_bounds__(256) void k_down(Groups gs, int d, int h, int hs, c
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) acc[c][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
     int kk = 0;
-    for (; kk + 32 * kUnroll <= klen; kk += 32 * kUnroll) {
-      u32x4 b[CPW][kUnroll], a[MB][kUnroll];
+    for (; kk + 32 * UNR <= klen; kk += 32 * UNR) {
+      u32x4 b[CPW][UNR], a[MB][UNR];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
+      for (int u = 0; u < UNR; ++u)
 #pragma unroll
         for (int c = 0; c < CPW; ++c) b[c][u] = load16(pb + (size_t)c * 16 * H + kk + 32 * u);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) a[mb][u] = va[mb] ? load16(pa[mb] + kk + 32 * u) : zero;
+        for (int u = 0; u < UNR; ++u) a[mb][u] = va[mb] ? load16(pa[mb] + kk + 32 * u) : zero;
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
+      for (int u = 0; u < UNR; ++u)
 #pragma unroll
         for (int c = 0; c < CPW; ++c)
 #pragma unroll
@@ -306,7 +308,10 @@ namespace {
 //   groups span several 16-row M-tiles, each of which reads the expert's
 //   weights again in the streaming kernels, while the tiled ones read them
 //   once per 256 rows (5.3 rows per group: 8% faster tiled; 57 rows per
-//   group: three times faster).
+//   group: three times faster).  Down turns tiled at 8 rows per group;
+//   from 4 to 8 it streams 32-row items (one M-tile for most groups) in
+//   batches of 4 K steps: 448 vs 493 us at 7.1 rows per group, 412 vs
+//   461 us at 5.3, while at 10.7 the tiled down wins (504 vs 542 us).
 // - the shared group alone (the dense FFN): the tiled kernels from 64
 //   tokens.  Up to 256 tokens (one M-tile) they need the caller's split
 //   scratch, which spreads each weight tile's reduction over several items
@@ -316,14 +321,15 @@ namespace {
 //   0.122 ms at 64 tokens, 0.355 -> 0.182 ms at 256; at 16 tokens the
 //   streaming kernels win (0.071 vs 0.110 ms).
 bool use_tiled(int T, int k, int E, const int32_t* offsets, bool down, bool split_scratch) {
-  if (offsets) return (long)T * k >= 4L * E;
+  if (offsets) return (long)T * k >= (down ? 8L : 4L) * E;
   if (T < 64) return false;
   return down ? T > 256 || split_scratch : true;
 }
 
 int pick_bm(int T, int k, int E) {
-  // Average rows per group decides the M-tile: 16 up to 16 rows (every routed
-  // launch that streams), else 32 (the shared group alone from 17 tokens).
+  // Average rows per group decides the M-tile: 16 up to 16 rows, else 32
+  // (the shared group alone from 17 tokens).  Routed down launches of 4 to 8
+  // rows per group take 32-row items in launch_down.
   const long rows = (long)T * k;
   return rows <= 16L * E ? 16 : 32;
 }
@@ -337,12 +343,13 @@ hipError_t gate_up_bm(const uint16_t* x, const Groups& gs, int d, int h, int hs,
   return hipGetLastError();
 }
 
-template <int BM, int KW>
+template <int BM, int KW, int UNR = kUnroll>
 hipError_t down_bm(const Groups& gs, int d, int h, int hs, const uint16_t* hid, const uint16_t* hid_shared,
                    const uint16_t* w_down, const uint16_t* ws_down, uint16_t* y_perm, float* y_shared,
                    hipStream_t stream) {
   // Two 16-column groups per wave where the item width (128 columns) divides d.
-  const auto kern = (KW == 1 && d % 128 == 0) ? k_down<BM, KW, 1, KW == 1 ? 2 : 1> : k_down<BM, KW>;
+  const auto kern =
+      (KW == 1 && d % 128 == 0) ? k_down<BM, KW, 1, KW == 1 ? 2 : 1, UNR> : k_down<BM, KW, 1, 1, UNR>;
   hipLaunchKernelGGL(kern, dim3(persistent_grid(kern) * kOversubscribe), dim3(256), 0, stream, gs, d, h, hs, hid, hid_shared, w_down,
                      ws_down, y_perm, y_shared, nullptr);
   return hipGetLastError();
@@ -407,6 +414,8 @@ hipError_t launch_down(int T, int d, int E, int k, int h, int hs, const int32_t*
     if (pick_bm(T, k, 1) == 16) return down_bm_split<16>(gs, d, hs, hid_shared, ws_down, y_shared, partial, stream);
     return down_bm_split<32>(gs, d, hs, hid_shared, ws_down, y_shared, partial, stream);
   }
+  if (offsets && (long)T * k >= 4L * et)
+    return down_bm<32, 1, 4>(gs, d, h, hs, hid, hid_shared, w_down, ws_down, y_perm, y_shared, stream);
   if (pick_bm(T, k, offsets ? et : 1) == 16) {
     if (split) return down_bm<16, 4>(gs, d, h, hs, hid, hid_shared, w_down, ws_down, y_perm, y_shared, stream);
     return down_bm<16, 1>(gs, d, h, hs, hid, hid_shared, w_down, ws_down, y_perm, y_shared, stream);
