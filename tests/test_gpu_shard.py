@@ -1,6 +1,8 @@
 """moe_expert_swiglu_range: the grouped expert kernels on one contiguous share
 of the experts, as one GPU of an 8-way expert-parallel group would run them
-(36 of 288 experts, with only those experts' weights).
+(36 of 288 experts, with only those experts' weights).  Workloads: tiny,
+decode (streaming kernels), T = 256 (7 rows per expert: tiled gate/up,
+32-row streaming down) and prefill (tiled kernels).
 
 Each share's rows must be bit-identical to the whole call's (same kernels,
 same reduction order), rows outside the share untouched, and sampled rows
@@ -26,7 +28,7 @@ def shard_bounds(E, shards):
     return [(i * per, (i + 1) * per) for i in range(shards)]
 
 
-@pytest.mark.parametrize("idx,shards", [(0, 4), (1, 8), (2, 8)])
+@pytest.mark.parametrize("idx,shards", [(0, 4), (1, 8), (4, 8), (2, 8)])
 def test_expert_shares_match_whole_call(device, idx, shards):
     cfg = moegen.CONFIGS[idx]
     log(f"[shard] config {idx}: {shards} shares of {cfg.E // shards} experts")
