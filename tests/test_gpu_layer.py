@@ -186,6 +186,29 @@ def test_layer_full_size_sampled(device, idx, n_sample):
     torch.cuda.empty_cache()
 
 
+def test_layer_beyond_32_bit_element_indices(device):
+    # 98,304 tokens: y_perm holds T*k*d = 3.2e9 elements, so the rows of the
+    # last experts sit beyond 2^31 elements (every index into it must be
+    # 64-bit).  Sampled tokens, among them ones routed to the highest-index
+    # touched expert (the last rows of y_perm).
+    cfg = moegen.custom(2, T=98304, seed=98304)
+    assert cfg.T * cfg.k * cfg.d > 2 ** 31
+    log(f"[layer] {cfg.T} tokens: y_perm beyond 2^31 elements")
+    dl = DeviceLayer(cfg)
+    buf = run_layer(dl)
+    g_ids = buf.topk_ids.cpu().numpy()
+    cnt = buf.expert_counts.cpu().numpy()
+    last = int(np.nonzero(cnt)[0][-1])
+    rng = np.random.default_rng(5)
+    tokens = set(rng.choice(cfg.T, 10, replace=False).tolist()) | {0, cfg.T - 1}
+    tokens |= set(np.where(np.any(g_ids == last, axis=1))[0][[0, -1]].tolist())
+    off = buf.expert_offsets.cpu().numpy()
+    assert int(off[last]) * cfg.d > 2 ** 31
+    check_layer(dl, buf, np.array(sorted(tokens)))
+    del dl, buf
+    torch.cuda.empty_cache()
+
+
 def test_stack_layers_on_generated_inputs(device):
     # Every layer of the 12-layer stack (distinct weights, T=256) on its own
     # generated input, all weights resident, launched back to back.
