@@ -74,6 +74,21 @@ def test_dense_prefill_sampled_rows(device):
     assert np.all(np.isfinite(y))
 
 
+def test_dense_beyond_32_bit_element_indices(device):
+    # 196,608 tokens at hidden 11,264: the hidden activations hold 2.2e9
+    # elements, so the rows of the last tokens sit beyond 2^31 elements.
+    T, d, H = 196608, 4096, DENSE_HIDDEN
+    assert T * H > 2 ** 31
+    cfg = moegen.custom(2, T=T, hs=H, seed=196608)
+    log(f"[dense] T={T} d={d} H={H}: hidden activations beyond 2^31 elements")
+    x_h = moegen.x(cfg)
+    y = run_dense(cfg, x_h, H)
+    rows = np.unique(np.concatenate([[0, T // 2, T - 256, T - 1], moegen.random_ids(78, 1, T, 8)[0]]))
+    assert rows[-1] * H > 2 ** 31
+    ref = oracle_rows(cfg, x_h, rows)
+    check_output(y[rows], ref, f"dense T={T} sampled")
+
+
 def test_dense_zero_tokens_and_rejections(device):
     d, H = 256, 128
     y = torch.full((1, d), 5.0, device="cuda")
