@@ -19,7 +19,7 @@ import oracle
 import sparse_moe_transformer_ffn_amd as moe
 from tests._util import to_bf16
 from tests.gpu_harness import (DeviceLayer, bf16_dev, bf16_host, check_output, f32_dev, i32_dev, log,
-                               oracle_layer_tokens)
+                               oracle_layer_tokens, oracle_route_all)
 
 pytestmark = pytest.mark.gpu
 
@@ -105,13 +105,15 @@ def test_combine_residual_parity(device, T, d, k, with_shared):
     assert np.all(np.abs(g - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6 * rms)
 
 
-def test_prenorm_block_decode(device):
-    # The whole block at the decode size: h -> moe_rmsnorm_route -> permute ->
-    # experts (shared fused) -> moe_combine_residual, against h + the oracle's
-    # layer on the oracle's normalised rows, on sampled tokens whose routing
-    # matches.
-    cfg = moegen.CONFIGS[1]
-    log("[prenorm-block] decode")
+@pytest.mark.parametrize("idx,stride", [(1, 4), (2, 512)])
+def test_prenorm_block(device, idx, stride):
+    # The whole block: h -> moe_rmsnorm_route -> permute -> experts (shared
+    # fused) -> moe_combine_residual, against h + the oracle's layer on the
+    # oracle's normalised rows, on sampled tokens whose routing matches: the
+    # decode size (router normalising as it loads) and the prefill size
+    # (normalisation pass, staged router, tiled experts).
+    cfg = moegen.CONFIGS[idx]
+    log(f"[prenorm-block] {cfg.name}")
     h_h = stream_rows(cfg)
     x_ref = oracle.rmsnorm(h_h, None, 1e-6)
     dl = DeviceLayer(cfg, x_host=x_ref)   # weights and router; x replaced below
@@ -129,10 +131,10 @@ def test_prenorm_block_decode(device):
     moe.moe_combine_residual(s, buf.y_perm, buf.pair_pos, buf.topk_weights, buf.y_shared, cfg.routed_scale, h, y)
     torch.cuda.synchronize()
     g_ids = buf.topk_ids.cpu().numpy()
-    o_ids, _, o_gap, _ = oracle.route(x_ref, dl.wr_h, dl.b_h, k, logit_bias=dl.c_h)
+    o_ids, _, o_gap = oracle_route_all(dl)   # dl's host rows are x_ref
     same = np.all(g_ids == o_ids, axis=1)
     assert np.all(o_gap[~same] < INPUT_ULP_GAP)
-    toks = np.array([t for t in range(0, T, 4) if same[t]], np.int32)
+    toks = np.array([t for t in range(0, T, stride) if same[t]], np.int32)
     _, y_ffn = oracle_layer_tokens(dl, toks, o_ids[toks])
     y_ref = moegen.bf16_to_f32(h_h[toks]).astype(np.float64) + y_ffn
     check_output(moegen.bf16_to_f32(bf16_host(y))[toks], y_ref, "pre-norm block y")
