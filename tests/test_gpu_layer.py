@@ -146,6 +146,8 @@ def test_layer_edge_shapes(device, T, k, hs, scale):
     (1000, 256, 16, 2, 128, 192),    # hidden % 128 != 0: direct gate/up, tiled down
     (700, 192, 8, 3, 64, 64),        # d % 256 != 0: direct kernels in the compute regime
     (1536, 512, 6, 1, 256, 0),       # k = 1, no shared expert
+    (100, 256, 1, 1, 128, 128),      # one expert: a dense SwiGLU plus the shared expert
+    (64, 256, 2, 2, 128, 0),         # k = E: every token takes every expert
     (64, 256, 1024, 16, 128, 128),   # E and k at their limits: streaming kernels
     (300, 256, 1024, 16, 128, 128),  # ... 4.7 rows per expert: tiled gate/up, 32-row streaming down
 ])
