@@ -36,6 +36,41 @@ constexpr int kUnroll = 8;  // K steps (of 32) per batch of loads
 // these kernels share no weights, so nothing is lost in L2.
 constexpr int kOversubscribe = 4;
 
+// Weight rows are read as whole 128-byte lines with non-temporal loads: lane
+// l reads 16 bytes of row l >> 3 (rows 8.. for `hi`) at segment l & 7 of a
+// 64-wide K block, so one load covers 8 rows x 128 B and the 16 rows of a
+// wave's operand take two loads per block.  The MFMA lane layout (row l & 15,
+// 32 bytes per row per step) would split every line over two loads; with
+// whole lines a plain read of this chip reaches 6.5-6.8 TB/s instead of
+// 6.0-6.1, and gate/up at decode took 480 us instead of 543.  The lanes then
+// trade data (ds_bpermute) into the MFMA layout; the weights are read once,
+// so the non-temporal hint costs no reuse.
+struct Lines {
+  u32x4 lo, hi;  // rows 0-7 and 8-15 of one 64-wide K block
+};
+
+__device__ __forceinline__ Lines load_lines(const uint16_t* p8, size_t hi_off) {
+  Lines L;
+  L.lo = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p8));
+  L.hi = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p8 + hi_off));
+  return L;
+}
+
+// MFMA operand of K step s of the block (elements 32 s .. 32 s + 31): lane l
+// gets row l & 15, elements 8 (l >> 4) .. +7 of the step, from lane
+// ((l & 7) << 3) | ((l >> 4) + 4 s) of `lo` or `hi`.  addr = 4 x that lane;
+// hi = (l & 15) >= 8.
+__device__ __forceinline__ u32x4 lines_operand(const Lines& L, int addr, bool hi) {
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int v0 = __builtin_amdgcn_ds_bpermute(addr, (int)L.lo[q]);
+    const int v1 = __builtin_amdgcn_ds_bpermute(addr, (int)L.hi[q]);
+    o[q] = (uint32_t)(hi ? v1 : v0);
+  }
+  return o;
+}
+
 }  // namespace
 
 // Phase 1: hid[row, j] = SiLU(x_row . W_g[j]) * (x_row . W_u[j]).  Routed
@@ -70,6 +105,10 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
     uint16_t* out = it.shared ? hid_shared : hid;
     const uint16_t* pg = wbase + (size_t)j * d + kbeg + kq * 8;
     const uint16_t* pu = wbase + (size_t)(H + j) * d + kbeg + kq * 8;
+    // Whole-line loads of the same 16 gate and up rows (see load_lines).
+    const int j8 = j - r16 + (lane >> 3);
+    const uint16_t* pg8 = wbase + (size_t)j8 * d + kbeg + (lane & 7) * 8;
+    const uint16_t* pu8 = wbase + (size_t)(H + j8) * d + kbeg + (lane & 7) * 8;
     const uint16_t* pa[MB];
     bool va[MB];
 #pragma unroll
@@ -86,28 +125,34 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
       ag[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
       au[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    const int addr0 = 4 * (((lane & 7) << 3) | kq), addr1 = addr0 + 16;
+    const bool hirow = r16 >= 8;
     // K in batches of kUnroll steps: every load of a batch is issued before
     // its MFMAs, so each wave keeps kUnroll weight rows' worth of requests in
     // flight (the streaming regime is latency x bandwidth bound).
     int kk = 0;
     for (; kk + 32 * kUnroll <= klen; kk += 32 * kUnroll) {
-      u32x4 bg[kUnroll], bu[kUnroll], a[MB][kUnroll];
+      Lines lg[kUnroll / 2], lu[kUnroll / 2];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        bg[u] = load16(pg + kk + 32 * u);
-        bu[u] = load16(pu + kk + 32 * u);
+      for (int b2 = 0; b2 < kUnroll / 2; ++b2) {
+        lg[b2] = load_lines(pg8 + kk + 64 * b2, (size_t)8 * d);
+        lu[b2] = load_lines(pu8 + kk + 64 * b2, (size_t)8 * d);
       }
+      u32x4 a[MB][kUnroll];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) a[mb][u] = va[mb] ? load16(pa[mb] + kk + 32 * u) : zero;
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
+      for (int u = 0; u < kUnroll; ++u) {
+        const u32x4 bg = lines_operand(lg[u / 2], u % 2 ? addr1 : addr0, hirow);
+        const u32x4 bu = lines_operand(lu[u / 2], u % 2 ? addr1 : addr0, hirow);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          ag[mb] = mfma_16x16x32(a[mb][u], bg[u], ag[mb]);
-          au[mb] = mfma_16x16x32(a[mb][u], bu[u], au[mb]);
+          ag[mb] = mfma_16x16x32(a[mb][u], bg, ag[mb]);
+          au[mb] = mfma_16x16x32(a[mb][u], bu, au[mb]);
         }
+      }
     }
     for (; kk < klen; kk += 32) {
       const u32x4 bg = load16(pg + kk);
@@ -214,13 +259,19 @@ __global__ __launch_bounds__(256) void k_down(Groups gs, int d, int h, int hs, c
     for (int c = 0; c < CPW; ++c)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) acc[c][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Whole-line loads of the same 16-row groups (see load_lines).
+    static_assert(UNR % 2 == 0, "whole-line loads cover two K steps");
+    const uint16_t* pb8 = pb - (size_t)r16 * H - kq * 8 + (size_t)(lane >> 3) * H + (lane & 7) * 8;
+    const int addr0 = 4 * (((lane & 7) << 3) | kq), addr1 = addr0 + 16;
+    const bool hirow = r16 >= 8;
     int kk = 0;
     for (; kk + 32 * UNR <= klen; kk += 32 * UNR) {
-      u32x4 b[CPW][UNR], a[MB][UNR];
+      Lines lb[CPW][UNR / 2];
 #pragma unroll
-      for (int u = 0; u < UNR; ++u)
+      for (int b2 = 0; b2 < UNR / 2; ++b2)
 #pragma unroll
-        for (int c = 0; c < CPW; ++c) b[c][u] = load16(pb + (size_t)c * 16 * H + kk + 32 * u);
+        for (int c = 0; c < CPW; ++c) lb[c][b2] = load_lines(pb8 + (size_t)c * 16 * H + kk + 64 * b2, (size_t)8 * H);
+      u32x4 a[MB][UNR];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -228,9 +279,11 @@ __global__ __launch_bounds__(256) void k_down(Groups gs, int d, int h, int hs, c
 #pragma unroll
       for (int u = 0; u < UNR; ++u)
 #pragma unroll
-        for (int c = 0; c < CPW; ++c)
+        for (int c = 0; c < CPW; ++c) {
+          const u32x4 b = lines_operand(lb[c][u / 2], u % 2 ? addr1 : addr0, hirow);
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) acc[c][mb] = mfma_16x16x32(a[mb][u], b[c][u], acc[c][mb]);
+          for (int mb = 0; mb < MB; ++mb) acc[c][mb] = mfma_16x16x32(a[mb][u], b, acc[c][mb]);
+        }
     }
     for (; kk < klen; kk += 32) {
 #pragma unroll
