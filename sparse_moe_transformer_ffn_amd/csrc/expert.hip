@@ -6,8 +6,8 @@
 // [Blog] "Step 3.5 Flash: Open Frontier-Level Intelligence with 11B Active
 // Parameters" §3.2.4 (fused MoE gather/scatter with grouped GEMM).
 //
-// These are the streaming-regime kernels (under 4 rows per expert on
-// average, 8 for down: decode-sized batches; the dense FFN below 64 tokens),
+// These are the streaming-regime kernels (under 5 rows per expert on
+// average, 10 for down: decode-sized batches; the dense FFN below 64 tokens),
 // where the weights are read once and the MFMA work is small: every wave
 // loads its operands straight from HBM/L2 into registers, keeping up to eight
 // K-steps of weight rows in flight.  The item decomposition is in grouped.h.
@@ -356,15 +356,16 @@ namespace {
 
 // Which regime a phase runs in (crossovers measured on the 288-expert layer,
 // d = 4,096, and on the dense FFN of hidden 11,264):
-// - routed launches: the LDS-tiled kernels from 4 rows per routed group on
-//   average.  At 3.6 rows per group the two regimes tie; above it more
-//   groups span several 16-row M-tiles, each of which reads the expert's
-//   weights again in the streaming kernels, while the tiled ones read them
-//   once per 256 rows (5.3 rows per group: 8% faster tiled; 57 rows per
-//   group: three times faster).  Down turns tiled at 8 rows per group;
-//   from 4 to 8 it streams 32-row items (one M-tile for most groups) in
-//   batches of 4 K steps: 448 vs 493 us at 7.1 rows per group, 412 vs
-//   461 us at 5.3, while at 10.7 the tiled down wins (504 vs 542 us).
+// - routed gate/up: the LDS-tiled kernels from 5 rows per routed group on
+//   average.  Below, the streaming kernels win (4.0 rows per group: 647 vs
+//   717 us); at 5.3 the two tie (744 vs 739 us); above, more groups span
+//   several 16-row M-tiles, each of which reads the expert's weights again
+//   in the streaming kernels, while the tiled ones read them once per 256
+//   rows (7.1 rows per group: 881 vs 798 us; 57: three times faster).
+// - routed down: tiled from 10 rows per group; from 4 to 10 it streams
+//   32-row items (one M-tile for most groups) in batches of 4 K steps
+//   (8.0 rows per group: 424 vs 496 us tiled; 10.7: 500 vs 505; 12.4: 566
+//   vs 513), below 4 16-row items.
 // - the shared group alone (the dense FFN): the tiled kernels from 64
 //   tokens.  Up to 256 tokens (one M-tile) they need the caller's split
 //   scratch, which spreads each weight tile's reduction over several items
@@ -374,14 +375,14 @@ namespace {
 //   0.122 ms at 64 tokens, 0.355 -> 0.182 ms at 256; at 16 tokens the
 //   streaming kernels win (0.071 vs 0.110 ms).
 bool use_tiled(int T, int k, int E, const int32_t* offsets, bool down, bool split_scratch) {
-  if (offsets) return (long)T * k >= (down ? 8L : 4L) * E;
+  if (offsets) return (long)T * k >= (down ? 10L : 5L) * E;
   if (T < 64) return false;
   return down ? T > 256 || split_scratch : true;
 }
 
 int pick_bm(int T, int k, int E) {
   // Average rows per group decides the M-tile: 16 up to 16 rows, else 32
-  // (the shared group alone from 17 tokens).  Routed down launches of 4 to 8
+  // (the shared group alone from 17 tokens).  Routed down launches of 4 to 10
   // rows per group take 32-row items in launch_down.
   const long rows = (long)T * k;
   return rows <= 16L * E ? 16 : 32;

@@ -130,7 +130,8 @@ def test_layer_diagnostic_side_outputs(device, idx):
 
 @pytest.mark.parametrize("T,k,hs,scale", [
     (1, 8, 1280, 1.0), (3, 1, 1280, 1.0), (97, 8, 0, 0.5), (130, 8, 1280, 2.0),  # streaming kernels
-    (144, 8, 1280, 1.0), (256, 8, 1280, 1.0),  # tiled from 4 rows per expert on average
+    (144, 8, 1280, 1.0),                       # 4 rows per expert: streaming gate/up, 32-row down items
+    (256, 8, 1280, 1.0), (400, 8, 1280, 1.0),  # tiled gate/up from 5 rows per expert, tiled down from 10
 ])
 def test_layer_edge_shapes(device, T, k, hs, scale):
     cfg = moegen.custom(1, T=T, k=k, hs=hs, routed_scale=scale, seed=500 + T)
@@ -149,7 +150,7 @@ def test_layer_edge_shapes(device, T, k, hs, scale):
     (100, 256, 1, 1, 128, 128),      # one expert: a dense SwiGLU plus the shared expert
     (64, 256, 2, 2, 128, 0),         # k = E: every token takes every expert
     (64, 256, 1024, 16, 128, 128),   # E and k at their limits: streaming kernels
-    (300, 256, 1024, 16, 128, 128),  # ... 4.7 rows per expert: tiled gate/up, 32-row streaming down
+    (350, 256, 1024, 16, 128, 128),  # ... 5.5 rows per expert: tiled gate/up, 32-row streaming down
 ])
 def test_layer_compute_regime_small(device, T, d, E, k, h, hs):
     cfg = moegen.custom(0, T=T, d=d, E=E, k=k, h=h, hs=hs, seed=900 + T)
