@@ -82,7 +82,8 @@ __device__ __forceinline__ u32x4 lines_operand(const Lines& L, int addr, bool hi
 //         added in wave order (a fixed order: results do not depend on the
 //         schedule).  Items are four times smaller, so the last items of the
 //         launch, which run alone, take a quarter of the time.
-template <int BM, int KW, bool CLAMP = false>
+// UNR: K steps per batch of loads.
+template <int BM, int KW, bool CLAMP = false, int UNR = kUnroll>
 __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x, Groups gs, int d, int h, int hs,
                                                  const uint16_t* __restrict__ w_gu,
                                                  const uint16_t* __restrict__ ws_gu, uint16_t* __restrict__ hid,
@@ -127,24 +128,24 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
     }
     const int addr0 = 4 * (((lane & 7) << 3) | kq), addr1 = addr0 + 16;
     const bool hirow = r16 >= 8;
-    // K in batches of kUnroll steps: every load of a batch is issued before
-    // its MFMAs, so each wave keeps kUnroll weight rows' worth of requests in
+    // K in batches of UNR steps: every load of a batch is issued before
+    // its MFMAs, so each wave keeps UNR weight rows' worth of requests in
     // flight (the streaming regime is latency x bandwidth bound).
     int kk = 0;
-    for (; kk + 32 * kUnroll <= klen; kk += 32 * kUnroll) {
-      Lines lg[kUnroll / 2], lu[kUnroll / 2];
+    for (; kk + 32 * UNR <= klen; kk += 32 * UNR) {
+      Lines lg[UNR / 2], lu[UNR / 2];
 #pragma unroll
-      for (int b2 = 0; b2 < kUnroll / 2; ++b2) {
+      for (int b2 = 0; b2 < UNR / 2; ++b2) {
         lg[b2] = load_lines(pg8 + kk + 64 * b2, (size_t)8 * d);
         lu[b2] = load_lines(pu8 + kk + 64 * b2, (size_t)8 * d);
       }
-      u32x4 a[MB][kUnroll];
+      u32x4 a[MB][UNR];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) a[mb][u] = va[mb] ? load16(pa[mb] + kk + 32 * u) : zero;
+        for (int u = 0; u < UNR; ++u) a[mb][u] = va[mb] ? load16(pa[mb] + kk + 32 * u) : zero;
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < UNR; ++u) {
         const u32x4 bg = lines_operand(lg[u / 2], u % 2 ? addr1 : addr0, hirow);
         const u32x4 bu = lines_operand(lu[u / 2], u % 2 ? addr1 : addr0, hirow);
 #pragma unroll
@@ -373,7 +374,7 @@ namespace {
 //   it down stays on the streaming kernels, whose own split covers its long
 //   reduction.  Dense FFN per call, streaming -> tiled with splits: 0.162 ->
 //   0.122 ms at 64 tokens, 0.355 -> 0.182 ms at 256; at 16 tokens the
-//   streaming kernels win (0.071 vs 0.110 ms).
+//   streaming kernels win (0.061 vs 0.110 ms).
 bool use_tiled(int T, int k, int E, const int32_t* offsets, bool down, bool split_scratch) {
   if (offsets) return (long)T * k >= (down ? 10L : 5L) * E;
   if (T < 64) return false;
@@ -388,10 +389,10 @@ int pick_bm(int T, int k, int E) {
   return rows <= 16L * E ? 16 : 32;
 }
 
-template <int BM, int KW>
+template <int BM, int KW, int UNR = kUnroll>
 hipError_t gate_up_bm(const uint16_t* x, const Groups& gs, int d, int h, int hs, const uint16_t* w_gu,
                       const uint16_t* ws_gu, uint16_t* hid, uint16_t* hid_shared, float clamp, hipStream_t stream) {
-  const auto kern = clamp > 0.f ? k_gate_up<BM, KW, true> : k_gate_up<BM, KW, false>;
+  const auto kern = clamp > 0.f ? k_gate_up<BM, KW, true, UNR> : k_gate_up<BM, KW, false, UNR>;
   hipLaunchKernelGGL(kern, dim3(persistent_grid(kern) * kOversubscribe), dim3(256), 0, stream, x, gs, d, h, hs, w_gu, ws_gu, hid,
                      hid_shared, clamp);
   return hipGetLastError();
@@ -410,10 +411,10 @@ hipError_t down_bm(const Groups& gs, int d, int h, int hs, const uint16_t* hid, 
 }
 
 // The shared group alone with its reduction also split over items.
-template <int BM>
+template <int BM, int UNR = kUnroll>
 hipError_t down_bm_split(const Groups& gs, int d, int hs, const uint16_t* hid_shared, const uint16_t* ws_down,
                          float* y_shared, float* partial, hipStream_t stream) {
-  const auto kern = k_down<BM, 4, kDownSplits>;
+  const auto kern = k_down<BM, 4, kDownSplits, 1, UNR>;
   hipLaunchKernelGGL(kern, dim3(persistent_grid(kern) * kOversubscribe), dim3(256), 0, stream, gs, d, 0, hs, nullptr, hid_shared,
                      nullptr, ws_down, nullptr, nullptr, partial);
   hipError_t err = hipGetLastError();
@@ -440,10 +441,22 @@ hipError_t launch_gate_up(int T, int d, int E, int k, int h, int hs, const uint1
   const Groups gs = make_groups(T, E, k, offsets, perm, ws_gu != nullptr);
   // Reduction split over the waves when every quarter is whole 32-wide steps.
   const bool split = d % 128 == 0;
+  // The shared group alone below 64 tokens: one M-tile, so every weight row
+  // is read once, in batches short enough for three waves per SIMD, so one
+  // round of blocks covers all items (704 at hidden 11,264).  Dense FFN of
+  // hidden 11,264 per call against batches of 8 steps and 32-row M-tiles:
+  // 8 tokens 0.062 -> 0.055 ms, 16: 0.072 -> 0.061, 32: 0.093 -> 0.079,
+  // 48: 0.157 -> 0.099.
+  if (!offsets && split && T <= 16)
+    return gate_up_bm<16, 4, 4>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, act_clamp, stream);
   if (pick_bm(T, k, offsets ? et : 1) == 16) {
     if (split) return gate_up_bm<16, 4>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, act_clamp, stream);
     return gate_up_bm<16, 1>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, act_clamp, stream);
   }
+  if (!offsets && split && T <= 32)
+    return gate_up_bm<32, 4, 4>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, act_clamp, stream);
+  if (!offsets && split && T <= 64)
+    return gate_up_bm<64, 4, 2>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, act_clamp, stream);
   if (split) return gate_up_bm<32, 4>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, act_clamp, stream);
   return gate_up_bm<32, 1>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, act_clamp, stream);
 }
@@ -464,8 +477,11 @@ hipError_t launch_down(int T, int d, int E, int k, int h, int hs, const int32_t*
   const bool split = !offsets && hs >= 4096 && hs % 128 == 0 && d % 16 == 0;
   // With few rows that still leaves too few items: split the reduction over
   // items too, into the caller's partial-sum buffer.
+  // Up to 64 tokens one M-tile, as in gate/up.
   if (split && partial && T <= kDownSplitMaxTokens && hs % (128 * kDownSplits) == 0) {
-    if (pick_bm(T, k, 1) == 16) return down_bm_split<16>(gs, d, hs, hid_shared, ws_down, y_shared, partial, stream);
+    if (T <= 16) return down_bm_split<16, 4>(gs, d, hs, hid_shared, ws_down, y_shared, partial, stream);
+    if (T <= 32) return down_bm_split<32, 4>(gs, d, hs, hid_shared, ws_down, y_shared, partial, stream);
+    if (T <= 64) return down_bm_split<64, 4>(gs, d, hs, hid_shared, ws_down, y_shared, partial, stream);
     return down_bm_split<32>(gs, d, hs, hid_shared, ws_down, y_shared, partial, stream);
   }
   if (offsets && (long)T * k >= 4L * et)
