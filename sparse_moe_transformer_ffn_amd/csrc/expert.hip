@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
   const int klen = d / KW, kbeg = KW > 1 ? wave * klen : 0;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   for (int w = (int)blockIdx.x; w < items; w += gridDim.x) {
-    const Item it = decode_item<0>(ip, gs, BM, h / UNITS, hs / UNITS, w);
+    const Item it = decode_item_xcd(ip, gs, BM, h / UNITS, hs / UNITS, w);
     const int H = it.shared ? hs : h;
     const int j = it.nt * UNITS + (KW > 1 ? 0 : wave * 16) + r16;
     const uint16_t* wbase = it.shared ? ws_gu : w_gu + (size_t)it.group * 2 * h * d;
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256) void k_down(Groups gs, int d, int h, int hs, c
   const int r16 = lane & 15, kq = lane >> 4;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   for (int w = (int)blockIdx.x; w < items; w += gridDim.x) {
-    const Item it = decode_item<0>(ip, gs, BM, ncol, ncol * KS, w);
+    const Item it = decode_item_xcd(ip, gs, BM, ncol, ncol * KS, w);
     const int H = it.shared ? hs : h;
     const int ks = KS > 1 ? it.nt / ncol : 0, cg = KS > 1 ? it.nt % ncol : it.nt;
     const int klen = H / (KW * KS), kbeg = (ks * KW + (KW > 1 ? wave : 0)) * klen;

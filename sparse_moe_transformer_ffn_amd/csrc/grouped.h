@@ -127,6 +127,38 @@ __device__ __forceinline__ Item decode_item(const int* ip, const Groups& gs, int
   return it;
 }
 
+// Item w -> (group, N-tile, first row) for kernels whose item w runs on XCD
+// w mod 8 (item w to block w mod grid, grid a multiple of 8, block b on XCD
+// b mod 8).  Inside a group the items go in runs of 8 N-tiles (fewer in the
+// last run) times all M-tiles, N-tile fastest: the M-tiles of one N-tile get
+// item numbers 8 apart, so they run side by side on one XCD and its L2 fetches
+// their weight rows from HBM once for all of them.  A group of one M-tile
+// keeps N-tile order.
+__device__ __forceinline__ Item decode_item_xcd(const int* ip, const Groups& gs, int BM, int nt_routed, int nt_shared,
+                                                int w) {
+  int lo = 0, hi = gs.count() - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (ip[mid] <= w) lo = mid;
+    else hi = mid - 1;
+  }
+  const GroupView v = group_view(gs, lo);
+  Item it;
+  it.group = lo;
+  it.shared = v.shared;
+  it.row0 = v.row0;
+  it.nrows = v.nrows;
+  const int tiles = (v.nrows + BM - 1) / BM;
+  const int nt = v.shared ? nt_shared : nt_routed;
+  const int wl = w - ip[lo];
+  const int run = wl / (8 * tiles);
+  const int r = wl - run * 8 * tiles;
+  const int span = min(8, nt - run * 8);  // N-tiles in this run
+  it.nt = run * 8 + r % span;
+  it.m0 = (r / span) * BM;
+  return it;
+}
+
 // Persistent grid: as many blocks as can be resident at once on the current
 // device (occupancy x compute units); a kernel launches this many, or a
 // multiple of it when it wants the dispatcher to balance the tail.  Cached
