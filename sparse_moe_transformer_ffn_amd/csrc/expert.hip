@@ -9,8 +9,10 @@
 // These are the streaming-regime kernels (under 5 rows per expert on
 // average, 10 for down: decode-sized batches; the dense FFN below 64 tokens),
 // where the weights are read once and the MFMA work is small: every wave
-// loads its operands straight from HBM/L2 into registers, keeping up to eight
-// K-steps of weight rows in flight.  The item decomposition is in grouped.h.
+// loads its operands straight from HBM/L2 into registers, keeping a batch of
+// 2 to 8 K-steps of weight rows in flight (6 at decode: the batch length
+// trades bytes in flight per wave against waves per SIMD).  The item
+// decomposition is in grouped.h.
 //
 // Phase 1 (gate/up): item = BM rows x 64 hidden units (or 16 with the
 // reduction split over the four waves); each wave computes both
