@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void k_perm_count(const int32_t* __restrict__ 
 // One block of 1024 threads; thread e owns expert e.  Its column of chunk
 // counts is read kScanBatch chunks at a time (loads of a batch in flight
 // together), summed, then rewritten as running bases.
-constexpr int kScanBatch = 16;
+constexpr int kScanBatch = 32;
 
 __global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ chunk_cnt, int nchunks, int E,
                                                     int32_t* __restrict__ offsets) {
