@@ -7,7 +7,7 @@
 // Parameters" §3.2.4 (fused MoE gather/scatter with grouped GEMM).
 //
 // These are the streaming-regime kernels (under 5 rows per expert on
-// average, 10 for down: decode-sized batches; the dense FFN below 64 tokens),
+// average, 10 for down: decode-sized batches; the dense FFN up to 64 tokens),
 // where the weights are read once and the MFMA work is small: every wave
 // loads its operands straight from HBM/L2 into registers, keeping a batch of
 // 2 to 8 K-steps of weight rows in flight (6 at decode: the batch length
@@ -85,7 +85,10 @@ __device__ __forceinline__ u32x4 lines_operand(const Lines& L, int addr, bool hi
 //         schedule).  Items are four times smaller, so the last items of the
 //         launch, which run alone, take a quarter of the time.
 // UNR: K steps per batch of loads.
-template <int BM, int KW, bool CLAMP = false, int UNR = kUnroll>
+// CPW: groups of 16 hidden units per wave (their gate and up rows share each
+//      load of token rows: with 64-row items the token operand would
+//      otherwise be twice the weight bytes per wave).
+template <int BM, int KW, bool CLAMP = false, int UNR = kUnroll, int CPW = 1>
 __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x, Groups gs, int d, int h, int hs,
                                                  const uint16_t* __restrict__ w_gu,
                                                  const uint16_t* __restrict__ ws_gu, uint16_t* __restrict__ hid,
@@ -93,8 +96,8 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
   __shared__ int ip[kMaxGroups + 1];
   __shared__ int wsum[4];
   constexpr int MB = BM / 16;
-  constexpr int UNITS = 64 / KW;  // hidden units per item
-  __shared__ float red[KW > 1 ? KW - 1 : 1][2 * MB * 4][kWave];
+  constexpr int UNITS = 64 * CPW / KW;  // hidden units per item
+  __shared__ float red[KW > 1 ? KW - 1 : 1][2 * CPW * MB * 4][kWave];
   const int items = item_prefix<BM>(ip, wsum, gs, h / UNITS, hs / UNITS);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int r16 = lane & 15, kq = lane >> 4;
@@ -103,7 +106,8 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
   for (int w = (int)blockIdx.x; w < items; w += gridDim.x) {
     const Item it = decode_item_xcd(ip, gs, BM, h / UNITS, hs / UNITS, w);
     const int H = it.shared ? hs : h;
-    const int j = it.nt * UNITS + (KW > 1 ? 0 : wave * 16) + r16;
+    // Unit of this lane in its first group; group c adds 16 c.
+    const int j = it.nt * UNITS + (KW > 1 ? 0 : wave * 16 * CPW) + r16;
     const uint16_t* wbase = it.shared ? ws_gu : w_gu + (size_t)it.group * 2 * h * d;
     uint16_t* out = it.shared ? hid_shared : hid;
     const uint16_t* pg = wbase + (size_t)j * d + kbeg + kq * 8;
@@ -122,12 +126,14 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
       if (va[mb]) tok = it.shared ? r : gs.perm[it.row0 + r] / gs.k;
       pa[mb] = x + (size_t)tok * d + kbeg + kq * 8;
     }
-    f32x4 ag[MB], au[MB];
+    f32x4 ag[CPW][MB], au[CPW][MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      ag[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      au[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        ag[c][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        au[c][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     const int addr0 = 4 * (((lane & 7) << 3) | kq), addr1 = addr0 + 16;
     const bool hirow = r16 >= 8;
     // K in batches of UNR steps: every load of a batch is issued before
@@ -135,12 +141,15 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
     // flight (the streaming regime is latency x bandwidth bound).  A batch of
     // `steps` < UNR (an even count) takes the whole-line pairs left at the end.
     auto batch = [&](int kk, int steps) {
-      Lines lg[UNR / 2], lu[UNR / 2];
+      Lines lg[CPW][UNR / 2], lu[CPW][UNR / 2];
 #pragma unroll
       for (int b2 = 0; b2 < UNR / 2; ++b2)
         if (2 * b2 < steps) {
-          lg[b2] = load_lines(pg8 + kk + 64 * b2, (size_t)8 * d);
-          lu[b2] = load_lines(pu8 + kk + 64 * b2, (size_t)8 * d);
+#pragma unroll
+          for (int c = 0; c < CPW; ++c) {
+            lg[c][b2] = load_lines(pg8 + (size_t)c * 16 * d + kk + 64 * b2, (size_t)8 * d);
+            lu[c][b2] = load_lines(pu8 + (size_t)c * 16 * d + kk + 64 * b2, (size_t)8 * d);
+          }
         }
       u32x4 a[MB][UNR];
 #pragma unroll
@@ -151,12 +160,15 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
 #pragma unroll
       for (int u = 0; u < UNR; ++u)
         if (u < steps) {
-          const u32x4 bg = lines_operand(lg[u / 2], u % 2 ? addr1 : addr0, hirow);
-          const u32x4 bu = lines_operand(lu[u / 2], u % 2 ? addr1 : addr0, hirow);
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            ag[mb] = mfma_16x16x32(a[mb][u], bg, ag[mb]);
-            au[mb] = mfma_16x16x32(a[mb][u], bu, au[mb]);
+          for (int c = 0; c < CPW; ++c) {
+            const u32x4 bg = lines_operand(lg[c][u / 2], u % 2 ? addr1 : addr0, hirow);
+            const u32x4 bu = lines_operand(lu[c][u / 2], u % 2 ? addr1 : addr0, hirow);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+              ag[c][mb] = mfma_16x16x32(a[mb][u], bg, ag[c][mb]);
+              au[c][mb] = mfma_16x16x32(a[mb][u], bu, au[c][mb]);
+            }
           }
         }
     };
@@ -167,52 +179,61 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
       kk += 32 * rest;
     }
     for (; kk < klen; kk += 32) {
-      const u32x4 bg = load16(pg + kk);
-      const u32x4 bu = load16(pu + kk);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const u32x4 a = va[mb] ? load16(pa[mb] + kk) : zero;
-        ag[mb] = mfma_16x16x32(a, bg, ag[mb]);
-        au[mb] = mfma_16x16x32(a, bu, au[mb]);
+      for (int c = 0; c < CPW; ++c) {
+        const u32x4 bg = load16(pg + (size_t)c * 16 * d + kk);
+        const u32x4 bu = load16(pu + (size_t)c * 16 * d + kk);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const u32x4 a = va[mb] ? load16(pa[mb] + kk) : zero;
+          ag[c][mb] = mfma_16x16x32(a, bg, ag[c][mb]);
+          au[c][mb] = mfma_16x16x32(a, bu, au[c][mb]);
+        }
       }
     }
     if (KW > 1) {
       // Waves 1..KW-1 hand their partial sums to wave 0.
       if (wave > 0) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int c = 0; c < CPW; ++c)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            red[wave - 1][mb * 8 + i][lane] = ag[mb][i];
-            red[wave - 1][mb * 8 + 4 + i][lane] = au[mb][i];
-          }
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              red[wave - 1][(c * MB + mb) * 8 + i][lane] = ag[c][mb][i];
+              red[wave - 1][(c * MB + mb) * 8 + 4 + i][lane] = au[c][mb][i];
+            }
       }
       __syncthreads();
       if (wave == 0) {
 #pragma unroll
         for (int q = 0; q < KW - 1; ++q)
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
+          for (int c = 0; c < CPW; ++c)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              ag[mb][i] += red[q][mb * 8 + i][lane];
-              au[mb][i] += red[q][mb * 8 + 4 + i][lane];
-            }
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                ag[c][mb][i] += red[q][(c * MB + mb) * 8 + i][lane];
+                au[c][mb][i] += red[q][(c * MB + mb) * 8 + 4 + i][lane];
+              }
       }
       __syncthreads();  // red[] free for the next item
       if (wave > 0) continue;
     }
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+    for (int c = 0; c < CPW; ++c)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = it.m0 + mb * 16 + kq * 4 + i;
-        if (r < it.nrows) {
-          const float g = ag[mb][i], u = au[mb][i];
-          out[(size_t)(it.row0 + r) * H + j] = (uint16_t)f32_to_bf16(swiglu(g, u, CLAMP ? clamp : 0.f));
+      for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = it.m0 + mb * 16 + kq * 4 + i;
+          if (r < it.nrows) {
+            const float g = ag[c][mb][i], u = au[c][mb][i];
+            out[(size_t)(it.row0 + r) * H + j + 16 * c] = (uint16_t)f32_to_bf16(swiglu(g, u, CLAMP ? clamp : 0.f));
+          }
         }
       }
-    }
   }
 }
 
@@ -222,10 +243,10 @@ __global__ __launch_bounds__(256) void k_gate_up(const uint16_t* __restrict__ x,
 //         of 16 columns over the whole reduction (the routed experts' 1,280);
 //         with CPW = 2 each wave keeps 16 weight rows' loads in flight per
 //         batch, as the gate/up waves do (292 vs 300 µs at decode).
-// KW = 4: an item is BM rows x 16 columns and wave w owns the w-th quarter of
-//         the reduction, the partial sums added in LDS in wave order: for a
-//         long reduction (the dense FFN's 11,264) with few rows, four times
-//         as many items keep enough waves streaming.
+// KW = 4: an item is BM rows x 16·CPW columns and wave w owns the w-th
+//         quarter of the reduction, the partial sums added in LDS in wave
+//         order: for a long reduction (the dense FFN's 11,264) with few rows,
+//         four times as many items keep enough waves streaming.
 // KS > 1 (the shared group alone): the reduction is also split over KS
 //         items, each writing its partial sums to partial[ks][row][d] (f32);
 //         k_sum_partials adds them in ks order into y_shared.
@@ -237,12 +258,11 @@ __global__ __launch_bounds__(256) void k_down(Groups gs, int d, int h, int hs, c
                                               const uint16_t* __restrict__ w_down,
                                               const uint16_t* __restrict__ ws_down, uint16_t* __restrict__ y_perm,
                                               float* __restrict__ y_shared, float* __restrict__ partial) {
-  static_assert(KW == 1 || CPW == 1, "column groups per wave need the whole reduction per wave");
   __shared__ int ip[kMaxGroups + 1];
   __shared__ int wsum[4];
   constexpr int MB = BM / 16;
   constexpr int COLS = 64 * CPW / KW;  // output columns per item
-  __shared__ float red[KW > 1 ? KW - 1 : 1][MB * 4][kWave];
+  __shared__ float red[KW > 1 ? KW - 1 : 1][CPW * MB * 4][kWave];
   const int ncol = d / COLS;
   const int items = item_prefix<BM>(ip, wsum, gs, ncol, ncol * KS);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -321,18 +341,22 @@ __global__ __launch_bounds__(256) void k_down(Groups gs, int d, int h, int hs, c
     if (KW > 1) {
       if (wave > 0) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int c = 0; c < CPW; ++c)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) red[wave - 1][mb * 4 + i][lane] = acc[0][mb][i];
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[wave - 1][(c * MB + mb) * 4 + i][lane] = acc[c][mb][i];
       }
       __syncthreads();
       if (wave == 0) {
 #pragma unroll
         for (int q = 0; q < KW - 1; ++q)
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
+          for (int c = 0; c < CPW; ++c)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[0][mb][i] += red[q][mb * 4 + i][lane];
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[c][mb][i] += red[q][(c * MB + mb) * 4 + i][lane];
       }
       __syncthreads();  // red[] free for the next item
       if (wave > 0) continue;
@@ -388,17 +412,18 @@ namespace {
 //   32-row items (one M-tile for most groups) in batches of 4 K steps
 //   (8.0 rows per group: 424 vs 496 us tiled; 10.7: 500 vs 505; 12.4: 566
 //   vs 513), below 4 16-row items.
-// - the shared group alone (the dense FFN): the tiled kernels from 64
+// - the shared group alone (the dense FFN): the tiled kernels above 64
 //   tokens.  Up to 256 tokens (one M-tile) they need the caller's split
 //   scratch, which spreads each weight tile's reduction over several items
 //   (gate/up 88 tiles x 4 splits, down 16 x 22 at hidden 11,264); without
 //   it down stays on the streaming kernels, whose own split covers its long
-//   reduction.  Dense FFN per call, streaming -> tiled with splits: 0.162 ->
-//   0.122 ms at 64 tokens, 0.355 -> 0.182 ms at 256; at 16 tokens the
-//   streaming kernels win (0.061 vs 0.110 ms).
+//   reduction.  Dense FFN per call, streaming (32-row items) -> tiled with
+//   splits: 0.229 -> 0.139 ms at 128 tokens, 0.355 -> 0.182 ms at 256; up to
+//   64 tokens the streaming kernels with one M-tile win (64 tokens: 0.092 vs
+//   0.122 ms; 80 to 128 tokens: within 3% of the tiled ones).
 bool use_tiled(int T, int k, int E, const int32_t* offsets, bool down, bool split_scratch) {
   if (offsets) return (long)T * k >= (down ? 10L : 5L) * E;
-  if (T < 64) return false;
+  if (T <= 64) return false;
   return down ? T > 256 || split_scratch : true;
 }
 
@@ -410,10 +435,10 @@ int pick_bm(int T, int k, int E) {
   return rows <= 16L * E ? 16 : 32;
 }
 
-template <int BM, int KW, int UNR = kUnroll>
+template <int BM, int KW, int UNR = kUnroll, int CPW = 1>
 hipError_t gate_up_bm(const uint16_t* x, const Groups& gs, int d, int h, int hs, const uint16_t* w_gu,
                       const uint16_t* ws_gu, uint16_t* hid, uint16_t* hid_shared, float clamp, hipStream_t stream) {
-  const auto kern = clamp > 0.f ? k_gate_up<BM, KW, true, UNR> : k_gate_up<BM, KW, false, UNR>;
+  const auto kern = clamp > 0.f ? k_gate_up<BM, KW, true, UNR, CPW> : k_gate_up<BM, KW, false, UNR, CPW>;
   hipLaunchKernelGGL(kern, dim3(persistent_grid(kern) * kOversubscribe), dim3(256), 0, stream, x, gs, d, h, hs, w_gu, ws_gu, hid,
                      hid_shared, clamp);
   return hipGetLastError();
@@ -432,10 +457,10 @@ hipError_t down_bm(const Groups& gs, int d, int h, int hs, const uint16_t* hid, 
 }
 
 // The shared group alone with its reduction also split over items.
-template <int BM, int UNR = kUnroll>
+template <int BM, int UNR = kUnroll, int CPW = 1>
 hipError_t down_bm_split(const Groups& gs, int d, int hs, const uint16_t* hid_shared, const uint16_t* ws_down,
                          float* y_shared, float* partial, hipStream_t stream) {
-  const auto kern = k_down<BM, 4, kDownSplits, 1, UNR>;
+  const auto kern = k_down<BM, 4, kDownSplits, CPW, UNR>;
   hipLaunchKernelGGL(kern, dim3(persistent_grid(kern) * kOversubscribe), dim3(256), 0, stream, gs, d, 0, hs, nullptr, hid_shared,
                      nullptr, ws_down, nullptr, nullptr, partial);
   hipError_t err = hipGetLastError();
@@ -462,12 +487,13 @@ hipError_t launch_gate_up(int T, int d, int E, int k, int h, int hs, const uint1
   const Groups gs = make_groups(T, E, k, offsets, perm, ws_gu != nullptr);
   // Reduction split over the waves when every quarter is whole 32-wide steps.
   const bool split = d % 128 == 0;
-  // The shared group alone below 64 tokens: one M-tile, so every weight row
-  // is read once, in batches short enough for three waves per SIMD, so one
-  // round of blocks covers all items (704 at hidden 11,264).  Dense FFN of
-  // hidden 11,264 per call against batches of 8 steps and 32-row M-tiles:
-  // 8 tokens 0.062 -> 0.055 ms, 16: 0.072 -> 0.061, 32: 0.093 -> 0.079,
-  // 48: 0.157 -> 0.099.
+  // The shared group alone up to 64 tokens: one M-tile, so every weight row
+  // is read once, in short batches so that one round of blocks covers all
+  // items.  From 17 rows each wave takes two groups of 16 units, whose four
+  // weight row sets share each load of token rows.  Dense FFN of hidden 11,264
+  // per call against batches of 8 steps, 32-row M-tiles and one group per
+  // wave (tiled kernels at 64 tokens): 8 tokens 0.062 -> 0.055 ms, 16: 0.072
+  // -> 0.061, 32: 0.093 -> 0.075, 48: 0.157 -> 0.082, 64: 0.122 -> 0.092.
   if (!offsets && split && T <= 16)
     return gate_up_bm<16, 4, 4>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, act_clamp, stream);
   // 16-row items in batches of 6 steps (three waves per SIMD): 483 -> 477 us
@@ -477,9 +503,9 @@ hipError_t launch_gate_up(int T, int d, int E, int k, int h, int hs, const uint1
     return gate_up_bm<16, 1>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, act_clamp, stream);
   }
   if (!offsets && split && T <= 32)
-    return gate_up_bm<32, 4, 4>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, act_clamp, stream);
+    return gate_up_bm<32, 4, 2, 2>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, act_clamp, stream);
   if (!offsets && split && T <= 64)
-    return gate_up_bm<64, 4, 2>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, act_clamp, stream);
+    return gate_up_bm<64, 4, 2, 2>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, act_clamp, stream);
   if (split) return gate_up_bm<32, 4>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, act_clamp, stream);
   return gate_up_bm<32, 1>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, act_clamp, stream);
 }
@@ -500,11 +526,13 @@ hipError_t launch_down(int T, int d, int E, int k, int h, int hs, const int32_t*
   const bool split = !offsets && hs >= 4096 && hs % 128 == 0 && d % 16 == 0;
   // With few rows that still leaves too few items: split the reduction over
   // items too, into the caller's partial-sum buffer.
-  // Up to 64 tokens one M-tile, as in gate/up.
+  // Up to 64 tokens one M-tile, as in gate/up; from 17 rows each wave takes
+  // four groups of 16 columns (d is a multiple of 64), which share each load
+  // of hidden rows.
   if (split && partial && T <= kDownSplitMaxTokens && hs % (128 * kDownSplits) == 0) {
     if (T <= 16) return down_bm_split<16, 4>(gs, d, hs, hid_shared, ws_down, y_shared, partial, stream);
-    if (T <= 32) return down_bm_split<32, 4>(gs, d, hs, hid_shared, ws_down, y_shared, partial, stream);
-    if (T <= 64) return down_bm_split<64, 4>(gs, d, hs, hid_shared, ws_down, y_shared, partial, stream);
+    if (T <= 32) return down_bm_split<32, 4, 4>(gs, d, hs, hid_shared, ws_down, y_shared, partial, stream);
+    if (T <= 64) return down_bm_split<64, 2, 4>(gs, d, hs, hid_shared, ws_down, y_shared, partial, stream);
     return down_bm_split<32>(gs, d, hs, hid_shared, ws_down, y_shared, partial, stream);
   }
   if (offsets && (long)T * k >= 4L * et)

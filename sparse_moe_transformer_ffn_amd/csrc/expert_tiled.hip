@@ -1,6 +1,6 @@
 // expert_tiled.hip -- grouped SwiGLU expert GEMMs for the compute regime
 // (from 5 rows per expert on average, 10 for down, up to prefill-sized
-// batches; the dense FFN from 64 tokens), bf16 MFMA 32x32x16.
+// batches; the dense FFN above 64 tokens), bf16 MFMA 32x32x16.
 //
 // Layer definition as in expert.hip ([Digest] "Step 3.5 Flash 技术论文深度解读"
 // architecture table and activation-explosion cause 3; grouped layout after

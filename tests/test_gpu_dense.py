@@ -3,8 +3,8 @@ the MTP heads, hidden 11,264) with the CPU oracle's SwiGLU, on generator
 inputs.  The weights are the generator's shared-expert tensors of a workload
 whose shared hidden size is the dense one; the oracle gets the host copy.
 
-Both launch regimes are covered: below 64 tokens the streaming kernels (one
-M-tile of 16, 32 or 64 rows, the down reduction split over items); from
+Both launch regimes are covered: up to 64 tokens the streaming kernels (one
+M-tile of 16, 32 or 64 rows, the down reduction split over items); above
 64 the LDS-tiled ones, which up to 256 tokens (one M-tile) split each weight
 tile's reduction over several items when the reduction is long enough
 (partial sums added afterwards in split order).  Bar: the layer's output tolerance
@@ -49,10 +49,12 @@ def oracle_rows(cfg, x_h, rows):
 
 @pytest.mark.parametrize("T,d,H", [
     (1, 256, 128), (37, 256, 384), (63, 512, 256),     # streaming kernels
-    (64, 256, 384), (256, 512, 256),                    # tiled, reductions too short to split
+    (64, 256, 384),                                     # streaming, one 64-row M-tile
+    (65, 256, 384), (256, 512, 256),                    # tiled, reductions too short to split
     (100, 1024, 1024), (200, 2048, 2560),               # tiled with split reductions (2 and 2; 4 and 5)
     (300, 512, 640), (1000, 256, 128),                  # tiled kernels, ragged last M-tile
-    (64, 4096, DENSE_HIDDEN), (256, 4096, DENSE_HIDDEN),  # the model's size: splits 4 (gate/up) and 22 (down)
+    (128, 4096, DENSE_HIDDEN), (256, 4096, DENSE_HIDDEN),  # the model's size: splits 4 (gate/up) and 22 (down)
+    (64, 4096, DENSE_HIDDEN),                             # streaming, one 64-row M-tile, down split 4 ways
     (16, 4096, DENSE_HIDDEN), (32, 4096, DENSE_HIDDEN),   # streaming at the model's size: 16- and 32-row
     (48, 4096, DENSE_HIDDEN),                             # M-tiles, and one 64-row M-tile
 ])

@@ -49,13 +49,15 @@ def test_layer_graph_replays_match_eager(device, idx):
     np.testing.assert_array_equal(bf16_host(eager.y), y_ref)
 
 
-def test_dense_split_graph_replays_match_eager(device):
-    # The dense FFN at 64 tokens runs the tiled kernels with split reductions
-    # (partial sums in the workspace, added by a second kernel): replays of
-    # the captured call must equal the eager call bit for bit.
-    T, d, H = 64, 4096, 11264
+@pytest.mark.parametrize("T", [64, 128])
+def test_dense_split_graph_replays_match_eager(device, T):
+    # The dense FFN with split reductions (partial sums in the workspace,
+    # added by a second kernel): at 64 tokens the streaming kernels (down
+    # split over items), at 128 the tiled ones (both phases split).  Replays
+    # of the captured call must equal the eager call bit for bit.
+    d, H = 4096, 11264
     cfg = moegen.custom(1, T=T, hs=H, seed=777)
-    log("[graph] dense FFN T=64 (split reductions)")
+    log(f"[graph] dense FFN T={T} (split reductions)")
     w_gu = torch.empty((2 * H, d), dtype=torch.bfloat16, device="cuda")
     w_d = torch.empty((d, H), dtype=torch.bfloat16, device="cuda")
     moegen.fill_shared_device(cfg, 0, w_gu.data_ptr(), w_d.data_ptr(), torch.cuda.current_stream().cuda_stream)
