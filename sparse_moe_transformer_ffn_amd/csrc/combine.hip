@@ -22,7 +22,11 @@ namespace moe {
 // row's sum of squares (f32: per thread in column order, then a butterfly
 // over the wave and the four waves in order) and stores it by permuted row,
 // row_ss[pair_pos[t*k+j]], and for the shared expert's row, shared_ss[t].
-template <int KMAX, bool DIAG>
+// NT: non-temporal loads of the routed and shared rows and non-temporal
+// stores of y, for large batches where nothing of them is read again soon
+// (k = 8, d = 4,096, 8,192 tokens: 145 -> 125 us; at 64 tokens the plain
+// policy is 0.2-0.5 us faster).
+template <int KMAX, bool DIAG, bool NT>
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y_perm,
                                                  const int32_t* __restrict__ pair_pos,
                                                  const float* __restrict__ topk_weights,
@@ -46,12 +50,21 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y_
     u32x4 rows[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
-      if (j < k) rows[j] = load16(y_perm + (size_t)pos[j] * d + c);
+      if (j < k)
+        rows[j] = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(y_perm + (size_t)pos[j] * d + c))
+                     : load16(y_perm + (size_t)pos[j] * d + c);
     float4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
     if (y_shared) {
       const float4* s = reinterpret_cast<const float4*>(y_shared + (size_t)t * d + c);
-      s0 = s[0];
-      s1 = s[1];
+      if constexpr (NT) {
+        const f32x4* sv = reinterpret_cast<const f32x4*>(s);
+        const f32x4 a0 = __builtin_nontemporal_load(sv), a1 = __builtin_nontemporal_load(sv + 1);
+        s0 = make_float4(a0[0], a0[1], a0[2], a0[3]);
+        s1 = make_float4(a1[0], a1[1], a1[2], a1[3]);
+      } else {
+        s0 = s[0];
+        s1 = s[1];
+      }
     }
     const u32x4 res = residual ? load16(residual + (size_t)t * d + c) : u32x4{0u, 0u, 0u, 0u};
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -87,7 +100,8 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y_
 #pragma unroll
       for (int q = 0; q < 8; ++q) o[q] = rv[q] + o[q];
     }
-    *reinterpret_cast<u32x4*>(y + (size_t)t * d + c) = pack8(o);
+    if constexpr (NT) __builtin_nontemporal_store(pack8(o), reinterpret_cast<u32x4*>(y + (size_t)t * d + c));
+    else *reinterpret_cast<u32x4*>(y + (size_t)t * d + c) = pack8(o);
   }
   if constexpr (DIAG) {
     const int wave = tid / kWave, lane = tid % kWave;
@@ -230,9 +244,17 @@ hipError_t launch_combine(int T, int d, int k, const uint16_t* y_perm, const int
   float* shared_ss = diag && y_shared ? row_ss + (size_t)T * k : nullptr;
   hipError_t err;
   if (T > 0) {
-#define MOE_COMBINE(KMAX, DIAG)                                                                                   \
-  hipLaunchKernelGGL((k_combine<KMAX, DIAG>), dim3(T), dim3(256), 0, stream, y_perm, pair_pos, topk_weights, y_shared, \
-                     residual, routed_scale, d, k, y, row_ss, shared_ss)
+    // Non-temporal from 64 MB of routed rows.
+    const bool nt = (size_t)T * k * d * sizeof(uint16_t) >= ((size_t)64 << 20);
+#define MOE_COMBINE(KMAX, DIAG)                                                                                    \
+  do {                                                                                                             \
+    if (nt)                                                                                                        \
+      hipLaunchKernelGGL((k_combine<KMAX, DIAG, true>), dim3(T), dim3(256), 0, stream, y_perm, pair_pos,           \
+                         topk_weights, y_shared, residual, routed_scale, d, k, y, row_ss, shared_ss);              \
+    else                                                                                                           \
+      hipLaunchKernelGGL((k_combine<KMAX, DIAG, false>), dim3(T), dim3(256), 0, stream, y_perm, pair_pos,          \
+                         topk_weights, y_shared, residual, routed_scale, d, k, y, row_ss, shared_ss);              \
+  } while (0)
     if (k <= 8) {
       if (diag) MOE_COMBINE(8, true);
       else MOE_COMBINE(8, false);
