@@ -33,10 +33,12 @@ constexpr int kUnroll = 8;  // K steps (of 32) per batch of loads
 // Blocks launched per resident block slot.  Item w goes to block w % grid and
 // block b runs on XCD b % 8, so every round of items is spread over all eight
 // XCDs (an XCD-contiguous order left the last, partial round on the first few
-// XCDs); with four blocks per slot the dispatcher hands the remaining blocks
-// to whichever CU of an XCD frees first, which evens out the tail.  Items of
-// these kernels share no weights, so nothing is lost in L2.
-constexpr int kOversubscribe = 4;
+// XCDs); with eight blocks per slot the dispatcher hands the remaining blocks
+// to whichever CU of an XCD frees first, which evens out the tail (decode
+// gate/up with 2, 4, 8, 16 blocks per slot: 481, 476, 470, 469 us; down 251,
+// 246, 245, 250 us).  Items of these kernels share no weights across XCDs,
+// so nothing is lost in L2.
+constexpr int kOversubscribe = 8;
 
 // Weight rows are read as whole 128-byte lines with non-temporal loads: lane
 // l reads 16 bytes of row l >> 3 (rows 8.. for `hi`) at segment l & 7 of a
