@@ -33,12 +33,15 @@ def lib():
         L.oracle_expert.argtypes = [_I, _I, _P, _P, _P, _P]
         L.oracle_layer.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
                                    _I, _P, _P, _P, _P, _P]
+        L.oracle_forward_given_routing.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
+                                                   ctypes.c_float, _I, _P, _P, _P, _P]
         L.oracle_rmsnorm.argtypes = [_I, _I, _P, _P, ctypes.c_float, _P]
         L.oracle_combine.argtypes = [_I, _I, _I, _P, _P, _P, _P, ctypes.c_float, _P, _P]
         L.oracle_route_diag.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P]
         L.oracle_activation_rms.argtypes = [_I, _I, _P, _P]
         L.oracle_expert_clamped.argtypes = [_I, _I, _P, _P, _P, ctypes.c_double, _P]
-        for f in (L.oracle_route, L.oracle_permute, L.oracle_expert, L.oracle_layer, L.oracle_rmsnorm,
+        for f in (L.oracle_route, L.oracle_permute, L.oracle_expert, L.oracle_layer,
+                  L.oracle_forward_given_routing, L.oracle_rmsnorm,
                   L.oracle_combine, L.oracle_route_diag, L.oracle_activation_rms, L.oracle_expert_clamped):
             f.restype = ctypes.c_int
         _lib = L
@@ -117,6 +120,22 @@ def expert_clamped(x_row, w_gu, w_d, clamp):
     return out
 
 
+def _expert_ptrs(w_gu, w_d, E):
+    """ctypes arrays of expert weight pointers (NULL where None) and the
+    contiguous copies that keep them alive."""
+    keep = []
+    gu_ptrs = (ctypes.c_void_p * E)()
+    d_ptrs = (ctypes.c_void_p * E)()
+    for e in range(E):
+        if w_gu[e] is not None:
+            a = _c(w_gu[e], np.uint16)
+            b = _c(w_d[e], np.uint16)
+            keep += [a, b]
+            gu_ptrs[e] = a.ctypes.data
+            d_ptrs[e] = b.ctypes.data
+    return gu_ptrs, d_ptrs, keep
+
+
 def layer(x, w_router, sel_bias, k, w_gu, w_d, ws_gu=None, ws_d=None, routed_scale=1.0, logit_bias=None,
           tokens=None):
     """Whole layer on the listed token rows (all rows if tokens is None).
@@ -132,16 +151,7 @@ def layer(x, w_router, sel_bias, k, w_gu, w_d, ws_gu=None, ws_d=None, routed_sca
     E = w_router.shape[0]
     assert len(w_gu) == E and len(w_d) == E
     h = next(w.shape[0] // 2 for w in w_gu if w is not None)
-    keep = []
-    gu_ptrs = (ctypes.c_void_p * E)()
-    d_ptrs = (ctypes.c_void_p * E)()
-    for e in range(E):
-        if w_gu[e] is not None:
-            a = _c(w_gu[e], np.uint16)
-            b = _c(w_d[e], np.uint16)
-            keep += [a, b]
-            gu_ptrs[e] = a.ctypes.data
-            d_ptrs[e] = b.ctypes.data
+    gu_ptrs, d_ptrs, keep = _expert_ptrs(w_gu, w_d, E)
     hs = 0
     if ws_gu is not None:
         ws_gu = _c(ws_gu, np.uint16)
@@ -156,8 +166,42 @@ def layer(x, w_router, sel_bias, k, w_gu, w_d, ws_gu=None, ws_d=None, routed_sca
     rc = lib().oracle_layer(T, d, E, k, h, hs, _ptr(x), _ptr(w_router), _ptr(sel_bias), _ptr(logit_bias), gu_ptrs,
                             d_ptrs, _ptr(ws_gu), _ptr(ws_d), float(routed_scale), n, _ptr(tok), _ptr(ids),
                             _ptr(wts), _ptr(gap), _ptr(y))
+    del keep
     _check(rc, "oracle_layer")
     return ids, wts, gap, y
+
+
+def forward_given_routing(x, w_router, ids, w_gu, w_d, ws_gu=None, ws_d=None, routed_scale=1.0, logit_bias=None,
+                          tokens=None):
+    """The layer on the listed token rows under the given chosen sets ids
+    [n,k] (each row ascending and distinct): weights from the unbiased scores
+    of those experts, the experts, the shared expert and the scaled combine.
+    Returns (weights [n,k] f32, y [n,d] f32)."""
+    x = _c(x, np.uint16)
+    w_router = _c(w_router, np.uint16)
+    logit_bias = _c(logit_bias, np.float32)
+    ids = _c(ids, np.int32)
+    T, d = x.shape
+    E = w_router.shape[0]
+    n, k = ids.shape
+    assert len(w_gu) == E and len(w_d) == E
+    h = next(w.shape[0] // 2 for w in w_gu if w is not None)
+    gu_ptrs, d_ptrs, keep = _expert_ptrs(w_gu, w_d, E)
+    hs = 0
+    if ws_gu is not None:
+        ws_gu = _c(ws_gu, np.uint16)
+        ws_d = _c(ws_d, np.uint16)
+        hs = ws_gu.shape[0] // 2
+    tok = None if tokens is None else np.ascontiguousarray(tokens, np.int32)
+    assert (T if tok is None else tok.shape[0]) == n
+    wts = np.zeros((n, k), np.float32)
+    y = np.zeros((n, d), np.float32)
+    rc = lib().oracle_forward_given_routing(T, d, E, k, h, hs, _ptr(x), _ptr(w_router), _ptr(logit_bias), gu_ptrs,
+                                            d_ptrs, _ptr(ws_gu), _ptr(ws_d), float(routed_scale), n, _ptr(tok),
+                                            _ptr(ids), _ptr(wts), _ptr(y))
+    del keep
+    _check(rc, "oracle_forward_given_routing")
+    return wts, y
 
 
 def combine(y_perm, pair_pos, weights, y_shared=None, routed_scale=1.0, residual=None):

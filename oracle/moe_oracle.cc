@@ -133,9 +133,54 @@ void swiglu_token(int d, int h, const uint16_t* x_row, const uint16_t* w_gu, con
 
 bool shape_ok(int T, int d, int E, int k) { return T >= 0 && d > 0 && E > 0 && k >= 1 && k <= E; }
 
+// Steps after the selection for one token whose chosen set is given: the
+// weights from the unbiased scores of the chosen experts ([Blog] §2.2.2: the
+// mask s_{t,e} of the top-K set), the chosen SwiGLU experts, the shared
+// expert, and the scaled sum in ascending expert order ([Blog] §4.1.2).
+//   ids [k]      the chosen set, ascending, distinct, in [0, E)
+//   wts [k]      out: w_e = s_e / sum_{S_t} s
+//   y   [d]      out (f32)
+// Returns -3 if a chosen expert has no weights.
+int forward_token_given_set(int d, int E, int k, int h, int hs, const uint16_t* xr, const uint16_t* w_router,
+                            const float* logit_bias, const int32_t* ids, const uint16_t* const* w_gu,
+                            const uint16_t* const* w_d, const uint16_t* ws_gu, const uint16_t* ws_d,
+                            float routed_scale, float* wts, float* y) {
+  std::vector<float> s(k), shared(d), expert_out((size_t)k * d);
+  double total = 0.0;
+  for (int j = 0; j < k; ++j) {
+    const int e = ids[j];
+    float z = dot_bf16(xr, w_router + (size_t)e * d, d);
+    if (logit_bias) z = z + logit_bias[e];
+    s[j] = (float)sigmoid((double)z);
+    total += (double)s[j];
+  }
+  for (int j = 0; j < k; ++j) wts[j] = (float)((double)s[j] / total);
+  for (int j = 0; j < k; ++j) {
+    if (!w_gu[ids[j]] || !w_d[ids[j]]) return -3;
+    swiglu_token(d, h, xr, w_gu[ids[j]], w_d[ids[j]], expert_out.data() + (size_t)j * d);
+  }
+  if (hs > 0) swiglu_token(d, hs, xr, ws_gu, ws_d, shared.data());
+  for (int i = 0; i < d; ++i) {
+    double routed = 0.0;
+    for (int j = 0; j < k; ++j) routed += (double)wts[j] * (double)expert_out[(size_t)j * d + i];
+    const double base = hs > 0 ? (double)shared[i] : 0.0;
+    y[i] = (float)(base + (double)routed_scale * routed);
+  }
+  return 0;
+}
+
+bool set_ok(int E, int k, const int32_t* ids) {
+  for (int j = 0; j < k; ++j) {
+    if (ids[j] < 0 || ids[j] >= E) return false;
+    if (j > 0 && ids[j] <= ids[j - 1]) return false;
+  }
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
+
 
 // Router for all T tokens.  x [T,d] bf16, w_router [E,d] bf16, sel_bias [E]
 // f32, logit_bias [E] f32 or NULL.  Outputs topk_ids [T,k] (ascending),
@@ -211,27 +256,50 @@ int oracle_layer(int T, int d, int E, int k, int h, int hs, const uint16_t* x, c
     return -1;
   if (hs > 0 && (!ws_gu || !ws_d)) return -1;
   std::vector<int32_t> ids(k);
-  std::vector<float> wts(k), shared(d), expert_out((size_t)k * d);
+  std::vector<float> wts(k), wts_route(k);
   for (int n = 0; n < n_tok; ++n) {
     const int t = tokens ? tokens[n] : n;
     if (t < 0 || t >= T) return -2;
     const uint16_t* xr = x + (size_t)t * d;
     float gap = 0.f;
-    route_token(d, E, k, xr, w_router, sel_bias, logit_bias, ids.data(), wts.data(), &gap, nullptr);
-    for (int j = 0; j < k; ++j) {
-      if (!w_gu[ids[j]] || !w_d[ids[j]]) return -3;
-      swiglu_token(d, h, xr, w_gu[ids[j]], w_d[ids[j]], expert_out.data() + (size_t)j * d);
-    }
-    if (hs > 0) swiglu_token(d, hs, xr, ws_gu, ws_d, shared.data());
-    for (int i = 0; i < d; ++i) {
-      double routed = 0.0;
-      for (int j = 0; j < k; ++j) routed += (double)wts[j] * (double)expert_out[(size_t)j * d + i];
-      const double base = hs > 0 ? (double)shared[i] : 0.0;
-      y[(size_t)n * d + i] = (float)(base + (double)routed_scale * routed);
-    }
+    route_token(d, E, k, xr, w_router, sel_bias, logit_bias, ids.data(), wts_route.data(), &gap, nullptr);
+    const int rc = forward_token_given_set(d, E, k, h, hs, xr, w_router, logit_bias, ids.data(), w_gu, w_d, ws_gu,
+                                           ws_d, routed_scale, wts.data(), y + (size_t)n * d);
+    if (rc != 0) return rc;
     if (topk_ids) memcpy(topk_ids + (size_t)n * k, ids.data(), sizeof(int32_t) * k);
     if (topk_weights) memcpy(topk_weights + (size_t)n * k, wts.data(), sizeof(float) * k);
     if (topk_gap) topk_gap[n] = gap;
+  }
+  return 0;
+}
+
+// The layer for listed tokens under a given routing: every step after the
+// selection (weights, experts, shared expert, scaled combine) on the chosen
+// sets passed in, instead of the sets this oracle's own selection would
+// pick.  Output comparisons "given the same routing" use it where two sets
+// are both correct (a near-tie between the k-th and (k+1)-th biased score).
+//   ids [n_tok, k]   each row ascending, distinct, in [0, E) (else -4)
+//   tokens           n_tok row indices into x (NULL: rows 0..n_tok-1)
+// Outputs: topk_weights [n,k] (NULL allowed) and y [n,d] f32.  Other
+// arguments as oracle_layer (no selection bias: it does not enter).
+int oracle_forward_given_routing(int T, int d, int E, int k, int h, int hs, const uint16_t* x,
+                                 const uint16_t* w_router, const float* logit_bias, const uint16_t* const* w_gu,
+                                 const uint16_t* const* w_d, const uint16_t* ws_gu, const uint16_t* ws_d,
+                                 float routed_scale, int n_tok, const int32_t* tokens, const int32_t* ids,
+                                 float* topk_weights, float* y) {
+  if (!shape_ok(T, d, E, k) || h <= 0 || hs < 0 || n_tok < 0 || !x || !w_router || !w_gu || !w_d || !ids || !y)
+    return -1;
+  if (hs > 0 && (!ws_gu || !ws_d)) return -1;
+  std::vector<float> wts(k);
+  for (int n = 0; n < n_tok; ++n) {
+    const int t = tokens ? tokens[n] : n;
+    if (t < 0 || t >= T) return -2;
+    const int32_t* set = ids + (size_t)n * k;
+    if (!set_ok(E, k, set)) return -4;
+    const int rc = forward_token_given_set(d, E, k, h, hs, x + (size_t)t * d, w_router, logit_bias, set, w_gu, w_d,
+                                           ws_gu, ws_d, routed_scale, wts.data(), y + (size_t)n * d);
+    if (rc != 0) return rc;
+    if (topk_weights) memcpy(topk_weights + (size_t)n * k, wts.data(), sizeof(float) * k);
   }
   return 0;
 }

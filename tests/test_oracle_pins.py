@@ -428,6 +428,95 @@ def test_layer_token_subset_matches_full():
         oracle.layer(x, wr, b, k, gu_missing, wd_missing, sgu, swd, tokens=np.array([0]))
 
 
+# ------------------------------------------------ layer under given routing --
+# [Blog] §2.2.2: the output is defined by the top-K set S_t and its mask; the
+# oracle's forward_given_routing takes S_t as an input.
+
+def _perm_expert(rng, d, h, scale):
+    """A permutation-matrix expert (see test_expert_permutation_matrix_closed_form)
+    and its closed form as a function of x (float64)."""
+    pi = rng.permutation(d)[:h]
+    rho = rng.permutation(d)[:h]
+    tau = rng.integers(0, h, d)
+    c = (np.linspace(-2, 2, h) * scale).astype(np.float32)
+    gu = np.zeros((2 * h, d), np.float32)
+    gu[np.arange(h), pi] = c
+    gu[h + np.arange(h), rho] = 1.0
+    wd = np.zeros((d, h), np.float32)
+    wd[np.arange(d), tau] = 1.0
+    cf = from_bf16(to_bf16(c)).astype(np.float64)
+
+    def closed(xf):
+        return F.silu(torch.from_numpy(cf[tau] * xf[pi[tau]])).numpy() * xf[rho[tau]]
+    return to_bf16(gu), to_bf16(wd), closed
+
+
+def test_given_routing_equals_layer_on_its_own_sets():
+    rng = np.random.default_rng(61)
+    T, d, E, k, h, hs = 14, 64, 8, 3, 32, 16
+    x, wr, b, gu, wd, sgu, swd = _layer_inputs(rng, T, d, E, k, h, hs)
+    c = rng.uniform(-0.5, 0.5, E).astype(np.float32)
+    ids, w, _, y = oracle.layer(x, wr, b, k, gu, wd, sgu, swd, routed_scale=0.75, logit_bias=c)
+    w2, y2 = oracle.forward_given_routing(x, wr, ids, gu, wd, sgu, swd, routed_scale=0.75, logit_bias=c)
+    np.testing.assert_array_equal(w2, w)
+    np.testing.assert_array_equal(y2, y)
+    sub = np.array([9, 2])
+    _, y3 = oracle.forward_given_routing(x, wr, ids[sub], gu, wd, sgu, swd, routed_scale=0.75, logit_bias=c,
+                                         tokens=sub)
+    np.testing.assert_array_equal(y3, y[sub])
+
+
+def test_given_routing_one_expert_is_that_expert_plus_shared():
+    # k = 1 with a set the router would not pick: weight exactly 1, output
+    # the chosen expert plus the shared expert (library SwiGLU).
+    rng = np.random.default_rng(62)
+    T, d, E, k, h, hs = 7, 128, 6, 1, 32, 32
+    x, wr, b, gu, wd, sgu, swd = _layer_inputs(rng, T, d, E, k, h, hs)
+    own, _, _, _ = oracle.route(x, wr, b, 1)
+    ids = ((own + 3) % E).astype(np.int32)
+    w, y = oracle.forward_given_routing(x, wr, ids, gu, wd, sgu, swd)
+    assert np.all(w == 1.0)
+    for t in range(T):
+        e = int(ids[t, 0])
+        ref = _torch_swiglu(x[t:t + 1], gu[e], wd[e])[0] + _torch_swiglu(x[t:t + 1], sgu, swd)[0]
+        assert rel_l2(y[t], ref) < 1e-6
+
+
+def test_given_routing_selects_the_named_experts_closed_form():
+    # Every expert is a different permutation-matrix expert, so each output
+    # element names which expert produced it; the given sets are arbitrary
+    # (not the router's), the weights library sigmoids of those experts'
+    # logits renormalised over the set.  Using slot j's expert for slot j+1,
+    # the router's own set, biased scores or unnormalised weights all fail.
+    rng = np.random.default_rng(63)
+    T, d, E, k, h = 10, 64, 7, 3, 32
+    experts = [_perm_expert(rng, d, h, 1.0 + 0.3 * e) for e in range(E)]
+    gu = [e[0] for e in experts]
+    wd = [e[1] for e in experts]
+    x = rand_bf16(rng, (T, d))
+    wr = rand_bf16(rng, (E, d), 0.2)
+    c = rng.uniform(-1, 1, E).astype(np.float32)
+    ids = np.stack([np.sort(rng.choice(E, k, replace=False)) for _ in range(T)]).astype(np.int32)
+    w, y = oracle.forward_given_routing(x, wr, ids, gu, wd, routed_scale=1.5, logit_bias=c)
+    z = from_bf16(x).astype(np.float64) @ from_bf16(wr).astype(np.float64).T + c.astype(np.float64)
+    s = scipy.special.expit(z)
+    for t in range(T):
+        wt = s[t, ids[t]] / s[t, ids[t]].sum()
+        np.testing.assert_allclose(w[t], wt, rtol=2e-6)
+        xf = from_bf16(x[t]).astype(np.float64)
+        ref = 1.5 * sum(wt[j] * experts[e][2](xf) for j, e in enumerate(ids[t]))
+        np.testing.assert_allclose(y[t], ref, rtol=2e-6, atol=1e-7)
+
+
+def test_given_routing_rejects_invalid_sets():
+    rng = np.random.default_rng(64)
+    T, d, E, k, h, hs = 2, 64, 6, 2, 32, 0
+    x, wr, b, gu, wd, _, _ = _layer_inputs(rng, T, d, E, k, h, hs)
+    for bad in ([[1, 1], [0, 2]], [[2, 1], [0, 2]], [[0, 6], [1, 2]], [[-1, 3], [1, 2]]):
+        with pytest.raises(ValueError):
+            oracle.forward_given_routing(x, wr, np.array(bad, np.int32), gu, wd)
+
+
 # ---------------------------------------------------------------- combine --
 
 def test_combine_closed_forms():
@@ -501,6 +590,32 @@ def test_rmsnorm_matches_library_and_is_scale_invariant():
     np.testing.assert_array_equal(from_bf16(out2), from_bf16(out) * 2.0)
     rms = np.sqrt((from_bf16(out).astype(np.float64) ** 2).mean(1))
     np.testing.assert_allclose(rms, 1.0, atol=4e-3)
+
+
+def test_rmsnorm_eps_inside_the_square_root():
+    # A constant row of value v gives v / sqrt(v^2 + eps) * (1 + gamma_i).
+    # With eps of the order of v^2 the place of eps matters: outside the root,
+    # v / (|v| + eps), the result would be near 1 instead of 1/sqrt(2).
+    d = 64
+    gamma = np.linspace(-0.5, 0.5, d).astype(np.float32)
+    for v, eps in ((0.01, 1e-4), (0.25, 0.0625), (-3.0, 9.0), (0.5, 1e-6)):
+        row = to_bf16(np.full((3, d), v, np.float32))
+        vb = float(from_bf16(row[0, 0]))
+        for g in (None, gamma):
+            out = from_bf16(oracle.rmsnorm(row, gamma=g, eps=eps)).astype(np.float64)
+            gain = 1.0 if g is None else 1.0 + g.astype(np.float64)
+            expect = vb / np.sqrt(vb * vb + np.float64(np.float32(eps))) * gain
+            np.testing.assert_allclose(out, np.broadcast_to(expect, (3, d)), rtol=2 ** -8, atol=0)
+    # Random rows whose mean square is comparable to eps, against the library
+    # in float64 (at most one bf16 ulp apart: both round once).
+    rng = np.random.default_rng(45)
+    T = 16
+    v = rand_bf16(rng, (T, d), 0.02)
+    for eps in (1e-4, 4e-4, 1e-3):
+        out = oracle.rmsnorm(v, eps=eps)
+        ref = F.rms_norm(torch.from_numpy(from_bf16(v).astype(np.float64)), (d,), eps=float(np.float32(eps)))
+        diff = np.abs(out.astype(np.int32) - to_bf16(ref.numpy().astype(np.float32)).astype(np.int32))
+        assert diff.max() <= 1
 
 
 # ------------------------------------------------------------ diagnostics --
