@@ -558,12 +558,9 @@ namespace {
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
-// Tokens per wave of the selection kernel: one for small batches (latency),
-// four for large ones, so each block's expert histogram covers 16 tokens and
-// the global count atomics drop fourfold.
-// Tokens per wave of the selection: fewer waves for large batches (whole
-// router at 8,192 tokens: 73 us with 4, 76 with 2, 84 with 8; at 4,096
-// tokens 53 us with 2, 58 with 4).
+// Tokens per wave of the selection: one below 2,048 tokens (latency), two up
+// to 8,191, four from 8,192 (whole router at 8,192 tokens: 73 us with 4, 76
+// with 2, 84 with 8; at 4,096 tokens 53 us with 2, 58 with 4).
 int select_tpw(int T) { return T >= 8192 ? 4 : T >= 2048 ? 2 : 1; }
 
 size_t logits_bytes(int T, int d, int E) {

@@ -4,8 +4,12 @@ seeded generator, threaded calls of the CPU oracle, and the acceptance checks.
 Inputs for both sides come from moegen only.  The oracle never receives a
 value the GPU computed: parity of each call is checked on generator or
 oracle-made inputs, and whole-layer parity compares the GPU's output with the
-oracle's own forward pass of the same generator inputs.
+oracle's forward pass of the same generator inputs.  Where a near tie makes
+two chosen sets both correct, the oracle enumerates its acceptable sets from
+its own scores and the GPU's pick only selects which of them the output is
+compared under ("given the same routing").
 """
+import itertools
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -84,47 +88,74 @@ def pool_size():
     return moegen.threads()
 
 
-def oracle_route_all(dl: DeviceLayer, tokens=None):
-    """Oracle routing of the listed rows (all if None), in parallel chunks."""
-    c = dl.cfg
-    idx = np.arange(c.T) if tokens is None else np.asarray(tokens)
-    chunks = [a for a in np.array_split(idx, pool_size() * 2) if a.size]
+def oracle_route_rows(x_rows, wr_h, b_h, k, c_h=None):
+    """Oracle routing of token rows, in parallel chunks.  Returns (ids, w,
+    gap, beta) with beta = fl32(s + b) [n, E], the biased scores the
+    selection compares."""
+    n = x_rows.shape[0]
+    chunks = [a for a in np.array_split(np.arange(n), pool_size() * 2) if a.size]
     with ThreadPoolExecutor(pool_size()) as pool:
-        parts = list(pool.map(lambda a: oracle.route(dl.x_h[a], dl.wr_h, dl.b_h, c.k, logit_bias=dl.c_h), chunks))
+        parts = list(pool.map(lambda a: oracle.route(x_rows[a], wr_h, b_h, k, logit_bias=c_h, want_scores=True),
+                              chunks))
     ids = np.concatenate([p[0] for p in parts])
     w = np.concatenate([p[1] for p in parts])
     gap = np.concatenate([p[2] for p in parts])
-    return ids, w, gap
+    scores = np.concatenate([p[3] for p in parts])
+    beta = (scores + b_h.astype(np.float32)[None, :]).astype(np.float32)
+    return ids, w, gap, beta
 
 
-def oracle_layer_tokens(dl: DeviceLayer, tokens, ids_of_tokens):
-    """Oracle forward of the listed tokens; expert weights generated on the
-    host for exactly the experts those tokens select."""
+def oracle_route_all(dl: DeviceLayer, tokens=None, with_beta=False):
+    """Oracle routing of the listed rows (all if None): (ids, w, gap) and,
+    with_beta, the biased scores too."""
     c = dl.cfg
-    needed = sorted(set(int(e) for e in np.asarray(ids_of_tokens).ravel()))
-    ew = moegen.expert_weights_host(c, dl.layer, needed)
-    gu = [ew[e][0] if e in ew else None for e in range(c.E)]
-    wd = [ew[e][1] if e in ew else None for e in range(c.E)]
-    sgu, swd = moegen.shared_weights_host(c, dl.layer)
-    tokens = np.asarray(tokens, np.int32)
-    chunks = [a for a in np.array_split(tokens, min(len(tokens), pool_size() * 2)) if a.size]
-    with ThreadPoolExecutor(pool_size()) as pool:
-        parts = list(pool.map(lambda a: oracle.layer(dl.x_h, dl.wr_h, dl.b_h, c.k, gu, wd, sgu, swd,
-                                                     c.routed_scale, logit_bias=dl.c_h, tokens=a), chunks))
-    ids = np.concatenate([p[0] for p in parts])
-    y = np.concatenate([p[3] for p in parts])
-    return ids, y
+    idx = np.arange(c.T) if tokens is None else np.asarray(tokens)
+    ids, w, gap, beta = oracle_route_rows(dl.x_h[idx], dl.wr_h, dl.b_h, c.k, dl.c_h)
+    return (ids, w, gap, beta) if with_beta else (ids, w, gap)
 
 
-def check_routing(gpu_ids, gpu_w, gpu_gap, gpu_counts, or_ids, or_w, or_gap, E):
-    """Routing ids bit-exact except near-tie tokens (which must still pick a
-    valid set); counts exact against the GPU's own ids and against the oracle
-    where no token differs.  Returns (mask of tokens that match, near count)."""
+def acceptable_sets(beta_row, k, tol=NEAR_TIE):
+    """Every k-set of experts that a selection within `tol` of the oracle's
+    biased scores may pick: S is acceptable iff min_S beta >= max_{not S}
+    beta - tol.  Such a set holds every expert more than tol above the k-th
+    largest score and fills the rest from those within tol of it, so the
+    candidates are enumerated from that window (sets ascending)."""
+    beta_row = np.asarray(beta_row, np.float64)
+    E = beta_row.shape[0]
+    if k >= E:
+        return [tuple(range(E))]
+    bk = np.sort(beta_row)[::-1][k - 1]
+    sure = [e for e in range(E) if beta_row[e] > bk + tol]
+    window = [e for e in range(E) if abs(beta_row[e] - bk) <= tol]
+    m = k - len(sure)
+    assert 0 < m <= len(window) and len(window) <= 12, f"tie window of {len(window)} experts"
+    out = []
+    for extra in itertools.combinations(window, m):
+        S = sorted(sure + list(extra))
+        rest = np.delete(beta_row, S)
+        if beta_row[S].min() >= rest.max() - tol:
+            out.append(tuple(S))
+    return out
+
+
+def check_routing(gpu_ids, gpu_w, gpu_gap, gpu_counts, or_ids, or_w, or_gap, E, beta=None, exact=False):
+    """Routing ids bit-exact except near-tie tokens, whose GPU set must be one
+    of the oracle's acceptable sets when the oracle's biased scores are given
+    (and a valid top-k set in any case); exact=True allows no exception.
+    Counts exact against the GPU's own ids and against the oracle where no
+    token differs.  Returns (mask of tokens that match, near count)."""
     T, k = or_ids.shape
     same = np.all(gpu_ids == or_ids, axis=1)
     near = or_gap < NEAR_TIE
+    if exact:
+        bad = np.where(~same)[0]
+        assert bad.size == 0, (f"{bad.size} tokens differ from the oracle's tie-broken routing: tokens {bad[:8]}, "
+                               f"gpu {gpu_ids[bad[:2]]}, oracle {or_ids[bad[:2]]}")
     bad = ~same & ~near
     assert not bad.any(), f"{bad.sum()} tokens routed differently with gap >= {NEAR_TIE}: {np.where(bad)[0][:8]}"
+    if beta is not None:
+        for t in np.where(~same)[0]:
+            assert tuple(int(e) for e in gpu_ids[t]) in acceptable_sets(beta[t], k), f"token {t}: not a top-k set"
     # Every row: k distinct ascending ids in range.
     assert np.all((gpu_ids >= 0) & (gpu_ids < E))
     assert np.all(np.diff(gpu_ids, axis=1) > 0)
@@ -136,6 +167,54 @@ def check_routing(gpu_ids, gpu_w, gpu_gap, gpu_counts, or_ids, or_w, or_gap, E):
     finite = np.isfinite(or_gap) & same
     np.testing.assert_allclose(gpu_gap[finite], or_gap[finite], rtol=0, atol=2e-5)
     return same, int(near.sum())
+
+
+def expected_ids(gpu_ids, or_ids, beta):
+    """The chosen set the oracle's output is computed for, per token: its own
+    where the GPU agrees; where a near tie makes several sets correct, the
+    one among the oracle's acceptable sets (from its own scores) that the GPU
+    picked -- "given the same routing"."""
+    ids = or_ids.copy()
+    k = or_ids.shape[1]
+    for t in np.where(np.any(gpu_ids != or_ids, axis=1))[0]:
+        g = tuple(int(e) for e in gpu_ids[t])
+        match = [c for c in acceptable_sets(beta[t], k) if c == g]
+        assert match, f"token {t}: the GPU's set is none of the oracle's acceptable sets"
+        ids[t] = match[0]
+    return ids
+
+
+def oracle_given_routing_rows(cfg, layer, x_rows, wr_h, c_h, ids, what=""):
+    """Oracle forward of token rows under the given chosen sets ids [n,k];
+    expert weights generated on the host for exactly the experts named."""
+    needed = sorted(set(int(e) for e in np.asarray(ids).ravel()))
+    ew = moegen.expert_weights_host(cfg, layer, needed)
+    gu = [ew[e][0] if e in ew else None for e in range(cfg.E)]
+    wd = [ew[e][1] if e in ew else None for e in range(cfg.E)]
+    sgu, swd = moegen.shared_weights_host(cfg, layer)
+    n = x_rows.shape[0]
+    nchunks = min(n, max(pool_size() * 2, n // 64))
+    chunks = [a for a in np.array_split(np.arange(n), nchunks) if a.size]
+    done = [0]
+
+    def run(a):
+        r = oracle.forward_given_routing(x_rows[a], wr_h, ids[a], gu, wd, sgu, swd, cfg.routed_scale, logit_bias=c_h)
+        done[0] += a.size
+        if n >= 1024 and len(chunks) > 4 and done[0] * 8 // n != (done[0] - a.size) * 8 // n:
+            log(f"  oracle {what}: {done[0]}/{n} tokens")
+        return r
+
+    with ThreadPoolExecutor(pool_size()) as pool:
+        parts = list(pool.map(run, chunks))
+    return np.concatenate([p[1] for p in parts])
+
+
+def oracle_layer_tokens(dl: DeviceLayer, tokens, ids_of_tokens):
+    """Oracle forward of the listed tokens of dl under the given chosen sets."""
+    tokens = np.asarray(tokens, np.int64)
+    c = dl.cfg
+    return None, oracle_given_routing_rows(c, dl.layer, dl.x_h[tokens], dl.wr_h, dl.c_h,
+                                           np.asarray(ids_of_tokens, np.int32), f"config {c.index}")
 
 
 def assert_same_up_to_order(a, b, what=""):

@@ -12,8 +12,10 @@ import torch
 import moegen
 import oracle
 import sparse_moe_transformer_ffn_amd as moe
+from concurrent.futures import ThreadPoolExecutor
+
 from tests.gpu_harness import (DeviceLayer, assert_same_up_to_order, bf16_dev, bf16_host, check_output, check_routing,
-                               f32_dev, i32_dev, log, oracle_route_all, stream_ptr)
+                               f32_dev, i32_dev, log, oracle_route_all, oracle_route_rows, pool_size, stream_ptr)
 
 pytestmark = pytest.mark.gpu
 
@@ -58,8 +60,8 @@ def test_route_parity(device, idx):
     log(f"[route] config {idx}: T={cfg.T} E={cfg.E} k={cfg.k}")
     x_h, wr_h, b_h, c_h = moegen.x(cfg), moegen.router(cfg), moegen.sel_bias(cfg), moegen.logit_bias(cfg)
     g_ids, g_w, g_gap, g_cnt = run_route(cfg, x_h, wr_h, b_h, c_h)
-    o_ids, o_w, o_gap, _ = oracle.route(x_h, wr_h, b_h, cfg.k, logit_bias=c_h)
-    same, near = check_routing(g_ids, g_w, g_gap, g_cnt, o_ids, o_w, o_gap, cfg.E)
+    o_ids, o_w, o_gap, beta = oracle_route_rows(x_h, wr_h, b_h, cfg.k, c_h)
+    same, near = check_routing(g_ids, g_w, g_gap, g_cnt, o_ids, o_w, o_gap, cfg.E, beta=beta)
     log(f"  near-tie tokens: {near}, differing: {int((~same).sum())}")
 
 
@@ -93,16 +95,66 @@ def test_route_edge_cases(device, T, E, k, bias_mode):
     (1100, 192, 32, 2),      # ragged last 128-token block, three splits
     (2048, 512, 288, 8),     # the model's expert count
     (8192, 448, 32, 2),      # last reduction split shorter than the others
+    # E = 1024 (not a staged-logits shape): split-K logits, selection over 16
+    # experts per lane at two and four tokens per wave.
+    (2048, 512, 1024, 16), (8192, 512, 1024, 16), (4096, 512, 1024, 8),
 ])
 def test_route_staged_logits(device, T, d, E, k):
-    # Batches of >= 1024 tokens take the LDS-staged logits kernel.
+    # Batches of >= 1024 tokens take the LDS-staged logits kernel (E <= 288).
     cfg = moegen.custom(0, T=T, d=d, E=E, k=k, seed=3000 + T + d + E)
     log(f"[route-staged] T={T} d={d} E={E} k={k}")
     x_h, wr_h, b_h = moegen.x(cfg), moegen.router(cfg), moegen.sel_bias(cfg)
     g_ids, g_w, g_gap, g_cnt = run_route(cfg, x_h, wr_h, b_h, None)
-    o_ids, o_w, o_gap, _ = oracle.route(x_h, wr_h, b_h, k)
-    same, near = check_routing(g_ids, g_w, g_gap, g_cnt, o_ids, o_w, o_gap, E)
+    o_ids, o_w, o_gap, beta = oracle_route_rows(x_h, wr_h, b_h, k)
+    same, near = check_routing(g_ids, g_w, g_gap, g_cnt, o_ids, o_w, o_gap, E, beta=beta)
     log(f"  near-tie tokens: {near}, differing: {int((~same).sum())}")
+
+
+def _tied_router(E, d, seed, group):
+    """Router rows repeated in groups of `group` experts spread over the
+    index range (expert g, g + E/group, g + 2E/group, ...): the experts of a
+    group score identically for every token."""
+    base = moegen.normal_bf16(seed, 320, (E // group, d), 0.02)
+    return np.ascontiguousarray(np.concatenate([base] * group, axis=0))
+
+
+@pytest.mark.parametrize("T", [64, 2048, 8192])
+@pytest.mark.parametrize("E,k,d", [(288, 8, 4096), (16, 2, 256), (1024, 16, 512)])
+@pytest.mark.parametrize("mode", ["zero_x", "repeated_rows"])
+def test_route_exact_ties(device, T, E, k, d, mode):
+    # Exact ties decided by the lower-index rule, bit-exact with no near-tie
+    # exception, at one, two and four tokens per wave of the selection and in
+    # every logits kernel the sizes reach.
+    #   zero_x:        x = 0, so every score is 1/2 and the biased scores tie
+    #                  in whole groups (biases drawn from four values);
+    #   repeated_rows: router rows repeated in groups of three with one bias
+    #                  per group, so for every token the k-th and (k+1)-th
+    #                  biased scores tie inside a group (k is not a multiple
+    #                  of three) and the rule picks that group's lower indices.
+    cfg = moegen.custom(0, T=T, d=d, E=E, k=k, seed=4000 + T + E)
+    log(f"[route-ties] {mode} T={T} E={E} k={k} d={d}")
+    u = moegen.uniform(cfg.seed, 321, E)
+    if mode == "zero_x":
+        x_h = np.zeros((T, d), np.uint16)
+        wr_h = moegen.router(cfg)
+        b_h = (np.floor(u * 4) * 0.03125).astype(np.float32)
+    else:
+        x_h = moegen.x(cfg)
+        group = 3
+        E3 = E - E % group
+        wr_h = _tied_router(E3, d, cfg.seed, group)
+        b_grp = (moegen.uniform(cfg.seed, 322, E3 // group) * 0.1 - 0.05).astype(np.float32)
+        b_h = np.concatenate([b_grp] * group)
+        if E3 < E:   # leftover experts score far below the rest
+            wr_h = np.concatenate([wr_h, np.zeros((E - E3, d), np.uint16)])
+            b_h = np.concatenate([b_h, np.full(E - E3, -2.0, np.float32)])
+    g_ids, g_w, g_gap, g_cnt = run_route(cfg, x_h, wr_h, b_h, None)
+    o_ids, o_w, o_gap, _ = oracle_route_rows(x_h, wr_h, b_h, k)
+    ties = int(np.sum(o_gap == 0))
+    log(f"  tokens whose k-th and (k+1)-th biased scores tie exactly: {ties}/{T}")
+    assert ties >= (T if mode == "zero_x" else T // 2)
+    check_routing(g_ids, g_w, g_gap, g_cnt, o_ids, o_w, o_gap, E, exact=True)
+    np.testing.assert_array_equal(g_gap[o_gap == 0], 0.0)
 
 
 def run_permute(T, E, k, ids_h):
@@ -158,18 +210,12 @@ def test_expert_swiglu_parity(device, idx):
     moe.moe_expert_swiglu(s, dl.x, i32_dev(off), i32_dev(perm), dl.w_gu, dl.w_d, y_perm, ws)
     torch.cuda.synchronize()
     yp = moegen.bf16_to_f32(bf16_host(y_perm))
-    # Rows to check: every row of config 0; at config 1 three rows of each of
-    # twenty touched experts (first, middle, last of the group).
-    rows = []
-    touched = np.where(np.diff(off) > 0)[0]
-    pick = touched if idx == 0 else touched[np.linspace(0, len(touched) - 1, 20).astype(int)]
-    for e in pick:
-        lo, hi = off[e], off[e + 1]
-        rows += list(range(lo, hi)) if idx == 0 else sorted({lo, (lo + hi - 1) // 2, hi - 1})
-    experts = sorted({int(np.searchsorted(off, r, side="right") - 1) for r in rows})
-    ew = moegen.expert_weights_host(cfg, 0, experts)
-    ref = np.stack([oracle.expert(dl.x_h[perm[r] // cfg.k], *ew[int(np.searchsorted(off, r, side="right") - 1)])
-                    for r in rows])
+    # Every row (512 at the decode size), each against the oracle's expert.
+    rows = np.arange(cfg.T * cfg.k)
+    owner = np.searchsorted(off, rows, side="right") - 1
+    ew = moegen.expert_weights_host(cfg, 0, sorted(set(owner.tolist())))
+    with ThreadPoolExecutor(pool_size()) as pool:
+        ref = np.stack(list(pool.map(lambda r: oracle.expert(dl.x_h[perm[r] // cfg.k], *ew[int(owner[r])]), rows)))
     check_output(yp[rows], ref, f"y_perm rows ({len(rows)})")
     # The phase entry points give the same rows as the combined call.
     hid = torch.empty((cfg.T * cfg.k, cfg.h), dtype=torch.bfloat16, device="cuda")

@@ -3,11 +3,13 @@ configuration the benchmark uses (shared expert fused into the grouped expert
 launches),
 against the CPU oracle's forward pass of the same generator inputs.
 
-Routing is compared for every token (bit-exact except near-ties); the output
-for every token at the small sizes and for sampled tokens at the full sizes,
-on tokens whose routing matches.  The 12-layer stack is checked layer by
-layer on generated inputs (each layer's weights at T=256), and its chained
-run by properties that hold at any size plus full parity of its first layer.
+Routing is compared for every token (bit-exact except near-ties, whose GPU
+set must be one of the oracle's acceptable sets); the output for every token
+up to the prefill size and for 1,024 tokens of the skewed batch, near-tie
+tokens included, each under the chosen set the oracle computed it for.  The
+12-layer stack is checked layer by layer on generated inputs (each layer's
+weights at T=256), and its chained run layer by layer on the oracle's own
+chained inputs, plus properties that hold at any size.
 """
 import numpy as np
 import pytest
@@ -16,8 +18,10 @@ import torch
 import moegen
 import oracle
 import sparse_moe_transformer_ffn_amd as moe
+from tests._util import to_bf16
 from tests.gpu_harness import (DeviceLayer, assert_same_up_to_order, bf16_dev, bf16_host, check_output, check_routing,
-                               log, oracle_layer_tokens, oracle_route_all)
+                               expected_ids, log, oracle_given_routing_rows, oracle_layer_tokens, oracle_route_all,
+                               oracle_route_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,17 +42,20 @@ def gpu_results(buf):
 def check_layer(dl, buf, tokens):
     cfg = dl.cfg
     g_ids, g_w, g_gap, g_cnt, g_y = gpu_results(buf)
-    o_ids, o_w, o_gap = oracle_route_all(dl)
-    same, near = check_routing(g_ids, g_w, g_gap, g_cnt, o_ids, o_w, o_gap, cfg.E)
+    o_ids, o_w, o_gap, beta = oracle_route_all(dl, with_beta=True)
+    same, near = check_routing(g_ids, g_w, g_gap, g_cnt, o_ids, o_w, o_gap, cfg.E, beta=beta)
     # Permutation invariants on the GPU's own routing.
     off = buf.expert_offsets.cpu().numpy()
     perm = buf.perm_pairs.cpu().numpy()
     pos = buf.pair_pos.cpu().numpy()
     np.testing.assert_array_equal(off, np.concatenate([[0], np.cumsum(g_cnt)]))
     np.testing.assert_array_equal(pos[perm], np.arange(cfg.T * cfg.k))
-    tokens = np.array([t for t in tokens if same[t]], np.int32)
-    log(f"  near-tie tokens {near}; comparing output of {len(tokens)} tokens")
-    _, y_ref = oracle_layer_tokens(dl, tokens, o_ids[tokens])
+    tokens = np.asarray(tokens, np.int32)
+    ids = expected_ids(g_ids, o_ids, beta)
+    flipped = int(np.sum(~same[tokens]))
+    log(f"  near-tie tokens {near}, routed the other way {int((~same).sum())}; comparing output of "
+        f"{len(tokens)} tokens ({flipped} of them under their acceptable other set)")
+    _, y_ref = oracle_layer_tokens(dl, tokens, ids[tokens])
     check_output(g_y[tokens], y_ref, f"config {cfg.index} layer {dl.layer} y")
     return g_ids, same
 
@@ -174,18 +181,43 @@ def test_layer_all_tokens_one_expert(device):
     check_layer(dl, buf, np.arange(cfg.T))
 
 
-@pytest.mark.parametrize("idx,n_sample", [(2, 16), (3, 16)])
-def test_layer_full_size_sampled(device, idx, n_sample):
-    cfg = moegen.CONFIGS[idx]
-    log(f"[layer] config {idx} ({cfg.workload}), {n_sample} sampled tokens")
+@pytest.mark.timeout(600)
+def test_layer_prefill_every_token(device):
+    # The prefill batch: every one of the 8,192 tokens against the oracle
+    # (about 2.3 TFLOP of oracle work on the host's threads).
+    cfg = moegen.CONFIGS[2]
+    log(f"[layer] config 2 ({cfg.workload}), every token")
     dl = DeviceLayer(cfg)
     buf = run_layer(dl)
-    rng = np.random.default_rng(idx)
-    tokens = set(rng.choice(cfg.T, n_sample - 4, replace=False).tolist()) | {0, cfg.T - 1}
-    # Include tokens routed to the busiest expert (the skewed workload's hot spot).
-    g_ids = buf.topk_ids.cpu().numpy()
-    hot = int(np.argmax(buf.expert_counts.cpu().numpy()))
-    tokens |= set(np.where(np.any(g_ids == hot, axis=1))[0][[0, -1]].tolist())
+    check_layer(dl, buf, np.arange(cfg.T))
+    del dl, buf
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(300)
+def test_layer_skew_hot_expert_slices(device):
+    # The skewed batch: 1,024 tokens or more, among them tokens from every
+    # 64-row slice of the three busiest experts' rows (the hot expert spans 18
+    # such slices of its M-tiles), the first and last token, and random others.
+    cfg = moegen.CONFIGS[3]
+    log(f"[layer] config 3 ({cfg.workload})")
+    dl = DeviceLayer(cfg)
+    buf = run_layer(dl)
+    cnt = buf.expert_counts.cpu().numpy()
+    off = buf.expert_offsets.cpu().numpy()
+    perm = buf.perm_pairs.cpu().numpy()
+    tokens = {0, cfg.T - 1}
+    busiest = np.argsort(-cnt, kind="stable")[:3]
+    for e in busiest:
+        for lo in range(int(off[e]), int(off[e + 1]), 64):
+            hi = min(lo + 64, int(off[e + 1]))
+            rows = np.unique(np.linspace(lo, hi - 1, 8).astype(np.int64))
+            tokens |= set((perm[rows] // cfg.k).tolist())
+    log(f"  busiest experts {busiest.tolist()} with {cnt[busiest].tolist()} rows: {len(tokens)} tokens")
+    rng = np.random.default_rng(3)
+    rest = rng.permutation(np.setdiff1d(np.arange(cfg.T), sorted(tokens)))
+    tokens |= set(rest[:max(0, 1024 - len(tokens))].tolist())
+    assert len(tokens) >= 1024
     check_layer(dl, buf, np.array(sorted(tokens)))
     del dl, buf
     torch.cuda.empty_cache()
@@ -228,16 +260,23 @@ def test_stack_layers_on_generated_inputs(device):
     torch.cuda.synchronize()
     for l, (dl, b) in enumerate(zip(layers, bufs)):
         log(f"[stack] checking layer {l}")
-        check_layer(dl, b, np.arange(0, cfg.T, 64 if l else 16))
+        check_layer(dl, b, np.arange(0, cfg.T, 16))
     del layers, bufs
     torch.cuda.empty_cache()
 
 
+@pytest.mark.timeout(600)
 def test_stack_chained(device):
     # The benchmark's chained run: x_{l+1} = unit-gain zero-centred RMSNorm of
-    # y_l.  Layer 0 sees the generator's x, so it gets full parity; later
-    # layers get properties that hold at any size, and the whole chain must be
-    # bit-reproducible.
+    # y_l ([Blog] §2.2, Figure 2 caption: pre-norm blocks).  The whole chain
+    # must be bit-reproducible and keep properties that hold at any size.
+    # Parity, layer by layer: the oracle runs the chain itself on 16 tokens
+    # (every layer under its own routing, its output rounded to bf16 as the
+    # layer stores it, then its RMSNorm), and each GPU layer runs on its own
+    # chained batch with those 16 rows replaced by the oracle's chained rows;
+    # the GPU's outputs of those rows are held to the oracle's at every layer.
+    # (The GPU's own chained rows drift from the oracle's as each layer's
+    # rounding feeds the next; that drift is logged, not bounded.)
     cfg = moegen.CONFIGS[4]
     layers = [DeviceLayer(cfg, layer=l) for l in range(cfg.layers)]
     log("[stack-chain] weights resident")
@@ -253,7 +292,6 @@ def test_stack_chained(device):
         return [bf16_host(b.y).copy() for b in bufs]
 
     first = chain()
-    check_layer(layers[0], bufs[0], np.arange(cfg.T))
     for l in range(cfg.layers):
         ids = bufs[l].topk_ids.cpu().numpy()
         cnt = bufs[l].expert_counts.cpu().numpy()
@@ -270,5 +308,37 @@ def test_stack_chained(device):
     again = chain()
     for a, b in zip(first, again):
         np.testing.assert_array_equal(a, b)
-    del layers, bufs, xs
+    gpu_x = [bf16_host(x).copy() for x in xs]
+    del bufs, again
+    torch.cuda.empty_cache()
+
+    toks = np.arange(0, cfg.T, 16)
+    check_buf = layers[0].buffers()
+    ox = layers[0].x_h[toks]               # the oracle chain's rows of layer l
+    for l, dl in enumerate(layers):
+        xin = gpu_x[l].copy()
+        xin[toks] = ox
+        check_buf.forward(bf16_dev(xin), dl.wr, dl.b, dl.c, dl.w_gu, dl.w_d, dl.ws_gu, dl.ws_d, cfg.routed_scale)
+        torch.cuda.synchronize()
+        g_ids = check_buf.topk_ids.cpu().numpy()[toks]
+        g_w = check_buf.topk_weights.cpu().numpy()[toks]
+        g_gap = check_buf.topk_gap.cpu().numpy()[toks]
+        g_y = moegen.bf16_to_f32(bf16_host(check_buf.y))[toks]
+        o_ids, o_w, o_gap, beta = oracle_route_rows(ox, dl.wr_h, dl.b_h, cfg.k, dl.c_h)
+        cnt = np.bincount(g_ids.ravel(), minlength=cfg.E)
+        check_routing(g_ids, g_w, g_gap, cnt, o_ids, o_w, o_gap, cfg.E, beta=beta)
+        ids = expected_ids(g_ids, o_ids, beta)
+        y_own = oracle_given_routing_rows(cfg, l, ox, dl.wr_h, dl.c_h, o_ids, f"stack layer {l}")
+        flip = np.where(np.any(ids != o_ids, axis=1))[0]
+        y_ref = y_own.copy()
+        if flip.size:
+            y_ref[flip] = oracle_given_routing_rows(cfg, l, ox[flip], dl.wr_h, dl.c_h, ids[flip])
+        log(f"[stack-chain] layer {l}: {len(toks)} tokens on the oracle's chained rows")
+        check_output(g_y, y_ref, f"stack layer {l} (chained input)")
+        drift = moegen.bf16_to_f32(gpu_x[l][toks]).astype(np.float64) - moegen.bf16_to_f32(ox).astype(np.float64)
+        log(f"  the GPU chain's own rows vs the oracle chain's: rel_l2 "
+            f"{np.linalg.norm(drift) / np.linalg.norm(moegen.bf16_to_f32(ox)):.3e}")
+        if l + 1 < cfg.layers:
+            ox = oracle.rmsnorm(to_bf16(y_own), None, 1e-6)
+    del layers, check_buf
     torch.cuda.empty_cache()
