@@ -41,7 +41,8 @@
  * Conventions for every call:
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
  *     never allocates or frees device memory and keeps no state between
- *     calls.  bf16 tensors are passed as uint16_t bit patterns.
+ *     calls (the one exception: moe_expert_swiglu_noalloc's static scratch
+ *     array, below).  bf16 tensors are passed as uint16_t bit patterns.
  *   - Matrices are row-major [out][in] (the reduction dimension contiguous).
  *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.
  *     Calls only enqueue work: they never synchronise and never copy to the
@@ -191,6 +192,26 @@ moe_status moe_expert_swiglu(const moe_shape* shape, const uint16_t* x, const in
                              const int32_t* perm_pairs, const uint16_t* w_gate_up, const uint16_t* w_down,
                              const uint16_t* ws_gate_up, const uint16_t* ws_down, uint16_t* y_perm, float* y_shared,
                              void* workspace, size_t ws_bytes, void* stream);
+
+/* moe_expert_swiglu for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with no workspace argument.  Its
+ * scratch ([work queue | hid | hid_shared]: 256 + T*k*h*2 + T*h_s*2 bytes,
+ * each part rounded up to 256) lives in a static array of the library,
+ * 32 MiB per GPU, held from the library's first use on a GPU until the
+ * process ends (at the model's shape, h = h_s = 1280 and k = 8: up to 1,456
+ * tokens).  A shape needing more returns MOE_ERR_WORKSPACE_TOO_SMALL and
+ * enqueues nothing.  The call allocates nothing: the array's address on the
+ * current device is looked up on the first call on that device (a failure
+ * returns MOE_ERR_HIP).  Every call on one GPU shares that GPU's array:
+ * calls that may overlap on one GPU (different streams, or host threads
+ * without ordering) race and must be serialised by the caller; each call
+ * clears what it needs cleared.  Other arguments, outputs and errors as
+ * moe_expert_swiglu.                                                       */
+moe_status moe_expert_swiglu_noalloc(const moe_shape* shape, const uint16_t* x, const int32_t* expert_offsets,
+                                     const int32_t* perm_pairs, const uint16_t* w_gate_up, const uint16_t* w_down,
+                                     const uint16_t* ws_gate_up, const uint16_t* ws_down, uint16_t* y_perm,
+                                     float* y_shared, void* stream);
 
 /* moe_expert_swiglu with activation clipping ([Blog] §4.1.3 and Figure 4:
  * clipping the activations, unlike the weights, keeps the largest expert

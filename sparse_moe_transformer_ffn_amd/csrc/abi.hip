@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "kernels.h"
@@ -195,25 +196,37 @@ moe_status moe_expert_down(const moe_shape* shape, const int32_t* expert_offsets
                                      (hipStream_t)stream));
 }
 
-moe_status moe_expert_swiglu(const moe_shape* shape, const uint16_t* x, const int32_t* expert_offsets,
-                             const int32_t* perm_pairs, const uint16_t* w_gate_up, const uint16_t* w_down,
-                             const uint16_t* ws_gate_up, const uint16_t* ws_down, uint16_t* y_perm, float* y_shared,
-                             void* workspace, size_t ws_bytes, void* stream) {
+// Checks of moe_expert_swiglu's arguments other than the workspace.
+static moe_status expert_swiglu_args(const moe_shape* shape, const uint16_t* x, const int32_t* expert_offsets,
+                                     const int32_t* perm_pairs, const uint16_t* w_gate_up, const uint16_t* w_down,
+                                     const uint16_t* ws_gate_up, const uint16_t* ws_down, const uint16_t* y_perm,
+                                     const float* y_shared, bool* shared) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
   if (!x || !expert_offsets || !perm_pairs || !w_gate_up || !w_down || !y_perm) return MOE_ERR_INVALID_ARGUMENT;
-  bool shared = false;
-  if ((st = shared_set(shape, {ws_gate_up, ws_down, y_shared}, &shared)) != MOE_OK) return st;
+  if ((st = shared_set(shape, {ws_gate_up, ws_down, y_shared}, shared)) != MOE_OK) return st;
   if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(y_perm) ||
       !aligned4(expert_offsets) || !aligned4(perm_pairs) ||
-      (shared && (!aligned16(ws_gate_up) || !aligned16(ws_down) || !aligned16(y_shared))))
+      (*shared && (!aligned16(ws_gate_up) || !aligned16(ws_down) || !aligned16(y_shared))))
     return MOE_ERR_MISALIGNED;
-  if ((st = check_workspace(shape, workspace, ws_bytes)) != MOE_OK) return st;
-  // Workspace: [work queue | hid | hid_shared].
+  return MOE_OK;
+}
+
+// Scratch of the grouped expert calls, [work queue | hid | hid_shared]:
+// its size, and the launches of both phases on it.
+static size_t expert_scratch_bytes(const moe_shape* s, bool shared) {
+  return moe::kQueueBytes + moe::expert_hid_bytes(s->num_tokens, s->top_k, s->d_expert) +
+         (shared ? moe::shared_hid_bytes(s->num_tokens, s->d_shared) : 0);
+}
+
+static moe_status expert_swiglu_on(const moe_shape* shape, const uint16_t* x, const int32_t* expert_offsets,
+                                   const int32_t* perm_pairs, const uint16_t* w_gate_up, const uint16_t* w_down,
+                                   const uint16_t* ws_gate_up, const uint16_t* ws_down, uint16_t* y_perm,
+                                   float* y_shared, bool shared, void* scratch, void* stream) {
   const int T = shape->num_tokens, d = shape->d_model, E = shape->num_experts, k = shape->top_k;
   const int h = shape->d_expert, hs = shape->d_shared;
-  int32_t* queue = static_cast<int32_t*>(workspace);
-  uint16_t* hid = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + moe::kQueueBytes);
+  int32_t* queue = static_cast<int32_t*>(scratch);
+  uint16_t* hid = reinterpret_cast<uint16_t*>(static_cast<char*>(scratch) + moe::kQueueBytes);
   uint16_t* hid_shared = shared ? hid + moe::expert_hid_bytes(T, k, h) / 2 : nullptr;
   hipError_t err = moe::launch_gate_up(T, d, E, k, h, hs, x, expert_offsets, perm_pairs, w_gate_up,
                                        shared ? ws_gate_up : nullptr, hid, hid_shared, queue, (hipStream_t)stream);
@@ -221,6 +234,73 @@ moe_status moe_expert_swiglu(const moe_shape* shape, const uint16_t* x, const in
     err = moe::launch_down(T, d, E, k, h, hs, expert_offsets, hid, hid_shared, w_down, shared ? ws_down : nullptr,
                            y_perm, shared ? y_shared : nullptr, queue, (hipStream_t)stream);
   return hip_status(err);
+}
+
+moe_status moe_expert_swiglu(const moe_shape* shape, const uint16_t* x, const int32_t* expert_offsets,
+                             const int32_t* perm_pairs, const uint16_t* w_gate_up, const uint16_t* w_down,
+                             const uint16_t* ws_gate_up, const uint16_t* ws_down, uint16_t* y_perm, float* y_shared,
+                             void* workspace, size_t ws_bytes, void* stream) {
+  bool shared = false;
+  moe_status st = expert_swiglu_args(shape, x, expert_offsets, perm_pairs, w_gate_up, w_down, ws_gate_up, ws_down,
+                                     y_perm, y_shared, &shared);
+  if (st != MOE_OK) return st;
+  if ((st = check_workspace(shape, workspace, ws_bytes)) != MOE_OK) return st;
+  return expert_swiglu_on(shape, x, expert_offsets, perm_pairs, w_gate_up, w_down, ws_gate_up, ws_down, y_perm,
+                          y_shared, shared, workspace, stream);
+}
+
+}  // extern "C"
+
+// Scratch of moe_expert_swiglu_noalloc: one array per GPU, in the library's
+// own device memory, held until the process ends.  In host code `scratch` is
+// only a handle of the symbol, not a device address: the address each device
+// holds its copy at is looked up once per device (device_scratch) and only
+// that address is handed to kernels.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_addr[kMaxDevices];
+
+// This device's copy of `scratch` (the current device), looked up on the
+// first call on that device with it current.
+hipError_t device_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    scratch_addr[dev] = p;
+  }
+  *out = scratch_addr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_expert_swiglu_noalloc(const moe_shape* shape, const uint16_t* x, const int32_t* expert_offsets,
+                                     const int32_t* perm_pairs, const uint16_t* w_gate_up, const uint16_t* w_down,
+                                     const uint16_t* ws_gate_up, const uint16_t* ws_down, uint16_t* y_perm,
+                                     float* y_shared, void* stream) {
+  bool shared = false;
+  const moe_status st = expert_swiglu_args(shape, x, expert_offsets, perm_pairs, w_gate_up, w_down, ws_gate_up,
+                                           ws_down, y_perm, y_shared, &shared);
+  if (st != MOE_OK) return st;
+  if (expert_scratch_bytes(shape, shared) > kNoAllocScratchBytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  if (device_scratch(&ws) != hipSuccess) return MOE_ERR_HIP;
+  return expert_swiglu_on(shape, x, expert_offsets, perm_pairs, w_gate_up, w_down, ws_gate_up, ws_down, y_perm,
+                          y_shared, shared, ws, stream);
 }
 
 moe_status moe_expert_swiglu_clamped(const moe_shape* shape, const uint16_t* x, const int32_t* expert_offsets,

@@ -298,3 +298,26 @@ def test_expert_clamped_validation():
     assert call(ysh=A) == INVALID          # shared pointers come as a set
     assert call(x=MIS) == MISALIGNED
     assert call(nbytes=nb - 256) == WS_SMALL
+
+
+def test_expert_noalloc_validation():
+    # moe_expert_swiglu_noalloc(shape, x, off, perm, w_gu, w_d, ws_gu, ws_d, y_perm, y_shared, stream): the
+    # checks of moe_expert_swiglu, then the shape against its 32 MiB static
+    # scratch, all before any HIP call.
+    L = moe.lib()
+
+    def call(s, x=A, wd=A, sh=(None, None, None), y=A):
+        return L.moe_expert_swiglu_noalloc(ctypes.byref(s), x, A, A, A, wd, sh[0], sh[1], y, sh[2], None)
+
+    s = shape(1)
+    assert call(s, x=None) == INVALID
+    assert call(s, wd=None) == INVALID
+    assert call(s, sh=(A, None, None)) == INVALID          # shared pointers come as a set
+    assert call(s, x=MIS) == MISALIGNED
+    assert call(s, sh=(A, A, A + 8)) == MISALIGNED
+    assert call(shape(1, top_k=0)) == UNSUPPORTED
+    # Scratch need: 256 + T*k*h*2 (+ T*h_s*2 with the shared expert), each
+    # part rounded up to 256 bytes, against 32 MiB.
+    assert call(shape(1, num_tokens=2000)) == WS_SMALL
+    assert call(shape(1, num_tokens=1500), sh=(A, A, A)) == WS_SMALL
+    assert call(shape(1, num_tokens=100000)) == WS_SMALL
