@@ -15,7 +15,8 @@ after it and reported in the "prefill" object; the skewed-load batch
 "stack" objects.  Prints one JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill]
-                       [--no-cpu-baseline] [--cpu-sample N]
+                       [--no-cpu-baseline] [--cpu-sample N] [--cpu-sample-large N]
+                       [--cpu-sample-stack N]
        python bench.py --write-traffic PMC_DIR   (HBM bytes from counter runs)
 """
 import argparse
@@ -98,14 +99,20 @@ def write_traffic(pmc_dir):
           python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-prefill --no-extras
       rocprofv3 --pmc FETCH_SIZE -f csv -d <pmc_dir>/pre_fetch -o pre_fetch -- \
           python3 bench.py --steps 2 --warmup 1 --only-prefill
-      (and the same three with WRITE_SIZE into *_write)
+      rocprofv3 --pmc FETCH_SIZE -f csv -d <pmc_dir>/skw_fetch -o skw_fetch -- \
+          python3 bench.py --steps 2 --warmup 1 --only-skew
+      (and the same four with WRITE_SIZE into *_write; a workload whose runs
+      are missing is skipped)
     """
     copy_fetch, _ = _counter_means(pmc_dir, "copy_fetch", "FETCH_SIZE", (COPY_KERNEL,))
     copy_write, _ = _counter_means(pmc_dir, "copy_write", "WRITE_SIZE", (COPY_KERNEL,))
     f_fetch = COPY_BYTES / (copy_fetch * 1024)
     f_write = COPY_BYTES / (copy_write * 1024)
     src = kernel_source_hash()
-    for workload, run in (("decode", "dec"), ("prefill", "pre")):
+    for workload, run in (("decode", "dec"), ("prefill", "pre"), ("skew", "skw")):
+        if not os.path.exists(os.path.join(pmc_dir, f"{run}_fetch")):
+            print(f"{workload}: no {run}_fetch run in {pmc_dir}, skipped")
+            continue
         for kernel, patterns in PHASE_KERNELS.items():
             fetch, n = _counter_means(pmc_dir, f"{run}_fetch", "FETCH_SIZE", patterns)
             write, _ = _counter_means(pmc_dir, f"{run}_write", "WRITE_SIZE", patterns)
@@ -306,26 +313,36 @@ def time_workload(cfg, steps, warmup, dev, extras=True):
     return wl, res
 
 
-def time_skew(steps, warmup, dev):
+def time_skew(steps, warmup, dev, cpu_sample=0):
     """The skewed-load workload (T = 4096, Zipf(1.1) logit offset: the
     busiest expert gets about ten times the mean load) timed like the others;
-    a supplementary figure, not the bench line."""
+    a supplementary figure, not the bench line.  Its dominant kernel (the
+    grouped gate/up launch) is HBM-bound: the roofline objects give its
+    algorithmic bytes and flops over its time."""
     import moegen
     cfg = moegen.CONFIGS[3]
     wl, r = time_workload(cfg, steps, warmup, dev, extras=False)
-    del wl
     alg = r["alg"]
     sec = r["ms_per_step"] * 1e-3
-    return {"workload": cfg.workload, "tok_s": cfg.T / sec, "ms_per_step": r["ms_per_step"],
-            "instrumented": instrumented(r), "steps": steps,
-            "step_hbm_gbs": alg["step_bytes"] / sec / 1e9, "step_hbm_frac": alg["step_bytes"] / sec / 1e9 / HBM_PEAK_GBS,
-            "step_tflops": alg["step_flops"] / sec / 1e12,
-            "step_mfma_frac": alg["step_flops"] / sec / 1e12 / BF16_PEAK_TFLOPS,
-            "kernels": {"gate_up_ms": r["gate_up_ms"], "down_ms": r["down_ms"]},
-            "touched_experts": r["n_touched"], "max_load": r["max_load"], "idle_experts": r["idle_experts"]}
+    gu_sec = r["gate_up_ms"] * 1e-3
+    out = {"workload": cfg.workload, "tok_s": cfg.T / sec, "ms_per_step": r["ms_per_step"],
+           "instrumented": instrumented(r), "steps": steps,
+           "step_hbm_gbs": alg["step_bytes"] / sec / 1e9, "step_hbm_frac": alg["step_bytes"] / sec / 1e9 / HBM_PEAK_GBS,
+           "step_tflops": alg["step_flops"] / sec / 1e12,
+           "step_mfma_frac": alg["step_flops"] / sec / 1e12 / BF16_PEAK_TFLOPS,
+           "roofline": roofline("hbm", alg["gate_up_bytes"] / gu_sec / 1e9, load_traffic("skew", "gate_up")),
+           "roofline_mfma": roofline("mfma", alg["gate_up_flops"] / gu_sec / 1e12, None),
+           "kernels": {"gate_up_ms": r["gate_up_ms"], "down_ms": r["down_ms"],
+                       "gate_up_gbs": alg["gate_up_bytes"] / gu_sec / 1e9,
+                       "down_gbs": alg["down_bytes"] / (r["down_ms"] * 1e-3) / 1e9},
+           "touched_experts": r["n_touched"], "max_load": r["max_load"], "idle_experts": r["idle_experts"]}
+    if cpu_sample:
+        out["cpu_baseline"] = cpu_baseline(wl, cpu_sample)
+    del wl
+    return out
 
 
-def time_stack(steps, warmup, dev):
+def time_stack(steps, warmup, dev, cpu_sample=0):
     """The 12-layer stack (T = 256, distinct weights per layer, 109 GB
     resident): layer l + 1 takes the unit-gain RMSNorm of layer l's output.
     One pass = 12 layer steps and 11 normalisations; supplementary figure."""
@@ -356,10 +373,14 @@ def time_stack(steps, warmup, dev):
     touched = [int((wl.buf.expert_counts.cpu().numpy() > 0).sum()) for wl in layers]
     nbytes = sum(algorithmic(cfg, n)["step_bytes"] for n in touched)
     ms = float(np.median(per))
+    x0 = layers[0].x_h
     del layers
-    return {"workload": cfg.workload, "layers": cfg.layers, "tok_s": cfg.T / (ms * 1e-3), "ms_per_pass_median": ms,
-            "ms_per_pass_min": float(per.min()), "passes": steps, "hbm_gbs": nbytes / (ms * 1e-3) / 1e9,
-            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "touched_experts_per_layer": touched}
+    out = {"workload": cfg.workload, "layers": cfg.layers, "tok_s": cfg.T / (ms * 1e-3), "ms_per_pass_median": ms,
+           "ms_per_pass_min": float(per.min()), "passes": steps, "hbm_gbs": nbytes / (ms * 1e-3) / 1e9,
+           "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "touched_experts_per_layer": touched}
+    if cpu_sample:
+        out["cpu_baseline"] = cpu_baseline_stack(cfg, x0, cpu_sample)
+    return out
 
 
 def mean_ms(call, n, stream):
@@ -471,6 +492,53 @@ def cpu_baseline(wl, n_sample):
                       f"{dt:.1f} s on one host thread pinned to one core"}
 
 
+def _to_bf16(a):
+    """float32 -> bf16 bit patterns, round to nearest even (the layer output
+    as the stack stores it)."""
+    import numpy as np
+    b = np.ascontiguousarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def cpu_baseline_stack(cfg, x0, n_sample):
+    """The CPU oracle on the 12-layer stack: n_sample tokens carried through
+    all layers (each layer's output rounded to bf16 and normalised, as the
+    chained run does), single-threaded; weight generation is not timed."""
+    import numpy as np
+    import moegen
+    import oracle
+    tokens = np.linspace(0, cfg.T - 1, n_sample).astype(np.int64)
+    x = np.ascontiguousarray(x0[tokens])
+    saved = os.sched_getaffinity(0)
+    core = min(saved)
+    dt = 0.0
+    for l in range(cfg.layers):
+        wr, b = moegen.router(cfg, l), moegen.sel_bias(cfg, l)
+        ids, _, _, _ = oracle.route(x, wr, b, cfg.k)
+        ew = moegen.expert_weights_host(cfg, l, sorted(set(ids.ravel().tolist())))
+        gu = [ew[e][0] if e in ew else None for e in range(cfg.E)]
+        wd = [ew[e][1] if e in ew else None for e in range(cfg.E)]
+        sgu, swd = moegen.shared_weights_host(cfg, l)
+        os.sched_setaffinity(0, {core})
+        try:
+            t = time.perf_counter()
+            _, _, _, y = oracle.layer(x, wr, b, cfg.k, gu, wd, sgu, swd, cfg.routed_scale)
+            if l + 1 < cfg.layers:
+                x = oracle.rmsnorm(_to_bf16(y), None, 1e-6)
+            dt += time.perf_counter() - t
+        finally:
+            os.sched_setaffinity(0, saved)
+    n = n_sample * cfg.layers
+    flops_per_token = 2 * cfg.d * cfg.E + 2 * 3 * cfg.d * (cfg.k * cfg.h + cfg.hs)
+    return {"value": n_sample / dt, "unit": "tok/s (through all 12 layers)", "cores": 1, "kind": "oracle",
+            "gflops": n * flops_per_token / dt / 1e9,
+            "host": {"cpu": host_cpu_model(), "online_cores": os.cpu_count(), "affinity_cores": len(saved),
+                     "pinned_to": core},
+            "sample": f"{n_sample} of the {cfg.T} tokens of the {cfg.name} workload carried through all "
+                      f"{cfg.layers} layers ({n} token-layers: route, {cfg.k} routed + 1 shared SwiGLU expert, "
+                      f"combine, RMSNorm between layers); {dt:.1f} s on one host thread pinned to one core"}
+
+
 def host_cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -503,6 +571,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--only-prefill", action="store_true", help="time only the prefill workload (profiling)")
+    ap.add_argument("--only-skew", action="store_true", help="time only the skewed-load workload (profiling)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 1 GiB device copy (the known-size reference for HBM byte counters)")
     ap.add_argument("--prefill-steps", type=int, default=10)
@@ -513,7 +582,11 @@ def main():
                          "(profiling runs)")
     ap.add_argument("--no-supplementary", action="store_true",
                     help="skip the skewed-load workload and the 12-layer stack")
-    ap.add_argument("--cpu-sample", type=int, default=64)
+    ap.add_argument("--cpu-sample", type=int, default=64, help="tokens of the decode batch the oracle runs")
+    ap.add_argument("--cpu-sample-large", type=int, default=32,
+                    help="tokens of the prefill and skewed batches the oracle runs")
+    ap.add_argument("--cpu-sample-stack", type=int, default=2,
+                    help="tokens the oracle carries through the 12-layer stack")
     ap.add_argument("--write-traffic", metavar="PMC_DIR",
                     help="no GPU work: write profiles/traffic_*.json from rocprofv3 counter runs in PMC_DIR")
     args = ap.parse_args()
@@ -538,8 +611,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": src.numel() * 2, "copies": 3}), flush=True)
         return
-    if args.only_prefill:
-        pcfg = moegen.CONFIGS[2]
+    if args.only_prefill or args.only_skew:
+        pcfg = moegen.CONFIGS[2 if args.only_prefill else 3]
         _, p = time_workload(pcfg, args.steps, args.warmup, dev, extras=False)
         print(json.dumps({"workload": pcfg.workload, "ms_per_step": p["ms_per_step"],
                           "gate_up_ms": p["gate_up_ms"], "down_ms": p["down_ms"]}), flush=True)
@@ -612,12 +685,15 @@ def main():
             out["prefill"].update(diagnostics=p["diagnostics"], prenorm_block=p["prenorm_block"],
                                   graph_replay=p["graph_replay"],
                                   ep_share=time_share(pwl, args.prefill_steps))
+        if not args.no_cpu_baseline:
+            out["prefill"]["cpu_baseline"] = cpu_baseline(pwl, args.cpu_sample_large)
         del pwl
     if extras and not args.no_supplementary:
         torch.cuda.empty_cache()
-        out["skew"] = time_skew(args.prefill_steps, args.warmup, dev)
+        no_cpu = args.no_cpu_baseline
+        out["skew"] = time_skew(args.prefill_steps, args.warmup, dev, 0 if no_cpu else args.cpu_sample_large)
         torch.cuda.empty_cache()
-        out["stack"] = time_stack(args.prefill_steps, args.warmup, dev)
+        out["stack"] = time_stack(args.prefill_steps, args.warmup, dev, 0 if no_cpu else args.cpu_sample_stack)
         torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
 
