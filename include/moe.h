@@ -312,7 +312,9 @@ moe_status moe_combine_diag(const moe_shape* shape, const uint16_t* y_perm, cons
 
 /* Dense SwiGLU FFN ([Digest] architecture table: dense FFN hidden size
  * 11,264; [Blog] §2.2, Figure 2 caption: the first three blocks and the MTP
- * heads use a dense FFN), run by the grouped expert kernels as one group of
+ * heads use a dense FFN): up to 64 tokens with a hidden size of at least
+ * 16 units per CU, by kernels in which each CU streams a fixed share of both
+ * weight matrices; otherwise by the grouped expert kernels as one group of
  * all T tokens:
  *   y[t,:] = W_d (SiLU(W_g x[t]) * (W_u x[t]))
  * In:  x [T, d] bf16; w_gate_up [2H, d] bf16 (rows 0..H-1 gate, H..2H-1

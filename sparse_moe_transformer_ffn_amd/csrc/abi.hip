@@ -465,6 +465,8 @@ moe_status moe_dense_swiglu(int32_t num_tokens, int32_t d_model, int32_t d_hidde
                        ? reinterpret_cast<float*>(static_cast<char*>(workspace) + moe::kQueueBytes +
                                                   moe::shared_hid_bytes(T, H))
                        : nullptr;
+  if (moe::dense_ffn_fits(T, d, H))
+    return hip_status(moe::launch_dense_ffn(T, d, H, x, w_gate_up, w_down, hid, partial, y, 0.f, (hipStream_t)stream));
   hipError_t err = moe::launch_gate_up(T, d, 1, 1, 128, H, x, nullptr, nullptr, nullptr, w_gate_up, nullptr, hid,
                                        queue, (hipStream_t)stream, 0, 0.f, partial);
   if (err == hipSuccess)

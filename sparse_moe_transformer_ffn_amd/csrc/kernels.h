@@ -84,6 +84,15 @@ hipError_t launch_down_tiled(int T, int d, int E, int k, int h, int hs, const in
                              uint16_t* y_perm, float* y_shared, int32_t* queue, hipStream_t stream,
                              float* partial = nullptr);
 size_t tiled_split_bytes(int T, int d, int hs);
+// The dense SwiGLU FFN at up to kDenseMaxTokens tokens (each CU streams a
+// fixed share of both weight matrices once).  dense_ffn_fits says whether a
+// shape suits it.  hid: T x H bf16; partial: kDenseDownSplits x T x d floats
+// (split_partial_bytes covers it).
+constexpr int kDenseMaxTokens = 64;
+constexpr int kDenseDownSplits = kDownSplits;
+bool dense_ffn_fits(int T, int d, int H);
+hipError_t launch_dense_ffn(int T, int d, int H, const uint16_t* x, const uint16_t* w_gu, const uint16_t* w_d,
+                            uint16_t* hid, float* partial, float* y, float clamp, hipStream_t stream);
 size_t expert_hid_bytes(int T, int k, int h);
 size_t shared_hid_bytes(int T, int hs);
 

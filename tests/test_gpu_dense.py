@@ -4,7 +4,9 @@ inputs.  The weights are the generator's shared-expert tensors of a workload
 whose shared hidden size is the dense one; the oracle gets the host copy.
 
 Both launch regimes are covered: up to 64 tokens the streaming kernels (one
-M-tile of 16, 32 or 64 rows, the down reduction split over items); above
+M-tile of 16, 32 or 64 rows, the down reduction split over items; with a
+hidden size of at least 16 units per CU, the kernels in which each CU owns a
+fixed share of the weights); above
 64 the LDS-tiled ones, which up to 256 tokens (one M-tile) split each weight
 tile's reduction over several items when the reduction is long enough
 (partial sums added afterwards in split order).  Bar: the layer's output tolerance
@@ -57,6 +59,12 @@ def oracle_rows(cfg, x_h, rows):
     (64, 4096, DENSE_HIDDEN),                             # streaming, one 64-row M-tile, down split 4 ways
     (16, 4096, DENSE_HIDDEN), (32, 4096, DENSE_HIDDEN),   # streaming at the model's size: 16- and 32-row
     (48, 4096, DENSE_HIDDEN),                             # M-tiles, and one 64-row M-tile
+    (8, 4096, DENSE_HIDDEN),
+    # Up to 64 tokens with a hidden size of at least 16 units per CU, each CU
+    # owns a fixed range of hidden units (gate/up) and of output columns over
+    # a quarter of the reduction (down): ragged unit ranges (the last block
+    # short), ragged reduction ranges, and waves left without K blocks.
+    (64, 1024, 4352), (33, 512, 6208), (1, 256, 4096), (20, 768, 8256),
 ])
 def test_dense_parity(device, T, d, H):
     cfg = moegen.custom(1, T=T, d=d, hs=H, seed=700 + T + H)
