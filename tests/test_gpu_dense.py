@@ -59,7 +59,7 @@ def oracle_rows(cfg, x_h, rows):
     (64, 4096, DENSE_HIDDEN),                             # streaming, one 64-row M-tile, down split 4 ways
     (16, 4096, DENSE_HIDDEN), (32, 4096, DENSE_HIDDEN),   # streaming at the model's size: 16- and 32-row
     (48, 4096, DENSE_HIDDEN),                             # M-tiles, and one 64-row M-tile
-    (8, 4096, DENSE_HIDDEN),
+    (1, 4096, DENSE_HIDDEN), (8, 4096, DENSE_HIDDEN), (17, 4096, DENSE_HIDDEN), (63, 4096, DENSE_HIDDEN),
     # Up to 64 tokens with a hidden size of at least 16 units per CU, each CU
     # owns a fixed range of hidden units (gate/up) and of output columns over
     # a quarter of the reduction (down): ragged unit ranges (the last block
