@@ -36,7 +36,9 @@
 // gfx950 direct-to-LDS load (global_load_lds_dwordx4: lane l of a wave writes
 // its 16 bytes at LDS base + 16*l), whole 128-byte rows per 64-wide chunk
 // (half rows cost a third of the L2 throughput), through two stages of
-// A 256x64 + B 256x64 bf16 = 64 KiB each, with no register staging.  Segment s
+// A 256x64 + B 256x64 bf16 = 64 KiB each, with no register staging (items of
+// one 64-row slice: a ring of three 40 KiB slots instead, see
+// run_item_small).  Segment s
 // of row r is stored at slot s ^ ((r >> 1) & 7), so a wave's 16-byte reads of
 // one segment of 16 consecutive rows cover all LDS banks.  The direct loads
 // choose their source segment to produce that layout.
@@ -119,7 +121,7 @@ __device__ __forceinline__ constexpr int b_row0(int wn, int ns) {
 // shrinks with the item.
 struct Pipe {
   const uint16_t* src[kLoads];  // per-thread source of each direct load (chunk 0)
-  int lds_off[kLoads];          // wave-uniform LDS element offset inside a stage
+  int lds_off[kLoads];          // wave-uniform LDS element offset inside its A slice or B tile
 };
 
 template <int NA>
@@ -127,15 +129,33 @@ __device__ __forceinline__ constexpr bool load_used(int q) {
   return q >= kLoadsA || q < NA;
 }
 
-template <int NA>
-__device__ __forceinline__ void issue_chunk(const Pipe& p, uint16_t* stage, int c) {
-#pragma unroll
-  for (int q = 0; q < kLoads; ++q)
-    if (load_used<NA>(q)) __builtin_amdgcn_global_load_lds(p.src[q] + c * kChunk, stage + p.lds_off[q], 16, 0, kPolicy);
+// One stage of operands in LDS: A slice q (64 token rows x 64) at
+// a + q * kSlice, this wave's A slice (the rows it multiplies) at a_read, the
+// 256 x 64 B tile at b.  A and B of every stage are separate arrays (see the
+// kernel), and a_read is computed from a alone, so the compiler, which waits
+// for a direct load before any LDS read that may alias it, tells the stages
+// apart.
+constexpr int kSlice = kStageA / kLoadsA;  // elements of one 64-row A slice
+
+struct StageRef {
+  uint16_t* a;
+  const uint16_t* a_read;
+  uint16_t* b;
+};
+
+__device__ __forceinline__ uint16_t* load_dst(const StageRef& st, const Pipe& p, int q) {
+  return (q < kLoadsA ? st.a + q * kSlice : st.b) + p.lds_off[q];
 }
 
-// LDS element offsets of this lane's fragment reads, per K step s: A row
-// 64 wm + l32 (M-subtile 0; subtile 1 is 32 rows further) and B row
+template <int NA>
+__device__ __forceinline__ void issue_chunk(const Pipe& p, const StageRef& st, int c) {
+#pragma unroll
+  for (int q = 0; q < kLoads; ++q)
+    if (load_used<NA>(q)) __builtin_amdgcn_global_load_lds(p.src[q] + c * kChunk, load_dst(st, p, q), 16, 0, kPolicy);
+}
+
+// LDS element offsets of this lane's fragment reads, per K step s: row l32
+// of the wave's A slice (M-subtile 0; subtile 1 is 32 rows further) and B row
 // b_row0(wn, 0) + l32 (N-subtile 0; subtile ns at b_row0(wn, ns) -
 // b_row0(wn, 0) further), each at the step's swizzled slot.  All rows a lane
 // reads have swz(row) = swz(l32).
@@ -150,10 +170,10 @@ struct Frags {
 };
 
 template <int PHASE>
-__device__ __forceinline__ u32x4 read_frag(const uint16_t* stage, const ReadMap& m, int s, int q) {
-  const int off = q < 2 ? m.a[s] + q * 32 * kChunk
-                        : m.b[s] + (b_row0<PHASE>(0, q - 2) - b_row0<PHASE>(0, 0)) * kChunk;
-  return *reinterpret_cast<const u32x4*>(&stage[off]);
+__device__ __forceinline__ u32x4 read_frag(const StageRef& st, const ReadMap& m, int s, int q) {
+  const uint16_t* ptr = q < 2 ? st.a_read + m.a[s] + q * 32 * kChunk
+                              : st.b + m.b[s] + (b_row0<PHASE>(0, q - 2) - b_row0<PHASE>(0, 0)) * kChunk;
+  return *reinterpret_cast<const u32x4*>(ptr);
 }
 
 // One K step: the eight MFMAs of `cur` (if MUL), after MFMA i the LDS read i
@@ -161,8 +181,8 @@ __device__ __forceinline__ u32x4 read_frag(const uint16_t* stage, const ReadMap&
 // READ) and, with LOADS and `issue` (uniform), direct load i of chunk `cload`
 // into `other`.  The order is pinned (sched_barrier).
 template <int PHASE, int NA, bool MUL, bool READ, bool LOADS>
-__device__ __forceinline__ void mma_step(const Frags& cur, Frags& nxt, const uint16_t* stage, const ReadMap& m,
-                                         int s, const Pipe& p, uint16_t* other, int cload, bool issue,
+__device__ __forceinline__ void mma_step(const Frags& cur, Frags& nxt, const StageRef& stage, const ReadMap& m,
+                                         int s, const Pipe& p, const StageRef& other, int cload, bool issue,
                                          f32x16 (&acc)[2][4]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -175,7 +195,7 @@ __device__ __forceinline__ void mma_step(const Frags& cur, Frags& nxt, const uin
       }
     }
     if (LOADS && issue && load_used<NA>(i)) {
-      __builtin_amdgcn_global_load_lds(p.src[i] + cload * kChunk, other + p.lds_off[i], 16, 0, kPolicy);
+      __builtin_amdgcn_global_load_lds(p.src[i] + cload * kChunk, load_dst(other, p, i), 16, 0, kPolicy);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -193,7 +213,7 @@ __device__ __forceinline__ void mma_step(const Frags& cur, Frags& nxt, const uin
 // every chunk issues and waits the same way.  The final reads fetch unused
 // data.  Waves without rows in the item (MUL = false) only load and wait.
 template <int PHASE, int NA, bool MUL>
-__device__ __forceinline__ void pipe_chunk(const Pipe& p, const uint16_t* cur, uint16_t* other, int c, int nch,
+__device__ __forceinline__ void pipe_chunk(const Pipe& p, const StageRef& cur, const StageRef& other, int c, int nch,
                                            const ReadMap& m, Frags (&fr)[2], f32x16 (&acc)[2][4]) {
   const int cl = min(c + 1, nch - 1);
   const bool issue = PHASE == kGateUp || c + 1 < nch;
@@ -212,7 +232,7 @@ __device__ __forceinline__ void pipe_chunk(const Pipe& p, const uint16_t* cur, u
 // The K loop of one item over the two stages (unrolled by two).  Chunk 0 was
 // issued into stage0 before the previous item's epilogue.
 template <int PHASE, int NA, bool MUL>
-__device__ __forceinline__ void run_item(const Pipe& p, uint16_t* stage0, uint16_t* stage1, int nch,
+__device__ __forceinline__ void run_item(const Pipe& p, const StageRef& stage0, const StageRef& stage1, int nch,
                                          const ReadMap& m, f32x16 (&acc)[2][4]) {
   __builtin_amdgcn_s_waitcnt(kWaitAll);
   __builtin_amdgcn_s_barrier();
@@ -227,6 +247,58 @@ __device__ __forceinline__ void run_item(const Pipe& p, uint16_t* stage0, uint16
     pipe_chunk<PHASE, NA, MUL>(p, stage1, stage0, c + 1, nch, m, fr, acc);
   }
   if (c < nch) pipe_chunk<PHASE, NA, MUL>(p, stage0, stage1, c, nch, m, fr, acc);
+}
+
+// Items of one 64-row slice move 40 KiB per chunk, so three chunks fit in
+// the operand memory: the ring of slots S0, S1, S2 holds chunk c in slot
+// c % 3, and chunk c's first K step issues chunk c + 2, two ahead for both
+// operands.  Such an item's chunk waits on the latency of its transfer more
+// than on the transfer (per item on the skewed routing: gate/up 89 -> 73 us,
+// down 36 -> 30 us; whole launches 3-4% faster there, 1% at prefill).  At the
+// end of chunk c each thread waits for all but its five loads of chunk c + 2.
+// Chunks 0 and 1 were issued into S0 and S1 before the previous item's
+// epilogue.
+constexpr int kLoadsSmall = 1 + kLoadsB;  // direct loads per thread per chunk of a one-slice item
+
+template <int PHASE, bool MUL>
+__device__ __forceinline__ void pipe_chunk_small(const Pipe& p, const StageRef& cur, const StageRef& ahead,
+                                                 const StageRef& next, int c, int nch, const ReadMap& m,
+                                                 Frags (&fr)[2], f32x16 (&acc)[2][4]) {
+  const bool issue = c + 2 < nch;
+  mma_step<PHASE, 1, MUL, true, true>(fr[0], fr[1], cur, m, 1, p, ahead, c + 2, issue, acc);
+  mma_step<PHASE, 1, MUL, true, false>(fr[1], fr[0], cur, m, 2, p, ahead, c + 2, issue, acc);
+  mma_step<PHASE, 1, MUL, true, false>(fr[0], fr[1], cur, m, 3, p, ahead, c + 2, issue, acc);
+  mma_step<PHASE, 1, MUL, false, false>(fr[1], fr[0], cur, m, 0, p, ahead, c + 2, issue, acc);
+  if (issue)
+    __builtin_amdgcn_s_waitcnt(kWaitAll | kLoadsSmall);
+  else
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+  __builtin_amdgcn_s_barrier();
+  if (MUL) {
+#pragma unroll
+    for (int q = 0; q < 6; ++q) fr[0].v[q] = read_frag<PHASE>(next, m, 0, q);
+  }
+}
+
+template <int PHASE, bool MUL>
+__device__ __forceinline__ void run_item_small(const Pipe& p, const StageRef& S0, const StageRef& S1,
+                                               const StageRef& S2, int nch, const ReadMap& m,
+                                               f32x16 (&acc)[2][4]) {
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
+  __builtin_amdgcn_s_barrier();
+  Frags fr[2];
+  if (MUL) {
+#pragma unroll
+    for (int q = 0; q < 6; ++q) fr[0].v[q] = read_frag<PHASE>(S0, m, 0, q);
+  }
+  int c = 0;
+  for (; c + 3 <= nch; c += 3) {
+    pipe_chunk_small<PHASE, MUL>(p, S0, S2, S1, c, nch, m, fr, acc);
+    pipe_chunk_small<PHASE, MUL>(p, S1, S0, S2, c + 1, nch, m, fr, acc);
+    pipe_chunk_small<PHASE, MUL>(p, S2, S1, S0, c + 2, nch, m, fr, acc);
+  }
+  if (c < nch) pipe_chunk_small<PHASE, MUL>(p, S0, S2, S1, c, nch, m, fr, acc);
+  if (c + 1 < nch) pipe_chunk_small<PHASE, MUL>(p, S1, S0, S2, c + 1, nch, m, fr, acc);
 }
 
 }  // namespace
@@ -277,7 +349,8 @@ __device__ __forceinline__ Plan make_plan(const int* ip, const Groups& gs, int n
   // Direct-load plan.  Load q of wave `wave` fills one 1 KiB region (8 rows
   // x 8 slots) of the A (q < kLoadsA) or B part of a stage: region
   // q' * kWaves + wave, lane l -> row 8 * region + l / 8, slot l % 8 =
-  // segment ^ swz(row).
+  // segment ^ swz(row); A region q * kWaves + wave is region `wave` of A
+  // slice q.
   const uint16_t* abase = it.shared ? a_src_shared : a_src;
   const int astride = PHASE == kGateUp ? d : pl.H;
   size_t arow[kLoadsA];
@@ -304,7 +377,7 @@ __device__ __forceinline__ Plan make_plan(const int* ip, const Groups& gs, int n
     const int region = (is_a ? q : q - kLoadsA) * kWaves + wave;
     const int row = region * kRegionRows + lane / kSegs;
     const int seg = (lane % kSegs) ^ swz(row);
-    pl.p.lds_off[q] = (is_a ? 0 : kStageA) + region * kRegionRows * kChunk;
+    pl.p.lds_off[q] = (is_a ? wave : region) * kRegionRows * kChunk;
     if (is_a) {
       pl.p.src[q] = abase + arow[q] * astride + k0 + seg * 8;
     } else {
@@ -315,13 +388,18 @@ __device__ __forceinline__ Plan make_plan(const int* ip, const Groups& gs, int n
   return pl;
 }
 
-// An item's first chunk, into stage0.
-__device__ __forceinline__ void issue_first(const Plan& pl, uint16_t* stage0) {
+// An item's first chunk into stage0 (one-slice items: its first two chunks
+// into ring slots S0 and S1).
+__device__ __forceinline__ void issue_first(const Plan& pl, const StageRef& stage0, const StageRef& S0,
+                                            const StageRef& S1) {
   switch (pl.na) {
     case 4: issue_chunk<4>(pl.p, stage0, 0); break;
     case 3: issue_chunk<3>(pl.p, stage0, 0); break;
     case 2: issue_chunk<2>(pl.p, stage0, 0); break;
-    default: issue_chunk<1>(pl.p, stage0, 0); break;
+    default:
+      issue_chunk<1>(pl.p, S0, 0);
+      if (pl.nch > 1) issue_chunk<1>(pl.p, S1, 1);
+      break;
   }
 }
 
@@ -346,8 +424,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
   __shared__ int ip[kMaxGroups + 1];
   __shared__ int next_item;
   __shared__ int wsum[kWaves];
-  __shared__ __attribute__((aligned(16))) uint16_t stage0[kStage];
-  __shared__ __attribute__((aligned(16))) uint16_t stage1[kStage];
+  // Operand memory (152 KiB): stage0 = A x0 + B y0, stage1 = A x1 + B y1;
+  // the one-slice ring's slots S0 = (s0, y0), S1 = (s1, y1), S2 = (s2, x1),
+  // with A slices of their own.
+  __shared__ __attribute__((aligned(16))) uint16_t x0[kStageA];
+  __shared__ __attribute__((aligned(16))) uint16_t y0[kStageB];
+  __shared__ __attribute__((aligned(16))) uint16_t x1[kStageA];
+  __shared__ __attribute__((aligned(16))) uint16_t y1[kStageB];
+  __shared__ __attribute__((aligned(16))) uint16_t s0[kSlice];
+  __shared__ __attribute__((aligned(16))) uint16_t s1[kSlice];
+  __shared__ __attribute__((aligned(16))) uint16_t s2[kSlice];
   const int nt_routed = PHASE == kGateUp ? h / (kTileN / 2) : d / kTileN;
   const int nt_shared = (PHASE == kGateUp ? hs / (kTileN / 2) : d / kTileN) * (SPLIT ? ks : 1);
   const int items = item_prefix<kTileM, kThreads>(ip, wsum, gs, nt_routed, nt_shared);
@@ -360,9 +446,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
 #pragma unroll
   for (int st = 0; st < kSteps; ++st) {
     const int slot = ((2 * st + lhi) ^ f) * 8;
-    m.a[st] = (wm * 64 + l32) * kChunk + slot;
-    m.b[st] = kStageA + (b_row0<PHASE>(wn, 0) + l32) * kChunk + slot;
+    m.a[st] = l32 * kChunk + slot;
+    m.b[st] = (b_row0<PHASE>(wn, 0) + l32) * kChunk + slot;
   }
+  const StageRef stage0{x0, x0 + wm * kSlice, y0};
+  const StageRef stage1{x1, x1 + wm * kSlice, y1};
+  const StageRef S0{s0, s0, y0};
+  const StageRef S1{s1, s1, y1};
+  const StageRef S2{s2, s2, x1};
 
   // Dynamic work queue per XCD: queue q owns items [items·q/8, items·(q+1)/8)
   // and hands them out in order, one atomic per item.  A block takes from its
@@ -389,7 +480,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
   int wi = next_item;
   if (wi < 0) return;  // uniform across the block
   Plan cur = make_plan<PHASE, SPLIT>(ip, gs, nt_routed, nt_shared, wi, d, h, hs, a_src, a_src_shared, w, ws, wave, lane, ks);
-  issue_first(cur, stage0);
+  issue_first(cur, stage0, S0, S1);
   for (;;) {
     const int wave_row0 = cur.it.m0 + wm * 64;
     // A wave multiplies iff some of its 64 rows exist (wm < na; uniform per
@@ -409,8 +500,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
       case 6: run_item<PHASE, 3, false>(cur.p, stage0, stage1, cur.nch, m, acc); break;
       case 5: run_item<PHASE, 2, true>(cur.p, stage0, stage1, cur.nch, m, acc); break;
       case 4: run_item<PHASE, 2, false>(cur.p, stage0, stage1, cur.nch, m, acc); break;
-      case 3: run_item<PHASE, 1, true>(cur.p, stage0, stage1, cur.nch, m, acc); break;
-      default: run_item<PHASE, 1, false>(cur.p, stage0, stage1, cur.nch, m, acc); break;
+      case 3: run_item_small<PHASE, true>(cur.p, S0, S1, S2, cur.nch, m, acc); break;
+      default: run_item_small<PHASE, false>(cur.p, S0, S1, S2, cur.nch, m, acc); break;
     }
     // Every wave is past the K loop (its LDS reads done, its trailing loads
     // landed: the release fence of this barrier drains both), so stage0 may
@@ -423,19 +514,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
     Plan nxt;
     if (more) {
       nxt = make_plan<PHASE, SPLIT>(ip, gs, nt_routed, nt_shared, wi, d, h, hs, a_src, a_src_shared, w, ws, wave, lane, ks);
-      issue_first(nxt, stage0);
+      issue_first(nxt, stage0, S0, S1);
     }
 
     // Epilogue.  Element i of acc[ms][ns] is row 8*(i/4) + 4*lhi + (i%4) of
     // M-subtile ms, column l32 of N-subtile ns.  The routed down output
-    // (bf16, 128 columns per wave) goes through stage1 (free: the down K
-    // loop's last chunk issued no loads, and the next item's first chunk went
-    // to stage0): each wave writes its tile there and reads it back as 16-byte
-    // row segments, so the global stores are whole 16-byte pieces (eight times
-    // fewer than one per element).  Only the wave's own 8 KiB region is
-    // touched, so a wave-level fence orders the writes before the reads and
-    // the reads before the next writes.  The other outputs are stored per
-    // element.
+    // (bf16, 128 columns per wave) goes through x1 (free: the down K loop's
+    // last chunks issued no loads, and the next item's first chunks went to
+    // stage0 or to slots S0 and S1): each wave writes 16 rows of its tile
+    // there at a time and reads them back as 16-byte row segments, so the
+    // global stores are whole 16-byte pieces (eight times fewer than one per
+    // element).  Only the wave's own 4 KiB region is touched, so a wave-level
+    // fence orders the writes before the reads and the reads before the next
+    // writes.  The other outputs are stored per element.
     if (mul) {
       const Item& it = cur.it;
       const int H = cur.H;
@@ -479,27 +570,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
           }
         }
       } else if (!it.shared) {
-        // 64 rows x 128 columns of this wave, in two halves of 32 rows.
-        uint16_t* sb = stage1 + wave * (32 * 128);  // 4096 bf16
+        // 64 rows x 128 columns of this wave, 16 rows at a time through its
+        // 4 KiB of x1 (free: the next item's first chunks went to stage0 or
+        // to slots S0 and S1).
+        uint16_t* sb = x1 + wave * (16 * 128);  // 2048 bf16
 #pragma unroll
         for (int ms = 0; ms < 2; ++ms) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
+          for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-            for (int ns = 0; ns < 4; ++ns) {
-              const int rr = 8 * (i / 4) + 4 * lhi + (i % 4);
-              sb[rr * 128 + ns * 32 + l32] = (uint16_t)f32_to_bf16(acc[ms][ns][i]);
+            for (int i4 = 0; i4 < 8; ++i4)
+#pragma unroll
+              for (int ns = 0; ns < 4; ++ns) {
+                const int rr = 8 * (i4 / 4) + 4 * lhi + (i4 % 4);
+                sb[rr * 128 + ns * 32 + l32] = (uint16_t)f32_to_bf16(acc[ms][ns][8 * hf + i4]);
+              }
+            wave_fence();
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {  // 16 rows x 16 segments
+              const int idx = lane + kWave * j, rr = idx / 16, sg = idx % 16;
+              const u32x4 v = *reinterpret_cast<const u32x4*>(sb + rr * 128 + sg * 8);
+              const int r = wave_row0 + ms * 32 + 16 * hf + rr;
+              if (r < it.nrows)
+                *reinterpret_cast<u32x4*>(out + (size_t)(it.row0 + r) * d + it.nt * kTileN + wn * 128 + sg * 8) = v;
             }
-          wave_fence();
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {  // 32 rows x 16 segments
-            const int idx = lane + kWave * j, rr = idx / 16, sg = idx % 16;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(sb + rr * 128 + sg * 8);
-            const int r = wave_row0 + ms * 32 + rr;
-            if (r < it.nrows)
-              *reinterpret_cast<u32x4*>(out + (size_t)(it.row0 + r) * d + it.nt * kTileN + wn * 128 + sg * 8) = v;
+            wave_fence();
           }
-          wave_fence();
         }
       } else {
 #pragma unroll
