@@ -42,6 +42,7 @@ def route_buffers(T, E, k):
 
 @pytest.mark.parametrize("T,d,E,k,with_gamma", [
     (64, 4096, 288, 8, False),     # decode batch: the router normalises as it loads
+    (256, 4096, 288, 8, False),    # a layer of the chained stack
     (1, 4096, 288, 8, True),
     (100, 256, 16, 2, True),
     (1024, 512, 64, 4, True),      # staged router: normalisation pass first
