@@ -6,12 +6,12 @@
 // [Blog] "Step 3.5 Flash: Open Frontier-Level Intelligence with 11B Active
 // Parameters" §3.2.4 (fused MoE gather/scatter with grouped GEMM).
 //
-// These are the streaming-regime kernels (under 5 rows per expert on
-// average, 10 for down: decode-sized batches; the dense FFN up to 64 tokens),
-// where the weights are read once and the MFMA work is small: every wave
-// loads its operands straight from HBM/L2 into registers, keeping a batch of
-// 2 to 8 K-steps of weight rows in flight (6 at decode: the batch length
-// trades bytes in flight per wave against waves per SIMD).  The item
+// These are the streaming-regime kernels (under 11 rows per expert on
+// average, 10 for down: decode-sized and small batches; the dense FFN up to
+// 64 tokens), where the weights are read once and the MFMA work is small:
+// every wave loads its operands straight from HBM/L2 into registers, keeping
+// a batch of 2 to 8 K-steps of weight rows in flight (6 at decode: the batch
+// length trades bytes in flight per wave against waves per SIMD).  The item
 // decomposition is in grouped.h.
 //
 // Phase 1 (gate/up): item = BM rows x 64 hidden units (or 16 with the
@@ -404,16 +404,26 @@ namespace {
 
 // Which regime a phase runs in (crossovers measured on the 288-expert layer,
 // d = 4,096, and on the dense FFN of hidden 11,264):
-// - routed gate/up: the LDS-tiled kernels from 5 rows per routed group on
-//   average.  Below, the streaming kernels win (4.0 rows per group: 647 vs
-//   717 us); at 5.3 the two tie (744 vs 739 us); above, more groups span
-//   several 16-row M-tiles, each of which reads the expert's weights again
-//   in the streaming kernels, while the tiled ones read them once per 256
-//   rows (7.1 rows per group: 881 vs 798 us; 57: three times faster).
+// - routed gate/up: the LDS-tiled kernels from 11 rows per routed group on
+//   average; from 2 to 11 the streaming kernels with 32-row items (one M-tile
+//   for nearly every group, so each weight row is read once; with 16-row
+//   items a group of 17-32 rows reads its weights twice) in batches of 2 K
+//   steps, two groups of 16 units per wave; below 2, 16-row items.  Gate/up
+//   per launch, the previous rule (16-row streaming items below 5 rows per
+//   group, tiled from 5) -> this one: 2.7 rows per group 0.558 -> 0.541 ms,
+//   3.6: 0.615 -> 0.591, 4.4: 0.659 -> 0.610, 5.3: 0.710 -> 0.627, 7.1:
+//   0.716 -> 0.633, 8.9: 0.786 -> 0.708, 10.7: 0.792 -> 0.767; at 12.4 the
+//   32-row items lose (0.826 vs 0.793), at 1.8 (decode) they tie.  Batches
+//   of 4 or 8 steps, or one group per wave, hold more registers per wave and
+//   ran 7-12% slower at 7.1 rows per group.
 // - routed down: tiled from 10 rows per group; from 4 to 10 it streams
-//   32-row items (one M-tile for most groups) in batches of 4 K steps
-//   (8.0 rows per group: 424 vs 496 us tiled; 10.7: 500 vs 505; 12.4: 566
-//   vs 513), below 4 16-row items.
+//   32-row items (one M-tile for most groups) in batches of 2 K steps with
+//   four groups of 16 columns per wave (8.0 rows per group: 424 vs 496 us
+//   tiled in batches of 4 with two groups; 10.7: 500 vs 505; 12.4: 566 vs
+//   513; four groups in batches of 2 against two in batches of 4: 7.1 rows
+//   per group 0.372 vs 0.381 ms, 8.9: 0.421 vs 0.438), below 4 16-row items
+//   (at decode two groups in batches of 6 beat four groups in batches of 2
+//   or 6: 0.248 vs 0.254 and 0.274 ms).
 // - the shared group alone (the dense FFN): the tiled kernels above 64
 //   tokens.  Up to 256 tokens (one M-tile) they need the caller's split
 //   scratch, which spreads each weight tile's reduction over several items
@@ -424,7 +434,7 @@ namespace {
 //   64 tokens the streaming kernels with one M-tile win (64 tokens: 0.092 vs
 //   0.122 ms; 80 to 128 tokens: within 3% of the tiled ones).
 bool use_tiled(int T, int k, int E, const int32_t* offsets, bool down, bool split_scratch) {
-  if (offsets) return (long)T * k >= (down ? 10L : 5L) * E;
+  if (offsets) return (long)T * k >= (down ? 10L : 11L) * E;
   if (T <= 64) return false;
   return down ? T > 256 || split_scratch : true;
 }
@@ -498,6 +508,10 @@ hipError_t launch_gate_up(int T, int d, int E, int k, int h, int hs, const uint1
   // -> 0.061, 32: 0.093 -> 0.075, 48: 0.157 -> 0.082, 64: 0.122 -> 0.092.
   if (!offsets && split && T <= 16)
     return gate_up_bm<16, 4, 4>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, act_clamp, stream);
+  // Routed groups of 2 to 11 rows on average (below the tiled kernels'
+  // threshold): 32-row items, batches of 2 steps, two 16-unit groups per wave.
+  if (offsets && split && (long)T * k >= 2L * et)
+    return gate_up_bm<32, 4, 2, 2>(x, gs, d, h, hs, w_gu, ws_gu, hid, hid_shared, act_clamp, stream);
   // 16-row items in batches of 6 steps (three waves per SIMD): 483 -> 477 us
   // at decode against batches of 8.
   if (pick_bm(T, k, offsets ? et : 1) == 16) {
@@ -537,8 +551,18 @@ hipError_t launch_down(int T, int d, int E, int k, int h, int hs, const int32_t*
     if (T <= 64) return down_bm_split<64, 2, 4>(gs, d, hs, hid_shared, ws_down, y_shared, partial, stream);
     return down_bm_split<32>(gs, d, hs, hid_shared, ws_down, y_shared, partial, stream);
   }
-  if (offsets && (long)T * k >= 4L * et)
+  // Routed groups of 4 to 10 rows on average: 32-row items, batches of 2
+  // steps, four 16-column groups per wave where the item width (256 columns)
+  // divides d, else two in batches of 4.
+  if (offsets && (long)T * k >= 4L * et) {
+    if (d % 256 == 0) {
+      const auto kern = k_down<32, 1, 1, 4, 2>;
+      hipLaunchKernelGGL(kern, dim3(persistent_grid(kern) * kOversubscribe), dim3(256), 0, stream, gs, d, h, hs, hid,
+                         hid_shared, w_down, ws_down, y_perm, y_shared, nullptr);
+      return hipGetLastError();
+    }
     return down_bm<32, 1, 4>(gs, d, h, hs, hid, hid_shared, w_down, ws_down, y_perm, y_shared, stream);
+  }
   if (pick_bm(T, k, offsets ? et : 1) == 16) {
     if (split) return down_bm<16, 4>(gs, d, h, hs, hid, hid_shared, w_down, ws_down, y_perm, y_shared, stream);
     // Batches of 6 steps, four waves per SIMD: 256 -> 247 us at decode

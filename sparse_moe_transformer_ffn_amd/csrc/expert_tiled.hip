@@ -1,5 +1,5 @@
 // expert_tiled.hip -- grouped SwiGLU expert GEMMs for the compute regime
-// (from 5 rows per expert on average, 10 for down, up to prefill-sized
+// (from 11 rows per expert on average, 10 for down, up to prefill-sized
 // batches; the dense FFN above 64 tokens), bf16 MFMA 32x32x16.
 //
 // Layer definition as in expert.hip ([Digest] "Step 3.5 Flash 技术论文深度解读"

@@ -33,7 +33,8 @@ def run(dl, off, perm, clamp):
 
 @pytest.mark.parametrize("cfg,clamp", [
     (moegen.custom(0, T=24, seed=951), 0.02),                                    # streaming kernels
-    (moegen.CONFIGS[0], 0.02),                                                   # 8 rows per expert: tiled gate/up
+    (moegen.CONFIGS[0], 0.02),                                                   # 8 rows per expert: 32-row items
+    (moegen.custom(0, T=96, seed=952), 0.02),                                    # 12 rows per expert: tiled gate/up
     (moegen.CONFIGS[1], 0.5),                                                    # decode size (streaming)
     (moegen.custom(0, T=2048, d=256, E=16, k=2, h=128, hs=128, seed=950), 0.02),  # tiled kernels
 ])

@@ -136,9 +136,11 @@ def test_layer_diagnostic_side_outputs(device, idx):
 
 
 @pytest.mark.parametrize("T,k,hs,scale", [
-    (1, 8, 1280, 1.0), (3, 1, 1280, 1.0), (97, 8, 0, 0.5), (130, 8, 1280, 2.0),  # streaming kernels
-    (144, 8, 1280, 1.0),                       # 4 rows per expert: streaming gate/up, 32-row down items
-    (256, 8, 1280, 1.0), (400, 8, 1280, 1.0),  # tiled gate/up from 5 rows per expert, tiled down from 10
+    (1, 8, 1280, 1.0), (3, 1, 1280, 1.0), (60, 8, 1280, 1.0),  # 16-row streaming items
+    (97, 8, 0, 0.5), (130, 8, 1280, 2.0),      # 2.7 and 3.6 rows per expert: 32-row gate/up items
+    (144, 8, 1280, 1.0),                       # 4 rows per expert: 32-row gate/up and down items
+    (256, 8, 1280, 1.0), (390, 8, 1280, 1.0),  # 7.1 and 10.8 rows: 32-row gate/up items, tiled down from 10
+    (400, 8, 1280, 1.0),                       # 11.1 rows per expert: tiled gate/up and down
 ])
 def test_layer_edge_shapes(device, T, k, hs, scale):
     cfg = moegen.custom(1, T=T, k=k, hs=hs, routed_scale=scale, seed=500 + T)
@@ -157,7 +159,10 @@ def test_layer_edge_shapes(device, T, k, hs, scale):
     (100, 256, 1, 1, 128, 128),      # one expert: a dense SwiGLU plus the shared expert
     (64, 256, 2, 2, 128, 0),         # k = E: every token takes every expert
     (64, 256, 1024, 16, 128, 128),   # E and k at their limits: streaming kernels
-    (350, 256, 1024, 16, 128, 128),  # ... 5.5 rows per expert: tiled gate/up, 32-row streaming down
+    (350, 256, 1024, 16, 128, 128),  # ... 5.5 rows per expert: 32-row streaming items in both phases
+    (200, 384, 64, 2, 128, 128),     # 6.3 rows per expert, d % 256 != 0: two column groups per down wave
+    (150, 192, 32, 2, 64, 64),       # 9.4 rows per expert, d % 128 != 0: the unsplit streaming kernels
+    (720, 256, 64, 1, 128, 128),     # 11.3 rows per expert: tiled gate/up and down
 ])
 def test_layer_compute_regime_small(device, T, d, E, k, h, hs):
     cfg = moegen.custom(0, T=T, d=d, E=E, k=k, h=h, hs=hs, seed=900 + T)
