@@ -572,6 +572,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--only-prefill", action="store_true", help="time only the prefill workload (profiling)")
     ap.add_argument("--only-skew", action="store_true", help="time only the skewed-load workload (profiling)")
+    ap.add_argument("--only-stack", action="store_true", help="time only the 12-layer stack (profiling)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 1 GiB device copy (the known-size reference for HBM byte counters)")
     ap.add_argument("--prefill-steps", type=int, default=10)
@@ -616,6 +617,9 @@ def main():
         _, p = time_workload(pcfg, args.steps, args.warmup, dev, extras=False)
         print(json.dumps({"workload": pcfg.workload, "ms_per_step": p["ms_per_step"],
                           "gate_up_ms": p["gate_up_ms"], "down_ms": p["down_ms"]}), flush=True)
+        return
+    if args.only_stack:
+        print(json.dumps(time_stack(args.steps, args.warmup, dev)), flush=True)
         return
     cfg = moegen.CONFIGS[1]
     extras = not args.no_extras
