@@ -345,7 +345,10 @@ def time_skew(steps, warmup, dev, cpu_sample=0):
 def time_stack(steps, warmup, dev, cpu_sample=0):
     """The 12-layer stack (T = 256, distinct weights per layer, 109 GB
     resident): layer l + 1 takes the unit-gain RMSNorm of layer l's output.
-    One pass = 12 layer steps and 11 normalisations; supplementary figure."""
+    One pass = 12 layer steps and 11 normalisations; supplementary figure.
+    Its dominant kernel (each layer's grouped gate/up launch) is HBM-bound:
+    the roofline object gives its algorithmic bytes over its time, summed
+    over the layers."""
     import numpy as np
     import torch
     import moegen
@@ -354,9 +357,9 @@ def time_stack(steps, warmup, dev, cpu_sample=0):
     layers = [Workload(cfg, dev, layer=l) for l in range(cfg.layers)]
     main = torch.cuda.current_stream()
 
-    def chain():
+    def chain(ev=None):
         for l, wl in enumerate(layers):
-            wl.step(main)
+            wl.step(main, ev[l] if ev else None)
             if l + 1 < cfg.layers:
                 moe.moe_rmsnorm(cfg.T, cfg.d, wl.buf.y, None, 1e-6, layers[l + 1].x, main)
 
@@ -370,14 +373,30 @@ def time_stack(steps, warmup, dev, cpu_sample=0):
         z.record(main)
     torch.cuda.synchronize()
     per = np.array([a.elapsed_time(z) for a, z in ev])
+    # The same passes with events around each layer's two expert launches
+    # (records idle the GPU between kernels, so these are not the timed
+    # passes): the dominant kernel's time.
+    lev = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in layers] for _ in range(steps)]
+    for p in lev:
+        chain(p)
+    torch.cuda.synchronize()
+    gu_ms = np.array([[e[1].elapsed_time(e[2]) for e in p] for p in lev]).mean(0)   # per layer
+    dn_ms = np.array([[e[2].elapsed_time(e[3]) for e in p] for p in lev]).mean(0)
     touched = [int((wl.buf.expert_counts.cpu().numpy() > 0).sum()) for wl in layers]
-    nbytes = sum(algorithmic(cfg, n)["step_bytes"] for n in touched)
+    algs = [algorithmic(cfg, n) for n in touched]
+    nbytes = sum(a["step_bytes"] for a in algs)
+    gu_gbs = sum(a["gate_up_bytes"] for a in algs) / (gu_ms.sum() * 1e-3) / 1e9
+    dn_gbs = sum(a["down_bytes"] for a in algs) / (dn_ms.sum() * 1e-3) / 1e9
     ms = float(np.median(per))
     x0 = layers[0].x_h
     del layers
     out = {"workload": cfg.workload, "layers": cfg.layers, "tok_s": cfg.T / (ms * 1e-3), "ms_per_pass_median": ms,
            "ms_per_pass_min": float(per.min()), "passes": steps, "hbm_gbs": nbytes / (ms * 1e-3) / 1e9,
-           "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "touched_experts_per_layer": touched}
+           "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "roofline": roofline("hbm", gu_gbs, None),
+           "kernels": {"gate_up_ms_per_layer": float(gu_ms.mean()), "down_ms_per_layer": float(dn_ms.mean()),
+                       "gate_up_gbs": gu_gbs, "down_gbs": dn_gbs},
+           "touched_experts_per_layer": touched}
     if cpu_sample:
         out["cpu_baseline"] = cpu_baseline_stack(cfg, x0, cpu_sample)
     return out
