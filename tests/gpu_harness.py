@@ -239,8 +239,12 @@ def assert_same_up_to_order(a, b, what=""):
     assert np.all(np.abs(err) <= bound), f"{what}: max abs {mx:.3e}"
 
 
-def check_output(y_gpu, y_ref, what=""):
-    """Relative L2 <= 5e-3 and max |err| <= 3e-2 * RMS(ref)."""
+def check_output(y_gpu, y_ref, what="", own_rounding=False):
+    """Relative L2 <= 5e-3 and max |err| <= 3e-2 * RMS(ref).  own_rounding:
+    each element's bound also takes the bf16 half-ulp of its own value
+    (2^-8 |ref|), which the stored bf16 output can be off by on its own --
+    for shapes whose outputs reach several times their RMS (the shape sweep),
+    not for the workloads, which meet the plain bar."""
     y_gpu = np.asarray(y_gpu, np.float64)
     y_ref = np.asarray(y_ref, np.float64)
     err = y_gpu - y_ref
@@ -249,5 +253,11 @@ def check_output(y_gpu, y_ref, what=""):
     mx = np.abs(err).max() if err.size else 0.0
     log(f"  {what}: rel_l2={rel:.3e} max_abs={mx:.3e} (rms {rms:.3e})")
     assert rel <= REL_L2_TOL, f"{what}: relative L2 {rel:.3e} > {REL_L2_TOL}"
-    assert mx <= MAX_ABS_TOL * rms, f"{what}: max abs {mx:.3e} > {MAX_ABS_TOL} * rms {rms:.3e}"
+    if own_rounding:
+        bound = MAX_ABS_TOL * rms + 2.0 ** -8 * np.abs(y_ref)
+        worst = int(np.argmax(np.abs(err) - bound)) if err.size else 0
+        assert np.all(np.abs(err) <= bound), (f"{what}: |err| {np.abs(err).flat[worst]:.3e} > "
+                                              f"{MAX_ABS_TOL} * rms {rms:.3e} + 2^-8 * |ref| {np.abs(y_ref).flat[worst]:.3e}")
+    else:
+        assert mx <= MAX_ABS_TOL * rms, f"{what}: max abs {mx:.3e} > {MAX_ABS_TOL} * rms {rms:.3e}"
     return rel, mx / max(rms, 1e-300)

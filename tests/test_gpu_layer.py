@@ -39,7 +39,7 @@ def gpu_results(buf):
             buf.expert_counts.cpu().numpy(), moegen.bf16_to_f32(bf16_host(buf.y)))
 
 
-def check_layer(dl, buf, tokens):
+def check_layer(dl, buf, tokens, own_rounding=False):
     cfg = dl.cfg
     g_ids, g_w, g_gap, g_cnt, g_y = gpu_results(buf)
     o_ids, o_w, o_gap, beta = oracle_route_all(dl, with_beta=True)
@@ -56,7 +56,7 @@ def check_layer(dl, buf, tokens):
     log(f"  near-tie tokens {near}, routed the other way {int((~same).sum())}; comparing output of "
         f"{len(tokens)} tokens ({flipped} of them under their acceptable other set)")
     _, y_ref = oracle_layer_tokens(dl, tokens, ids[tokens])
-    check_output(g_y[tokens], y_ref, f"config {cfg.index} layer {dl.layer} y")
+    check_output(g_y[tokens], y_ref, f"config {cfg.index} layer {dl.layer} y", own_rounding=own_rounding)
     return g_ids, same
 
 
@@ -170,6 +170,37 @@ def test_layer_compute_regime_small(device, T, d, E, k, h, hs):
     dl = DeviceLayer(cfg)
     buf = run_layer(dl)
     check_layer(dl, buf, np.arange(T))
+
+
+def _sweep_shapes(n=64, seed=20261203):
+    """Seeded random layer shapes: 1 to 1,024 experts, top-1 to top-16,
+    model, expert and shared sizes that are and are not multiples of 128 and
+    256, and 0.3 to 60 rows per expert on average, so the draws fall in every
+    kernel regime and on both sides of each threshold between them."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for i in range(n):
+        E = int(rng.choice([1, 4, 8, 16, 48, 64, 128, 288, 1024]))
+        k = int(rng.integers(1, min(16, E) + 1))
+        d = int(rng.choice([64, 128, 192, 256, 320, 384, 512]))
+        h = int(rng.choice([64, 128, 192, 256]))
+        hs = int(rng.choice([0, 64, 128, 192]))
+        rows = float(np.exp(rng.uniform(np.log(0.3), np.log(60.0))))
+        T = int(min(3000, max(1, round(rows * E / k))))
+        shapes.append((T, d, E, k, h, hs, 7000 + i))
+    return shapes
+
+
+@pytest.mark.parametrize("T,d,E,k,h,hs,seed", _sweep_shapes())
+def test_layer_shape_sweep(device, T, d, E, k, h, hs, seed):
+    # Outputs of these shapes reach 7 times their RMS, where the bf16 output's
+    # own rounding (2^-8 relative) is most of the 3e-2 * RMS bar; the bound
+    # per element adds it (check_output's own_rounding).
+    cfg = moegen.custom(0, T=T, d=d, E=E, k=k, h=h, hs=hs, seed=seed)
+    log(f"[layer-sweep] T={T} d={d} E={E} k={k} h={h} hs={hs} seed={seed}: {T * k / E:.1f} rows per expert")
+    dl = DeviceLayer(cfg)
+    buf = run_layer(dl)
+    check_layer(dl, buf, np.arange(T), own_rounding=True)
 
 
 def test_layer_all_tokens_one_expert(device):

@@ -53,3 +53,25 @@ def test_check_routing_accepts_only_valid_near_tie_flips():
     wrong = np.array([[0, 2], [0, 1]], np.int32)   # expert 2 is far below the k-th score
     with pytest.raises(AssertionError):
         check_routing(wrong, o_w, o_gap, np.bincount(wrong.ravel(), minlength=E), o_ids, o_w, o_gap, E, beta=beta)
+
+
+def test_check_output_own_rounding_bound():
+    # A heavy-tailed output (a few elements at 8 times the RMS) stored as
+    # bf16: the stored values alone can miss the plain 3e-2 * RMS bar, and
+    # pass once each element's bound takes its own half-ulp; an error of a
+    # tenth of the RMS on one element fails either way.
+    from tests._util import bf16_round
+    from tests.gpu_harness import check_output
+    rng = np.random.default_rng(3)
+    ref = rng.standard_normal((64, 256))
+    ref[0, :4] = np.ldexp(1.0 + 2.0 ** -8 - 1e-6, 3) * np.array([1.0, -1.0, 1.0, -1.0])  # just below a tie above 8
+    got = bf16_round(ref)
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert np.abs(got - ref).max() > 3e-2 * rms
+    with pytest.raises(AssertionError):
+        check_output(got, ref, "plain bar")
+    check_output(got, ref, "own rounding", own_rounding=True)
+    bad = got.copy()
+    bad[5, 7] += 0.1 * rms
+    with pytest.raises(AssertionError):
+        check_output(bad, ref, "planted error", own_rounding=True)
