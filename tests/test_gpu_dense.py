@@ -75,6 +75,32 @@ def test_dense_parity(device, T, d, H):
     check_output(y[:T], ref, f"dense T={T} H={H}")
 
 
+def _dense_sweep(n=32, seed=20261204):
+    """Seeded random dense shapes: half of them up to 64 tokens (the per-CU
+    share kernels where the hidden size allows, else the streaming ones),
+    half up to 300 (the tiled kernels, split or not); hidden sizes from 64 to
+    12,800 units and model sizes from 64 to 1,024, all multiples of 64."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for i in range(n):
+        T = int(rng.integers(1, 65)) if i % 2 == 0 else int(rng.integers(65, 301))
+        d = 64 * int(rng.integers(1, 17))
+        H = 64 * int(rng.integers(64, 201)) if rng.random() < 0.6 else 64 * int(rng.integers(1, 64))
+        shapes.append((T, d, H, 9000 + i))
+    return shapes
+
+
+@pytest.mark.parametrize("T,d,H,seed", _dense_sweep())
+def test_dense_shape_sweep(device, T, d, H, seed):
+    # Every token against the oracle, at the plain bar (the output is f32).
+    cfg = moegen.custom(1, T=T, d=d, hs=H, seed=seed)
+    log(f"[dense-sweep] T={T} d={d} H={H} seed={seed}")
+    x_h = moegen.x(cfg)
+    y = run_dense(cfg, x_h, H)
+    ref = oracle_rows(cfg, x_h, range(T))
+    check_output(y[:T], ref, f"dense T={T} d={d} H={H}")
+
+
 def test_dense_prefill_sampled_rows(device):
     T, d, H = 8192, 4096, DENSE_HIDDEN
     cfg = moegen.custom(2, hs=H, seed=2)
