@@ -1,8 +1,9 @@
 """moe_expert_swiglu_range: the grouped expert kernels on one contiguous share
 of the experts, as one GPU of an 8-way expert-parallel group would run them
 (36 of 288 experts, with only those experts' weights).  Workloads: tiny,
-decode (streaming kernels), T = 256 (7 rows per expert: tiled gate/up,
-32-row streaming down) and prefill (tiled kernels).
+decode (streaming kernels), T = 256 (7 rows per expert: 32-row streaming
+items in both phases) and prefill (tiled kernels), and seeded random layer
+shapes cut into shares at random expert boundaries.
 
 Each share's rows must be bit-identical to the whole call's (same kernels,
 same reduction order), rows outside the share untouched, and sampled rows
@@ -75,3 +76,50 @@ def test_share_without_rows_writes_nothing(device):
     moe.moe_expert_swiglu_range(s, 4, 8, dl.x, i32_dev(off), i32_dev(perm), dl.w_gu[4:8], dl.w_d[4:8], y, ws)
     torch.cuda.synchronize()
     assert np.all(moegen.bf16_to_f32(bf16_host(y)) == 3.0)
+
+
+def _share_sweep(n=16, seed=20261205):
+    """Seeded random layer shapes (as the layer sweep draws them) and random
+    cuts of the experts into two to five contiguous shares."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([4, 8, 16, 48, 64, 128, 288, 1024]))
+        k = int(rng.integers(1, min(16, E) + 1))
+        d = int(rng.choice([64, 128, 192, 256, 384, 512]))
+        h = int(rng.choice([64, 128, 192, 256]))
+        hs = int(rng.choice([0, 64, 128]))
+        rows = float(np.exp(rng.uniform(np.log(0.3), np.log(60.0))))
+        T = int(min(3000, max(1, round(rows * E / k))))
+        ncut = int(rng.integers(1, min(4, E - 1) + 1))
+        cuts = sorted(int(c) for c in rng.choice(np.arange(1, E), ncut, replace=False))
+        out.append((T, d, E, k, h, hs, 8000 + i, tuple(cuts)))
+    return out
+
+
+@pytest.mark.parametrize("T,d,E,k,h,hs,seed,cuts", _share_sweep())
+def test_random_shares_match_whole_call(device, T, d, E, k, h, hs, seed, cuts):
+    # The launches of a share pick their regime from the rows per expert of
+    # the whole routing (e_total), so every share runs the whole call's
+    # kernels on its rows: bit-identical, nothing written outside.
+    cfg = moegen.custom(0, T=T, d=d, E=E, k=k, h=h, hs=hs, seed=seed)
+    log(f"[shard-sweep] T={T} d={d} E={E} k={k} h={h} hs={hs} cuts={cuts}: {T * k / E:.1f} rows per expert")
+    dl = DeviceLayer(cfg)
+    o_ids, _, _ = oracle_route_all(dl)
+    _, off, perm, _ = oracle.permute(o_ids, cfg.E)
+    s = moe.make_shape(T, d, E, k, h, hs)
+    ws = torch.empty(moe.moe_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    off_d, perm_d = i32_dev(off), i32_dev(perm)
+    y_full = torch.zeros((T * k, d), dtype=torch.bfloat16, device="cuda")
+    moe.moe_expert_swiglu(s, dl.x, off_d, perm_d, dl.w_gu, dl.w_d, y_full, ws)
+    torch.cuda.synchronize()
+    full = bf16_host(y_full)
+    bounds = list(zip((0,) + cuts, cuts + (E,)))
+    for b, e in bounds:
+        y = torch.full((T * k, d), SENTINEL, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        moe.moe_expert_swiglu_range(s, b, e, dl.x, off_d, perm_d, dl.w_gu[b:e], dl.w_d[b:e], y, ws)
+        torch.cuda.synchronize()
+        got = bf16_host(y)
+        lo, hi = off[b], off[e]
+        np.testing.assert_array_equal(got[lo:hi], full[lo:hi])
+        assert np.all(got[:lo] == SENTINEL) and np.all(got[hi:] == SENTINEL)
