@@ -1,7 +1,7 @@
 """moe_expert_swiglu_noalloc (for callers that cannot allocate device memory)
 against moe_expert_swiglu with a caller workspace: the same kernels, so the
-same bits, on two calls in a row -- the second with a smaller batch, and in
-the other kernel regime -- sharing the library's static scratch."""
+same bits, on calls in a row -- each with a smaller batch than the last,
+and in another kernel regime -- sharing the library's static scratch."""
 import numpy as np
 import pytest
 import torch
@@ -43,16 +43,20 @@ def _both(dl, T, seed, shared):
 @pytest.mark.parametrize("shared", [True, False])
 def test_noalloc_matches_workspace_call_twice(device, shared):
     # First call: 1,024 tokens of the decode layer's shape (about 28 rows per
-    # expert: the tiled kernels and their work queue); second call: 48 tokens
-    # (streaming kernels), into the same static scratch.
+    # expert: the tiled kernels and their work queue); then 256 tokens (7 rows
+    # per expert: 32-row streaming items) and 48 (16-row streaming items),
+    # into the same static scratch.
     cfg = moegen.custom(1, T=1024, seed=77)
     dl = DeviceLayer(cfg)
-    log(f"[noalloc] shared={shared}: 1024 tokens, then 48")
+    log(f"[noalloc] shared={shared}: 1024 tokens, then 256, then 48")
     first = _both(dl, 1024, 5, shared)
     keep = bf16_host(first).copy()
+    second = _both(dl, 256, 7, shared)
+    keep2 = bf16_host(second).copy()
     _both(dl, 48, 6, shared)
-    # The first call's output is the caller's and stays as it was.
+    # The earlier calls' outputs are the caller's and stay as they were.
     np.testing.assert_array_equal(bf16_host(first), keep)
+    np.testing.assert_array_equal(bf16_host(second), keep2)
 
 
 def test_noalloc_rejects_shapes_beyond_its_scratch(device):
