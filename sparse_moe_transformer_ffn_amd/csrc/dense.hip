@@ -114,7 +114,7 @@ struct Stream {
   static constexpr int NT = (G + 1) / 2;
   const uint16_t* wsrc[G];
   const uint16_t* xsrc[MB];
-  uint16_t* patch;  // this wave's G KiB of LDS
+  uint16_t* patch;  // this wave's 2 NT KiB of LDS
   int wr;           // lane's LDS element offset of its line writes (group 0)
   int rd[2];        // lane's LDS element offset of its B operand, per step (tile 0)
   bool zero_hi;     // lane reads the missing upper group of the last tile (odd G)
@@ -220,12 +220,15 @@ __device__ __forceinline__ void stream_setup(Stream<MB, G>& st, const uint16_t* 
   st.zero_hi = c >= 8;
 }
 
-// LDS of a kernel: each wave's G KiB patch (8 KiB for down), the same memory
-// holding the partial sums of tree_sum afterwards.
+// LDS of a kernel: each wave's patch of 2 NT KiB (G rounded up to even: the
+// B reads of an odd G's last tile cover the missing group's KiB too, whose
+// values are replaced by zeros; 8 KiB for down), the same memory holding the
+// partial sums of tree_sum afterwards.
 template <int MB, int G>
 struct DenseLds {
   static constexpr int NT = (G + 1) / 2;
-  static constexpr int kPatch = kDenseWaves * (G > 8 ? G : 8) * 512;                   // uint16 elements
+  static constexpr int kPatchPerWave = 2 * NT * 512;                                    // uint16 elements
+  static constexpr int kPatch = kDenseWaves * (2 * NT > 8 ? 2 * NT : 8) * 512;          // uint16 elements
   static constexpr int kRedGu = (kDenseWaves / 2) * NT * 16 * (MB * 16 + kRedPad) * 2;  // uint16 elements
   static constexpr int kRedDown = (kDenseWaves / 2) * 4 * 16 * (MB * 16 + kRedPad) * 2;
   static constexpr int kSize = kPatch > kRedGu ? (kPatch > kRedDown ? kPatch : kRedDown)
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_dense_gate_up(const uint16
                  const int u = s < U ? s : s - U;
                  return u < nu ? (s < U ? u0 + u : H + u0 + u) : 0;
                },
-               x, T, lds + wave * G * 512);
+               x, T, lds + wave * Lds::kPatchPerWave);
   f32x4 acc[NT][MB];
 #pragma unroll
   for (int t = 0; t < NT; ++t)

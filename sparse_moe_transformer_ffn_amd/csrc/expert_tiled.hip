@@ -689,9 +689,14 @@ int down_splits(int T, int d, int hs) { return tiled_splits(T, d / kTileN, hs / 
 
 }  // namespace
 
+// Scratch for the splits the two launchers above take, each under the
+// condition that sends its phase to the tiled kernels: gate/up when hs is a
+// multiple of 128 (whatever d), down when d is a multiple of 256 (whatever
+// hs).  Either may split while the other does not tile at all.
 size_t tiled_split_bytes(int T, int d, int hs) {
-  if (T > kTileM || hs % (kTileN / 2) || d % kTileN) return 0;
-  const int kg = gate_up_splits(T, d, hs), kd = down_splits(T, d, hs);
+  if (T > kTileM) return 0;
+  const int kg = hs % (kTileN / 2) == 0 ? gate_up_splits(T, d, hs) : 1;
+  const int kd = d % kTileN == 0 ? down_splits(T, d, hs) : 1;
   const size_t g = kg > 1 ? (size_t)kg * T * 2 * hs * sizeof(float) : 0;
   const size_t n = kd > 1 ? (size_t)kd * T * d * sizeof(float) : 0;
   return ((g > n ? g : n) + 255) / 256 * 256;

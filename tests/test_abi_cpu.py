@@ -233,6 +233,27 @@ def test_dense_validation():
     assert L.moe_dense_swiglu(64, 256, 128, A, A, A, A, A, nb - 1, None) == WS_SMALL
 
 
+def test_dense_workspace_holds_each_phase_split():
+    # From 65 to 256 tokens one phase may run tiled with its reduction split
+    # over items while the other streams, and the split partial sums must fit
+    # the workspace.  The tiled kernels take 64-wide K chunks and split into
+    # ks equal ranges of at least 8 chunks (the smallest ks reaching 320
+    # items, else the largest):
+    # - T=230, d=1024, H=10944: down tiled (d % 256 == 0) over 171 = 9 * 19
+    #   hidden chunks, 4 output tiles: ks = 19 (9 chunks each), so 19 planes
+    #   of T x d f32; gate/up streams (H % 128 == 64).
+    # - T=165, d=768, H=8512: down over 133 = 7 * 19 chunks, ks = 7.
+    # - T=128, d=1152, H=4096: gate/up tiled (H % 128 == 0) over 18 chunks,
+    #   32 unit tiles: ks = 2, two planes of T x 2H f32; down streams
+    #   (d % 256 != 0).
+    L = moe.lib()
+    n = ctypes.c_size_t(0)
+    for T, d, H, planes in ((230, 1024, 10944, 19 * 230 * 1024), (165, 768, 8512, 7 * 165 * 768),
+                            (128, 1152, 4096, 2 * 128 * 2 * 4096)):
+        assert L.moe_dense_workspace_bytes(T, d, H, ctypes.byref(n)) == OK
+        assert n.value >= 256 + T * H * 2 + planes * 4, (T, d, H, n.value)
+
+
 def test_expert_range_validation():
     s = shape(1)
     L = moe.lib()

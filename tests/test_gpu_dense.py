@@ -65,6 +65,11 @@ def oracle_rows(cfg, x_h, rows):
     # a quarter of the reduction (down): ragged unit ranges (the last block
     # short), ragged reduction ranges, and waves left without K blocks.
     (64, 1024, 4352), (33, 512, 6208), (1, 256, 4096), (20, 768, 8256),
+    # Tiled with one phase split while the other does not tile: down split
+    # 19 and 7 ways over an odd count of 64-wide hidden chunks (hidden % 128
+    # == 64: gate/up streams), gate/up split 2 ways with d % 256 != 0 (down
+    # streams).  Their split scratch is sized per phase.
+    (230, 1024, 10944), (165, 768, 8512), (128, 1152, 4096),
 ])
 def test_dense_parity(device, T, d, H):
     cfg = moegen.custom(1, T=T, d=d, hs=H, seed=700 + T + H)
