@@ -14,12 +14,12 @@
 // length trades bytes in flight per wave against waves per SIMD).  The item
 // decomposition is in grouped.h.
 //
-// Phase 1 (gate/up): item = BM rows x 64 hidden units (or 16 with the
+// Phase 1 (gate/up): item = BM rows x 64 CPW hidden units (16 CPW with the
 // reduction split over the four waves); each wave computes both
 // G = X W_g[j]^T and U = X W_u[j]^T for its units j so that SwiGLU
 // (SiLU(G) * U) is applied in registers before the bf16 store.
-// Phase 2 (down): item = BM rows x 128 output columns (two groups of 16 per
-// wave), reduction over h.
+// Phase 2 (down): item = BM rows x 64 CPW output columns (CPW groups of 16
+// per wave), reduction over h.
 #include "common.h"
 #include "grouped.h"
 #include "kernels.h"
@@ -79,9 +79,9 @@ __device__ __forceinline__ u32x4 lines_operand(const Lines& L, int addr, bool hi
 
 // Phase 1: hid[row, j] = SiLU(x_row . W_g[j]) * (x_row . W_u[j]).  Routed
 // rows gather their token via perm_pairs; shared rows are tokens in order.
-// KW = 1: an item is BM rows x 64 hidden units, wave w owns units 16w..16w+15
-//         over the whole reduction.
-// KW = 4: an item is BM rows x 16 hidden units and wave w owns the w-th
+// KW = 1: an item is BM rows x 64 CPW hidden units, wave w owns CPW groups of
+//         16 units over the whole reduction.
+// KW = 4: an item is BM rows x 16 CPW hidden units and wave w owns the w-th
 //         quarter of the reduction; the four partial sums meet in LDS and are
 //         added in wave order (a fixed order: results do not depend on the
 //         schedule).  Items are four times smaller, so the last items of the
@@ -441,8 +441,9 @@ bool use_tiled(int T, int k, int E, const int32_t* offsets, bool down, bool spli
 
 int pick_bm(int T, int k, int E) {
   // Average rows per group decides the M-tile: 16 up to 16 rows, else 32
-  // (the shared group alone from 17 tokens).  Routed down launches of 4 to 10
-  // rows per group take 32-row items in launch_down.
+  // (the shared group alone from 17 tokens).  Routed launches take 32-row
+  // items earlier, in launch_gate_up from 2 rows per group and in
+  // launch_down from 4.
   const long rows = (long)T * k;
   return rows <= 16L * E ? 16 : 32;
 }
