@@ -2,8 +2,9 @@
 the libmoe calls) and replayed: every replay must give the eager result bit
 for bit, with eager work and synchronisations between replays.  No call in
 the path records a memset node (counters and queues are cleared by kernels).
-Covered: the decode forward (streaming kernels), the prefill forward (tiled
-kernels, work queues), and the dense FFN with split reductions.
+Covered: the decode forward (16-row streaming items), a 256-token layer
+(32-row streaming items), the prefill forward (tiled kernels, work queues),
+and the dense FFN with split reductions.
 """
 import numpy as np
 import pytest
@@ -16,7 +17,7 @@ from tests.gpu_harness import DeviceLayer, bf16_host, log
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("idx", [1, 2])
+@pytest.mark.parametrize("idx", [1, 4, 2])
 def test_layer_graph_replays_match_eager(device, idx):
     cfg = moegen.CONFIGS[idx]
     log(f"[graph] config {idx}: {cfg.workload}")
@@ -52,9 +53,10 @@ def test_layer_graph_replays_match_eager(device, idx):
 @pytest.mark.parametrize("T", [64, 128])
 def test_dense_split_graph_replays_match_eager(device, T):
     # The dense FFN with split reductions (partial sums in the workspace,
-    # added by a second kernel): at 64 tokens the streaming kernels (down
-    # split over items), at 128 the tiled ones (both phases split).  Replays
-    # of the captured call must equal the eager call bit for bit.
+    # added by another kernel): at 64 tokens the per-CU share kernels (down
+    # split four ways over the hidden reduction), at 128 the tiled ones (both
+    # phases split).  Replays of the captured call must equal the eager call
+    # bit for bit.
     d, H = 4096, 11264
     cfg = moegen.custom(1, T=T, hs=H, seed=777)
     log(f"[graph] dense FFN T={T} (split reductions)")
