@@ -14,12 +14,19 @@ constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, one L2 each
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t v16) { return __uint_as_float(v16 << 16); }
 
-// float -> bf16, round to nearest even; NaN stays NaN.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// float -> bf16, round to nearest even; NaN stays NaN (one
+// v_cvt_pk_bf16_f32, gfx950's conversion instruction).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t b = __float_as_uint(f);
-  if ((b & 0x7fffffffu) > 0x7f800000u) return (b >> 16) | 0x40u;
-  b += 0x7fffu + ((b >> 16) & 1u);
-  return b >> 16;
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Two floats -> two bf16 in one word, lo in bits 15:0 (one conversion).
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // 16x16x32 bf16 MFMA, f32 accumulate.  Operand lanes: lane l supplies row
@@ -55,7 +62,7 @@ __device__ __forceinline__ void unpack8(u32x4 v, float* f) {
 __device__ __forceinline__ u32x4 pack8(const float* f) {
   u32x4 v;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) v[q] = f32_to_bf16(f[2 * q]) | (f32_to_bf16(f[2 * q + 1]) << 16);
+  for (int q = 0; q < 4; ++q) v[q] = pack2_bf16(f[2 * q], f[2 * q + 1]);
   return v;
 }
 

@@ -75,7 +75,6 @@ constexpr int kChunk = 64;                        // K elements per stage
 constexpr int kSegs = kChunk / 8;                 // 16-byte segments per row
 constexpr int kStageA = kTileM * kChunk;          // bf16 elements
 constexpr int kStageB = kTileN * kChunk;
-constexpr int kStage = kStageA + kStageB;         // 64 KiB
 constexpr int kSteps = kChunk / 16;               // MFMA K steps per chunk
 constexpr int kRegionRows = 64 / kSegs;           // rows written by one wave-wide direct load
 constexpr int kLoadsA = kTileM / kRegionRows / kWaves;  // per thread per chunk
@@ -102,6 +101,27 @@ __device__ __forceinline__ void wave_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// LDS byte address of a pointer into this block's shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// The down epilogue stages through a buffer that no direct load in flight
+// writes.  Written as plain C++ its LDS accesses would each wait for every
+// outstanding global load and store first, because the compiler cannot tell
+// the direct loads' target buffers apart; these two do their own waiting
+// instead.  One wave's LDS accesses execute in order, so a write needs no
+// wait before a later read, and each read waits for itself.  `off` must fold
+// to a constant below 65536.
+__device__ __forceinline__ void lds_write_b16_own(uint32_t base, int off, uint32_t v) {
+  asm volatile("ds_write_b16 %0, %1 offset:%2" ::"v"(base), "v"(v), "i"(off) : "memory");
+}
+__device__ __forceinline__ u32x4 lds_read_b128_own(uint32_t base, int off) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(base), "i"(off) : "memory");
+  return v;
 }
 
 enum Phase { kGateUp = 0, kDown = 1 };
@@ -574,6 +594,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
         // 4 KiB of x1 (free: the next item's first chunks went to stage0 or
         // to slots S0 and S1).
         uint16_t* sb = x1 + wave * (16 * 128);  // 2048 bf16
+        const uint32_t sb_w = lds_addr(sb + 4 * lhi * 128 + l32);
+        const uint32_t sb_r = lds_addr(sb + (lane / 16) * 128 + (lane % 16) * 8);
+        // The item's output rows from its first column, addressed through a
+        // buffer resource: a uniform base and a 32-bit offset per lane, so no
+        // 64-bit row pointer stays live across the K loop.
+        uint16_t* ob = out + (size_t)it.row0 * d + it.nt * kTileN;
+        const int ob_bytes = ((it.nrows - 1) * d + (d - it.nt * kTileN)) * 2;
+        const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(ob, (short)0, ob_bytes, 0x00020000);
 #pragma unroll
         for (int ms = 0; ms < 2; ++ms) {
 #pragma unroll
@@ -581,34 +609,36 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
 #pragma unroll
             for (int i4 = 0; i4 < 8; ++i4)
 #pragma unroll
-              for (int ns = 0; ns < 4; ++ns) {
-                const int rr = 8 * (i4 / 4) + 4 * lhi + (i4 % 4);
-                sb[rr * 128 + ns * 32 + l32] = (uint16_t)f32_to_bf16(acc[ms][ns][8 * hf + i4]);
-              }
+              for (int ns = 0; ns < 4; ++ns)  // row 8*(i4/4) + 4*lhi + i4%4
+                lds_write_b16_own(sb_w, ((8 * (i4 / 4) + i4 % 4) * 128 + ns * 32) * 2,
+                                  f32_to_bf16(acc[ms][ns][8 * hf + i4]));
             wave_fence();
 #pragma unroll
             for (int j = 0; j < 4; ++j) {  // 16 rows x 16 segments
               const int idx = lane + kWave * j, rr = idx / 16, sg = idx % 16;
-              const u32x4 v = *reinterpret_cast<const u32x4*>(sb + rr * 128 + sg * 8);
+              const u32x4 v = lds_read_b128_own(sb_r, j * (kWave / 16) * 128 * 2);
               const int r = wave_row0 + ms * 32 + 16 * hf + rr;
               if (r < it.nrows)
-                *reinterpret_cast<u32x4*>(out + (size_t)(it.row0 + r) * d + it.nt * kTileN + wn * 128 + sg * 8) = v;
+                __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, (r * d + wn * 128 + sg * 8) * 2, 0, 0);
             }
             wave_fence();
           }
         }
       } else {
+        // fp32 rows of the shared expert, through a buffer resource as above.
+        float* ob = static_cast<float*>(out_shared) + (size_t)it.row0 * d + it.nt * kTileN;
+        const int ob_bytes = ((it.nrows - 1) * d + (d - it.nt * kTileN)) * 4;
+        const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(ob, (short)0, ob_bytes, 0x00020000);
 #pragma unroll
         for (int ms = 0; ms < 2; ++ms) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int r = wave_row0 + ms * 32 + 8 * (i / 4) + 4 * lhi + (i % 4);
             if (r >= it.nrows) continue;
-            const size_t grow = (size_t)(it.row0 + r);
 #pragma unroll
             for (int ns = 0; ns < 4; ++ns)
-              static_cast<float*>(out_shared)[grow * d + it.nt * kTileN + wn * 128 + ns * 32 + l32] =
-                  acc[ms][ns][i];
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[ms][ns][i]), orsrc,
+                                                    (r * d + wn * 128 + ns * 32 + l32) * 4, 0, 0);
           }
         }
       }
@@ -641,8 +671,8 @@ __global__ __launch_bounds__(256) void k_swiglu_splits(const float* __restrict__
       g.x += gs.x, g.y += gs.y, g.z += gs.z, g.w += gs.w;
       u.x += us.x, u.y += us.y, u.z += us.z, u.w += us.w;
     }
-    const uint32_t lo = f32_to_bf16(swiglu(g.x, u.x, clamp)) | (f32_to_bf16(swiglu(g.y, u.y, clamp)) << 16);
-    const uint32_t hi = f32_to_bf16(swiglu(g.z, u.z, clamp)) | (f32_to_bf16(swiglu(g.w, u.w, clamp)) << 16);
+    const uint32_t lo = pack2_bf16(swiglu(g.x, u.x, clamp), swiglu(g.y, u.y, clamp));
+    const uint32_t hi = pack2_bf16(swiglu(g.z, u.z, clamp), swiglu(g.w, u.w, clamp));
     *reinterpret_cast<uint2*>(hid + t * H + j) = make_uint2(lo, hi);
   }
 }
