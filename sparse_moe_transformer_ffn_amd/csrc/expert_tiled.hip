@@ -108,15 +108,24 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// The down epilogue stages through a buffer that no direct load in flight
-// writes.  Written as plain C++ its LDS accesses would each wait for every
-// outstanding global load and store first, because the compiler cannot tell
-// the direct loads' target buffers apart; these two do their own waiting
-// instead.  One wave's LDS accesses execute in order, so a write needs no
-// wait before a later read, and each read waits for itself.  `off` must fold
-// to a constant below 65536.
-__device__ __forceinline__ void lds_write_b16_own(uint32_t base, int off, uint32_t v) {
-  asm volatile("ds_write_b16 %0, %1 offset:%2" ::"v"(base), "v"(v), "i"(off) : "memory");
+// The lane's index, computed where it is called: values derived from it are
+// not hoisted out of the item loop to sit in registers across the K loop.
+__device__ __forceinline__ int lane_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// The epilogue stages through a buffer that no direct load in flight writes.
+// Written as plain C++ its LDS accesses would each wait for every outstanding
+// global load and store first, because the compiler cannot tell the direct
+// loads' target buffers apart; these two do their own waiting instead.  One
+// wave's LDS accesses execute in order, so a write needs no wait before a
+// later read, and each read waits for itself.  `off` must fold to a
+// constant below 65536.
+__device__ __forceinline__ void lds_write_b64_own(uint32_t addr, uint32_t lo, uint32_t hi) {
+  asm volatile("ds_write_b64 %0, %1" ::"v"(addr), "v"(__builtin_bit_cast(unsigned long long, (u32x2){lo, hi}))
+               : "memory");
 }
 __device__ __forceinline__ u32x4 lds_read_b128_own(uint32_t base, int off) {
   u32x4 v;
@@ -207,7 +216,8 @@ __device__ __forceinline__ void mma_step(const Frags& cur, Frags& nxt, const Sta
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     if (MUL) {
-      acc[i / 4][i % 4] = mfma_32x32x16(cur.v[i / 4], cur.v[2 + i % 4], acc[i / 4][i % 4]);
+      acc[i / 4][i % 4] = PHASE == kDown ? mfma_32x32x16(cur.v[2 + i % 4], cur.v[i / 4], acc[i / 4][i % 4])
+                                         : mfma_32x32x16(cur.v[i / 4], cur.v[2 + i % 4], acc[i / 4][i % 4]);
       __builtin_amdgcn_sched_barrier(0);
       if (READ && i < 6) {
         nxt.v[i] = read_frag<PHASE>(stage, m, s, i);
@@ -537,16 +547,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
       issue_first(nxt, stage0, S0, S1);
     }
 
-    // Epilogue.  Element i of acc[ms][ns] is row 8*(i/4) + 4*lhi + (i%4) of
-    // M-subtile ms, column l32 of N-subtile ns.  The routed down output
-    // (bf16, 128 columns per wave) goes through x1 (free: the down K loop's
-    // last chunks issued no loads, and the next item's first chunks went to
-    // stage0 or to slots S0 and S1): each wave writes 16 rows of its tile
-    // there at a time and reads them back as 16-byte row segments, so the
-    // global stores are whole 16-byte pieces (eight times fewer than one per
-    // element).  Only the wave's own 4 KiB region is touched, so a wave-level
-    // fence orders the writes before the reads and the reads before the next
-    // writes.  The other outputs are stored per element.
+    // Epilogue.  In gate/up, element i of acc[ms][ns] is row
+    // 8*(i/4) + 4*lhi + (i%4) of M-subtile ms, column l32 of N-subtile ns.
+    // Down multiplies with the operands swapped, so its tile comes out
+    // transposed: element i is column 8*(i/4) + 4*lhi + (i%4) of N-subtile ns,
+    // row l32 of M-subtile ms -- four adjacent columns of one row per lane,
+    // which pack into 8 bytes of bf16 or 16 of f32.
     if (mul) {
       const Item& it = cur.it;
       const int H = cur.H;
@@ -558,14 +564,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
         for (int ms = 0; ms < 2; ++ms) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int r = wave_row0 + ms * 32 + 8 * (i / 4) + 4 * lhi + (i % 4);
+            const int r = wave_row0 + ms * 32 + (PHASE == kGateUp ? 8 * (i / 4) + 4 * lhi + (i % 4) : l32);
             if (r >= it.nrows) continue;
             const size_t grow = (size_t)(it.row0 + r);
 #pragma unroll
             for (int ns = 0; ns < 4; ++ns) {
               const int col = PHASE == kGateUp
                                   ? (ns < 2 ? 0 : H) + it.nt * (kTileN / 2) + wn * 64 + (ns % 2) * 32 + l32
-                                  : it.nt * kTileN + wn * 128 + ns * 32 + l32;
+                                  : it.nt * kTileN + wn * 128 + ns * 32 + 8 * (i / 4) + 4 * lhi + (i % 4);
               pp[grow * NW + col] = acc[ms][ns][i];
             }
           }
@@ -590,55 +596,65 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
           }
         }
       } else if (!it.shared) {
-        // 64 rows x 128 columns of this wave, 16 rows at a time through its
-        // 4 KiB of x1 (free: the next item's first chunks went to stage0 or
-        // to slots S0 and S1).
-        uint16_t* sb = x1 + wave * (16 * 128);  // 2048 bf16
-        const uint32_t sb_w = lds_addr(sb + 4 * lhi * 128 + l32);
-        const uint32_t sb_r = lds_addr(sb + (lane / 16) * 128 + (lane % 16) * 8);
-        // The item's output rows from its first column, addressed through a
-        // buffer resource: a uniform base and a 32-bit offset per lane, so no
-        // 64-bit row pointer stays live across the K loop.
+        // 32 rows x 64 columns at a time through the wave's 4 KiB of x1 (free:
+        // the down K loop's last chunks issued no loads, and the next item's
+        // first chunks went to stage0 or to slots S0 and S1).  A lane writes
+        // its 4 columns of one row as 8 bytes; 16-byte segment s of row r sits
+        // at slot s ^ (r & 7) of the row's 128 bytes, so the 32 rows of one
+        // write spread over the banks.  Read back as whole segments, 8 rows
+        // of 128 bytes per read, they go out as 16-byte stores through a
+        // buffer resource (uniform base, 32-bit offset per lane).
+        const int ln = lane_here(), lr = ln & 31;
+        const uint32_t sb = lds_addr(x1 + wave * 2048);
+        const uint32_t wbase = sb + lr * 128 + (ln >> 5) * 8, wxor = (lr & 7) << 4;
+        const int rr = ln / 8, sg = ln % 8;
+        const uint32_t rbase = sb + rr * 128 + ((sg ^ rr) << 4);
         uint16_t* ob = out + (size_t)it.row0 * d + it.nt * kTileN;
         const int ob_bytes = ((it.nrows - 1) * d + (d - it.nt * kTileN)) * 2;
         const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(ob, (short)0, ob_bytes, 0x00020000);
 #pragma unroll
         for (int ms = 0; ms < 2; ++ms) {
 #pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
+          for (int nh = 0; nh < 2; ++nh) {
 #pragma unroll
-            for (int i4 = 0; i4 < 8; ++i4)
+            for (int n2 = 0; n2 < 2; ++n2)
 #pragma unroll
-              for (int ns = 0; ns < 4; ++ns)  // row 8*(i4/4) + 4*lhi + i4%4
-                lds_write_b16_own(sb_w, ((8 * (i4 / 4) + i4 % 4) * 128 + ns * 32) * 2,
-                                  f32_to_bf16(acc[ms][ns][8 * hf + i4]));
+              for (int q = 0; q < 4; ++q) {
+                const f32x16& a = acc[ms][2 * nh + n2];
+                lds_write_b64_own(wbase + (((n2 * 4 + q) << 4) ^ wxor), pack2_bf16(a[4 * q], a[4 * q + 1]),
+                                  pack2_bf16(a[4 * q + 2], a[4 * q + 3]));
+              }
             wave_fence();
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {  // 16 rows x 16 segments
-              const int idx = lane + kWave * j, rr = idx / 16, sg = idx % 16;
-              const u32x4 v = lds_read_b128_own(sb_r, j * (kWave / 16) * 128 * 2);
-              const int r = wave_row0 + ms * 32 + 16 * hf + rr;
+            for (int j = 0; j < 4; ++j) {
+              const u32x4 v = lds_read_b128_own(rbase, j * 1024);
+              const int r = wave_row0 + ms * 32 + 8 * j + rr;
               if (r < it.nrows)
-                __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, (r * d + wn * 128 + sg * 8) * 2, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, (r * d + wn * 128 + nh * 64 + sg * 8) * 2, 0, 0);
             }
             wave_fence();
           }
         }
       } else {
-        // fp32 rows of the shared expert, through a buffer resource as above.
+        // f32 rows of the shared expert: a lane's 4 columns of a row are 16
+        // contiguous bytes, stored through a buffer resource as above.
         float* ob = static_cast<float*>(out_shared) + (size_t)it.row0 * d + it.nt * kTileN;
         const int ob_bytes = ((it.nrows - 1) * d + (d - it.nt * kTileN)) * 4;
         const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(ob, (short)0, ob_bytes, 0x00020000);
 #pragma unroll
         for (int ms = 0; ms < 2; ++ms) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int r = wave_row0 + ms * 32 + 8 * (i / 4) + 4 * lhi + (i % 4);
-            if (r >= it.nrows) continue;
+          const int r = wave_row0 + ms * 32 + l32;
+          if (r < it.nrows) {
 #pragma unroll
             for (int ns = 0; ns < 4; ++ns)
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[ms][ns][i]), orsrc,
-                                                    (r * d + wn * 128 + ns * 32 + l32) * 4, 0, 0);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const f32x16& a = acc[ms][ns];
+                const u32x4 v = {__float_as_uint(a[4 * q]), __float_as_uint(a[4 * q + 1]),
+                                 __float_as_uint(a[4 * q + 2]), __float_as_uint(a[4 * q + 3])};
+                __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, (r * d + wn * 128 + ns * 32 + 8 * q + 4 * lhi) * 4,
+                                                       0, 0);
+              }
           }
         }
       }
