@@ -216,8 +216,7 @@ __device__ __forceinline__ void mma_step(const Frags& cur, Frags& nxt, const Sta
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     if (MUL) {
-      acc[i / 4][i % 4] = PHASE == kDown ? mfma_32x32x16(cur.v[2 + i % 4], cur.v[i / 4], acc[i / 4][i % 4])
-                                         : mfma_32x32x16(cur.v[i / 4], cur.v[2 + i % 4], acc[i / 4][i % 4]);
+      acc[i / 4][i % 4] = mfma_32x32x16(cur.v[2 + i % 4], cur.v[i / 4], acc[i / 4][i % 4]);
       __builtin_amdgcn_sched_barrier(0);
       if (READ && i < 6) {
         nxt.v[i] = read_frag<PHASE>(stage, m, s, i);
@@ -547,70 +546,86 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
       issue_first(nxt, stage0, S0, S1);
     }
 
-    // Epilogue.  In gate/up, element i of acc[ms][ns] is row
-    // 8*(i/4) + 4*lhi + (i%4) of M-subtile ms, column l32 of N-subtile ns.
-    // Down multiplies with the operands swapped, so its tile comes out
-    // transposed: element i is column 8*(i/4) + 4*lhi + (i%4) of N-subtile ns,
-    // row l32 of M-subtile ms -- four adjacent columns of one row per lane,
-    // which pack into 8 bytes of bf16 or 16 of f32.
+    // Epilogue.  The MFMAs take the weight operand first, so the tile comes
+    // out transposed: element i of acc[ms][ns] is column 8*(i/4) + 4*lhi +
+    // (i%4) of N-subtile ns, row l32 of M-subtile ms -- four adjacent columns
+    // of one row per lane, which pack into 8 bytes of bf16 or 16 of f32.
+    // The bf16 outputs go through the wave's 4 KiB of x1 (free: the K loop's
+    // last loads landed before the barrier above, and the next item's first
+    // chunks went to stage0 or to slots S0 and S1), 32 rows x 64 columns at a
+    // time: a lane writes its 4 columns of a row as 8 bytes, 16-byte segment
+    // s of row r at slot s ^ (r & 7) of the row's 128 bytes so that the 32
+    // rows of one write spread over the banks; read back as whole segments, 8
+    // rows of 128 bytes per read, they go out as 16-byte stores through a
+    // buffer resource (uniform base at the item's first row, 32-bit offset
+    // per lane: an item's 256 rows of at most 65,536 f32 span 64 MiB).
     if (mul) {
       const Item& it = cur.it;
       const int H = cur.H;
       if (SPLIT) {
-        // Raw f32 sums of this split, per element.
+        // Raw f32 sums of this split, 16 bytes (4 columns of a row) a store.
         const int NW = PHASE == kGateUp ? 2 * H : d;
         float* pp = partial + (size_t)cur.ksi * gs.T * NW;
 #pragma unroll
         for (int ms = 0; ms < 2; ++ms) {
+          const int r = wave_row0 + ms * 32 + l32;
+          if (r < it.nrows) {
+            float* prow = pp + (size_t)(it.row0 + r) * NW;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int r = wave_row0 + ms * 32 + (PHASE == kGateUp ? 8 * (i / 4) + 4 * lhi + (i % 4) : l32);
-            if (r >= it.nrows) continue;
-            const size_t grow = (size_t)(it.row0 + r);
+            for (int ns = 0; ns < 4; ++ns)
 #pragma unroll
-            for (int ns = 0; ns < 4; ++ns) {
-              const int col = PHASE == kGateUp
-                                  ? (ns < 2 ? 0 : H) + it.nt * (kTileN / 2) + wn * 64 + (ns % 2) * 32 + l32
-                                  : it.nt * kTileN + wn * 128 + ns * 32 + 8 * (i / 4) + 4 * lhi + (i % 4);
-              pp[grow * NW + col] = acc[ms][ns][i];
-            }
+              for (int q = 0; q < 4; ++q) {
+                const int col = (PHASE == kGateUp ? (ns < 2 ? 0 : H) + it.nt * (kTileN / 2) + wn * 64 + (ns % 2) * 32
+                                                  : it.nt * kTileN + wn * 128 + ns * 32) +
+                                8 * q + 4 * lhi;
+                const f32x16& a = acc[ms][ns];
+                *reinterpret_cast<f32x4*>(prow + col) = f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+              }
           }
         }
       } else if (PHASE == kGateUp) {
-        // Unit ns*32 + l32 pairs gate acc[ms][ns] with up acc[ms][ns+2]; the
-        // hidden rows are short (64 units of this wave), stored per element.
-        uint16_t* o = it.shared ? static_cast<uint16_t*>(out_shared) : out;
-#pragma unroll
-        for (int ms = 0; ms < 2; ++ms) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int r = wave_row0 + ms * 32 + 8 * (i / 4) + 4 * lhi + (i % 4);
-            if (r >= it.nrows) continue;
-            const size_t grow = (size_t)(it.row0 + r);
-#pragma unroll
-            for (int ns = 0; ns < 2; ++ns) {
-              const float g = acc[ms][ns][i], u = acc[ms][ns + 2][i];
-              o[grow * H + it.nt * (kTileN / 2) + wn * 64 + ns * 32 + l32] =
-                  (uint16_t)f32_to_bf16(swiglu(g, u, CLAMP ? clamp : 0.f));
-            }
-          }
-        }
-      } else if (!it.shared) {
-        // 32 rows x 64 columns at a time through the wave's 4 KiB of x1 (free:
-        // the down K loop's last chunks issued no loads, and the next item's
-        // first chunks went to stage0 or to slots S0 and S1).  A lane writes
-        // its 4 columns of one row as 8 bytes; 16-byte segment s of row r sits
-        // at slot s ^ (r & 7) of the row's 128 bytes, so the 32 rows of one
-        // write spread over the banks.  Read back as whole segments, 8 rows
-        // of 128 bytes per read, they go out as 16-byte stores through a
-        // buffer resource (uniform base, 32-bit offset per lane).
+        // Hidden unit u of the wave's 64 pairs gate acc[ms][u / 32] with up
+        // acc[ms][u / 32 + 2] (same element); 64 rows x 64 units in two passes.
         const int ln = lane_here(), lr = ln & 31;
         const uint32_t sb = lds_addr(x1 + wave * 2048);
         const uint32_t wbase = sb + lr * 128 + (ln >> 5) * 8, wxor = (lr & 7) << 4;
         const int rr = ln / 8, sg = ln % 8;
         const uint32_t rbase = sb + rr * 128 + ((sg ^ rr) << 4);
-        uint16_t* ob = out + (size_t)it.row0 * d + it.nt * kTileN;
-        const int ob_bytes = ((it.nrows - 1) * d + (d - it.nt * kTileN)) * 2;
+        uint16_t* ob = (it.shared ? static_cast<uint16_t*>(out_shared) : out) + (size_t)(it.row0 + it.m0) * H +
+                       it.nt * (kTileN / 2);
+        const int ob_bytes = ((min(it.nrows - it.m0, kTileM) - 1) * H + (H - it.nt * (kTileN / 2))) * 2;
+        const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(ob, (short)0, ob_bytes, 0x00020000);
+        const float cl = CLAMP ? clamp : 0.f;
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms) {
+#pragma unroll
+          for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x16& g = acc[ms][ns];
+              const f32x16& u = acc[ms][ns + 2];
+              lds_write_b64_own(wbase + (((ns * 4 + q) << 4) ^ wxor),
+                                pack2_bf16(swiglu(g[4 * q], u[4 * q], cl), swiglu(g[4 * q + 1], u[4 * q + 1], cl)),
+                                pack2_bf16(swiglu(g[4 * q + 2], u[4 * q + 2], cl), swiglu(g[4 * q + 3], u[4 * q + 3], cl)));
+            }
+          wave_fence();
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const u32x4 v = lds_read_b128_own(rbase, j * 1024);
+            const int r = wave_row0 + ms * 32 + 8 * j + rr;
+            if (r < it.nrows)
+              __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, ((r - it.m0) * H + wn * 64 + sg * 8) * 2, 0, 0);
+          }
+          wave_fence();
+        }
+      } else if (!it.shared) {
+        const int ln = lane_here(), lr = ln & 31;
+        const uint32_t sb = lds_addr(x1 + wave * 2048);
+        const uint32_t wbase = sb + lr * 128 + (ln >> 5) * 8, wxor = (lr & 7) << 4;
+        const int rr = ln / 8, sg = ln % 8;
+        const uint32_t rbase = sb + rr * 128 + ((sg ^ rr) << 4);
+        uint16_t* ob = out + (size_t)(it.row0 + it.m0) * d + it.nt * kTileN;
+        const int ob_bytes = ((min(it.nrows - it.m0, kTileM) - 1) * d + (d - it.nt * kTileN)) * 2;
         const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(ob, (short)0, ob_bytes, 0x00020000);
 #pragma unroll
         for (int ms = 0; ms < 2; ++ms) {
@@ -630,7 +645,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
               const u32x4 v = lds_read_b128_own(rbase, j * 1024);
               const int r = wave_row0 + ms * 32 + 8 * j + rr;
               if (r < it.nrows)
-                __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, (r * d + wn * 128 + nh * 64 + sg * 8) * 2, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, ((r - it.m0) * d + wn * 128 + nh * 64 + sg * 8) * 2,
+                                                       0, 0);
             }
             wave_fence();
           }
@@ -638,8 +654,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
       } else {
         // f32 rows of the shared expert: a lane's 4 columns of a row are 16
         // contiguous bytes, stored through a buffer resource as above.
-        float* ob = static_cast<float*>(out_shared) + (size_t)it.row0 * d + it.nt * kTileN;
-        const int ob_bytes = ((it.nrows - 1) * d + (d - it.nt * kTileN)) * 4;
+        float* ob = static_cast<float*>(out_shared) + (size_t)(it.row0 + it.m0) * d + it.nt * kTileN;
+        const int ob_bytes = ((min(it.nrows - it.m0, kTileM) - 1) * d + (d - it.nt * kTileN)) * 4;
         const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(ob, (short)0, ob_bytes, 0x00020000);
 #pragma unroll
         for (int ms = 0; ms < 2; ++ms) {
@@ -652,8 +668,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_expert_tiled(const uint16_t* __
                 const f32x16& a = acc[ms][ns];
                 const u32x4 v = {__float_as_uint(a[4 * q]), __float_as_uint(a[4 * q + 1]),
                                  __float_as_uint(a[4 * q + 2]), __float_as_uint(a[4 * q + 3])};
-                __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, (r * d + wn * 128 + ns * 32 + 8 * q + 4 * lhi) * 4,
-                                                       0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    v, orsrc, ((r - it.m0) * d + wn * 128 + ns * 32 + 8 * q + 4 * lhi) * 4, 0, 0);
               }
           }
         }
