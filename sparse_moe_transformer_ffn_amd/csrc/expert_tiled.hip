@@ -55,7 +55,9 @@
 //
 // MFMA 32x32x16 operands: lane l supplies row (l % 32) of A / column (l % 32)
 // of B for the 8 reduction elements 8*(l/32) .. +7 of the 16; result element
-// i of lane l is D[8*(i/4) + 4*(l/32) + (i%4)][l % 32].
+// i of lane l is D[8*(i/4) + 4*(l/32) + (i%4)][l % 32].  The kernels pass the
+// weight fragment as A and the token fragment as B, so D is the transposed
+// output tile: four adjacent output columns of one token row per lane.
 #include "common.h"
 #include "grouped.h"
 #include "kernels.h"
@@ -236,11 +238,11 @@ __device__ __forceinline__ void mma_step(const Frags& cur, Frags& nxt, const Sta
 // having been consumed by that chunk's MFMAs).  Steps 0-2 read steps 1-3 of
 // `cur`; step 3 only multiplies.  Then each thread waits for its loads of
 // chunk c+1 and the block barrier makes them visible; its first fragments
-// are read last.  In the down phase the last chunk issues no loads, so both
-// stages are free once the item's K loop ends (its epilogue uses one); in
+// are read last.  In the down phase the last chunk issues no loads; in
 // gate/up it repeats its own loads (an L2 hit into a stage nobody reads), so
-// every chunk issues and waits the same way.  The final reads fetch unused
-// data.  Waves without rows in the item (MUL = false) only load and wait.
+// every chunk issues and waits the same way (issuing none there measured no
+// faster).  Either way the barrier after the K loop drains them, and the
+// epilogue may use x1.  The final reads fetch unused data.  Waves without rows in the item (MUL = false) only load and wait.
 template <int PHASE, int NA, bool MUL>
 __device__ __forceinline__ void pipe_chunk(const Pipe& p, const StageRef& cur, const StageRef& other, int c, int nch,
                                            const ReadMap& m, Frags (&fr)[2], f32x16 (&acc)[2][4]) {
