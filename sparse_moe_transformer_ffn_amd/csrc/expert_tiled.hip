@@ -88,7 +88,8 @@ static_assert(kLoads == 8 && kSteps == 4, "pipeline shape");
 // 6:4 and lgkmcnt 11:8 not waited on).
 constexpr int kWaitAll = 0x0F70;
 
-constexpr int kPolicy = 0;  // default cache policy for both operands
+constexpr int kPolicy = 0;       // default cache policy of the direct loads
+constexpr int kNonTemporal = 2;  // the loads' nt bit (gfx950 cache-policy operand)
 
 __device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -153,7 +154,18 @@ __device__ __forceinline__ constexpr int b_row0(int wn, int ns) {
 struct Pipe {
   const uint16_t* src[kLoads];  // per-thread source of each direct load (chunk 0)
   int lds_off[kLoads];          // wave-uniform LDS element offset inside its A slice or B tile
+  bool wnt;                     // weight loads non-temporal (uniform; see make_plan)
 };
+
+// Direct load q of a chunk: the weight loads (q >= kLoadsA) of an item whose
+// weight tile no other item reads go non-temporal, so they do not push the
+// token rows, which the group's other N-tiles read again, out of L2.
+__device__ __forceinline__ void dload(const Pipe& p, int q, const uint16_t* src, uint16_t* dst) {
+  if (q >= kLoadsA && p.wnt)
+    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, kNonTemporal);
+  else
+    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, kPolicy);
+}
 
 template <int NA>
 __device__ __forceinline__ constexpr bool load_used(int q) {
@@ -182,7 +194,7 @@ template <int NA>
 __device__ __forceinline__ void issue_chunk(const Pipe& p, const StageRef& st, int c) {
 #pragma unroll
   for (int q = 0; q < kLoads; ++q)
-    if (load_used<NA>(q)) __builtin_amdgcn_global_load_lds(p.src[q] + c * kChunk, load_dst(st, p, q), 16, 0, kPolicy);
+    if (load_used<NA>(q)) dload(p, q, p.src[q] + c * kChunk, load_dst(st, p, q));
 }
 
 // LDS element offsets of this lane's fragment reads, per K step s: row l32
@@ -226,7 +238,7 @@ __device__ __forceinline__ void mma_step(const Frags& cur, Frags& nxt, const Sta
       }
     }
     if (LOADS && issue && load_used<NA>(i)) {
-      __builtin_amdgcn_global_load_lds(p.src[i] + cload * kChunk, load_dst(other, p, i), 16, 0, kPolicy);
+      dload(p, i, p.src[i] + cload * kChunk, load_dst(other, p, i));
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -366,6 +378,10 @@ __device__ __forceinline__ Plan make_plan(const int* ip, const Groups& gs, int n
   }
   pl.it = it;
   pl.na = min(kLoadsA, (it.nrows - it.m0 + 63) / 64);
+  // A group of one M-tile reads each weight tile in one item only (skewed
+  // load: gate/up 1.258 -> 1.239 ms, down 0.728 -> 0.715; prefill within
+  // 1%).  Groups of more M-tiles share their weight tiles through L2.
+  pl.p.wnt = __builtin_amdgcn_readfirstlane(it.nrows <= kTileM ? 1 : 0) != 0;
   const uint16_t* wmat;
   int b_lo, b_hi;  // weight-matrix row of tile row r: b_lo + r (r < 128), b_hi + r (r >= 128)
   if (PHASE == kGateUp) {
