@@ -101,15 +101,18 @@ def write_traffic(pmc_dir):
           python3 bench.py --steps 2 --warmup 1 --only-prefill
       rocprofv3 --pmc FETCH_SIZE -f csv -d <pmc_dir>/skw_fetch -o skw_fetch -- \
           python3 bench.py --steps 2 --warmup 1 --only-skew
-      (and the same four with WRITE_SIZE into *_write; a workload whose runs
-      are missing is skipped)
+      rocprofv3 --pmc FETCH_SIZE -f csv -d <pmc_dir>/stk_fetch -o stk_fetch -- \
+          python3 bench.py --steps 2 --warmup 1 --only-stack
+      (and the same five with WRITE_SIZE into *_write; a workload whose runs
+      are missing is skipped).  The stack's figure is the mean over its twelve
+      layers' launches.
     """
     copy_fetch, _ = _counter_means(pmc_dir, "copy_fetch", "FETCH_SIZE", (COPY_KERNEL,))
     copy_write, _ = _counter_means(pmc_dir, "copy_write", "WRITE_SIZE", (COPY_KERNEL,))
     f_fetch = COPY_BYTES / (copy_fetch * 1024)
     f_write = COPY_BYTES / (copy_write * 1024)
     src = kernel_source_hash()
-    for workload, run in (("decode", "dec"), ("prefill", "pre"), ("skew", "skw")):
+    for workload, run in (("decode", "dec"), ("prefill", "pre"), ("skew", "skw"), ("stack", "stk")):
         if not os.path.exists(os.path.join(pmc_dir, f"{run}_fetch")):
             print(f"{workload}: no {run}_fetch run in {pmc_dir}, skipped")
             continue
@@ -348,7 +351,7 @@ def time_stack(steps, warmup, dev, cpu_sample=0):
     One pass = 12 layer steps and 11 normalisations; supplementary figure.
     Its dominant kernel (each layer's grouped gate/up launch) is HBM-bound:
     the roofline object gives its algorithmic bytes over its time, summed
-    over the layers."""
+    over the layers, and its counted traffic as the mean per launch."""
     import numpy as np
     import torch
     import moegen
@@ -393,7 +396,7 @@ def time_stack(steps, warmup, dev, cpu_sample=0):
     out = {"workload": cfg.workload, "layers": cfg.layers, "tok_s": cfg.T / (ms * 1e-3), "ms_per_pass_median": ms,
            "ms_per_pass_min": float(per.min()), "passes": steps, "hbm_gbs": nbytes / (ms * 1e-3) / 1e9,
            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-           "roofline": roofline("hbm", gu_gbs, None),
+           "roofline": roofline("hbm", gu_gbs, load_traffic("stack", "gate_up")),
            "kernels": {"gate_up_ms_per_layer": float(gu_ms.mean()), "down_ms_per_layer": float(dn_ms.mean()),
                        "gate_up_gbs": gu_gbs, "down_gbs": dn_gbs},
            "touched_experts_per_layer": touched}
